@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the
+benchmark.
+
+This module holds no part of the product's arithmetic: it draws random numbers
+with numpy's PCG64 and rounds them to the element formats with torch's CPU
+casts (round-to-nearest-even).  The GPU path and the CPU oracle both consume
+the raw codes it returns.
+
+Seeds: ``1000*workload + 10*shape_index + {0: A, 1: B}``.
+
+Storage convention (the layouts of the sweep command in section "Practical
+shape sweep" of page "10. Tensor Cores, shapes, and tile alignment": A
+row-major, B column-major):
+  * A is M x K row-major, lda = K  (array shape (M, K))
+  * B is K x N column-major, ldb = K (array shape (N, K): column j of B is
+    row j of the array)
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+
+def seed_for(workload: int, shape_index: int, operand: int) -> int:
+    return 1000 * workload + 10 * shape_index + operand
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def draw(gen: np.random.Generator, shape, dist: str, K: Optional[int] = None) -> np.ndarray:
+    """binary64 samples: 'uniform' U[-1,1], 'normal' N(0,1), 'normal_sqrtk'
+    N(0,1)/sqrt(K)."""
+    if dist == "uniform":
+        return gen.uniform(-1.0, 1.0, size=shape)
+    if dist == "normal":
+        return gen.standard_normal(size=shape)
+    if dist == "normal_sqrtk":
+        if not K:
+            raise ValueError("normal_sqrtk needs K")
+        return gen.standard_normal(size=shape) / np.sqrt(K)
+    raise ValueError("unknown distribution %r" % dist)
+
+
+def to_bf16_codes(x: np.ndarray) -> np.ndarray:
+    """binary64 -> binary32 (RNE) -> bf16 (RNE); returns uint16 codes."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def to_e4m3_codes(x: np.ndarray, scale: Optional[float] = None) -> Tuple[np.ndarray, float]:
+    """Per-tensor quantisation to OCP E4M3FN.  In binary32: s = amax|x|/448
+    (unless given), q = e4m3_rne(clamp(x/s, -448, 448)).  Returns (uint8
+    codes, s); x is approximately s * decode(q)."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    if scale is None:
+        amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+        scale = float(np.float32(amax) / np.float32(E4M3_MAX)) if amax > 0 else 1.0
+    s32 = np.float32(scale)
+    y = np.clip(x32 / s32, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    q = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return q, float(s32)
+
+
+def small_int_codes(gen: np.random.Generator, shape, fmt: str, lo: int = -4,
+                    hi: int = 4) -> np.ndarray:
+    """Integers in [lo, hi], exactly representable in bf16 and E4M3."""
+    v = gen.integers(lo, hi + 1, size=shape).astype(np.float64)
+    if fmt == "bf16":
+        return to_bf16_codes(v)
+    q, _ = to_e4m3_codes(v, scale=1.0)
+    return q
+
+
+def codes_to_torch(codes: np.ndarray) -> torch.Tensor:
+    """View raw codes as a torch tensor of the matching element type."""
+    if codes.dtype == np.uint16:
+        return torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16)
+    if codes.dtype == np.uint8:
+        return torch.from_numpy(codes).view(torch.float8_e4m3fn)
+    raise TypeError("codes must be uint16 (bf16) or uint8 (E4M3)")
+
+
+def sha256(*arrays: np.ndarray) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+@dataclass
+class Operands:
+    """One GEMM's operands as raw codes in the storage convention above."""
+    M: int
+    N: int
+    K: int
+    fmt: str                      # "bf16" or "e4m3"
+    A: np.ndarray                 # (batch, M, K) or (M, K)
+    B: np.ndarray                 # (batch, N, K) or (N, K)  (column-major B)
+    scale_a: List[float] = field(default_factory=list)
+    scale_b: List[float] = field(default_factory=list)
+    seeds: Tuple[int, int] = (0, 0)
+
+    @property
+    def batch(self) -> int:
+        return self.A.shape[0] if self.A.ndim == 3 else 1
+
+
+def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
+                  seed_b: int, batch: int = 0) -> Operands:
+    """Draw A (M x K) and B (K x N, column-major) with separate seeds; for a
+    batch, entry g of each is drawn in turn from the same generator."""
+    ga, gb = rng(seed_a), rng(seed_b)
+    nb = max(batch, 1)
+    As, Bs, sa, sb = [], [], [], []
+    for _ in range(nb):
+        xa = draw(ga, (M, K), dist, K)
+        xb = draw(gb, (N, K), dist, K)
+        if fmt == "bf16":
+            As.append(to_bf16_codes(xa))
+            Bs.append(to_bf16_codes(xb))
+            sa.append(1.0)
+            sb.append(1.0)
+        elif fmt == "e4m3":
+            qa, s_a = to_e4m3_codes(xa)
+            qb, s_b = to_e4m3_codes(xb)
+            As.append(qa)
+            Bs.append(qb)
+            sa.append(s_a)
+            sb.append(s_b)
+        else:
+            raise ValueError(fmt)
+    if batch:
+        A, B = np.stack(As), np.stack(Bs)
+    else:
+        A, B = As[0], Bs[0]
+    return Operands(M, N, K, fmt, A, B, sa, sb, (seed_a, seed_b))
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A named synthetic workload: shapes, element format, value recipe."""
+    index: int
+    name: str
+    fmt: str
+    out: str                      # "f32" or "bf16"
+    dist: str
+    shapes: Tuple[Tuple[int, int, int], ...]
+    batch: int = 0
+
+
+# The synthetic workloads, numbered 1..5 (value recipes and shapes as named;
+# workload 5 has two parts: one 8192^3 product and a batch of 64 products,
+# the batch drawn with shape index 1).
+WORKLOADS = (
+    Workload(1, "bf16-256cube-f32", "bf16", "f32", "uniform", ((256, 256, 256),)),
+    Workload(2, "bf16-4096cube-bf16out", "bf16", "bf16", "normal", ((4096, 4096, 4096),)),
+    Workload(3, "bf16-ragged-f32", "bf16", "f32", "uniform",
+             ((4000, 4000, 4000), (4097, 4095, 4104), (1000, 3000, 777))),
+    Workload(4, "bf16-splitk-f32", "bf16", "f32", "normal_sqrtk",
+             ((256, 256, 65536), (128, 512, 131072), (64, 64, 262144))),
+    Workload(5, "e4m3-8192cube-f32", "e4m3", "f32", "normal", ((8192, 8192, 8192),)),
+    Workload(5, "e4m3-batch64-f32", "e4m3", "f32", "normal", ((512, 1024, 4096),), batch=64),
+)
+
+
+def workload_operands(w: Workload, shape_index: int = 0) -> Operands:
+    M, N, K = w.shapes[shape_index]
+    si = shape_index + (1 if w.batch else 0)
+    return make_operands(M, N, K, w.fmt, w.dist, seed_for(w.index, si, 0),
+                         seed_for(w.index, si, 1), batch=w.batch)
