@@ -1,0 +1,279 @@
+"""Benchmark of libgemm355 on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-detail] [--workload NAME]
+
+A step is one call of the library on the headline workload (bf16
+4096 x 4096 x 4096, A row-major, B column-major, bf16 C, fp32 accumulate)
+with inputs already resident in HBM.  Prints ONE JSON line: throughput in
+TFLOP/s of useful work 2MNK per step (section "Shape the operation" of page
+"10. Tensor Cores, shapes, and tile alignment"), the roofline of the main
+kernel (achieved vs the dense bf16 MFMA peak, timed with HIP events on the
+launch stream), the CPU oracle timed on a bounded sample, and a per-workload
+detail list (every named workload, each timed the same way, HBM-bound shapes
+rotating input copies so they cannot sit in the 256 MB last-level cache).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2}   # MI355X dense MFMA, 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+KERNEL_SOURCES = ["dense_tiled_gemm_fp8_amd/csrc/kernels.hip", "dense_tiled_gemm_fp8_amd/csrc/sched.h",
+                  "dense_tiled_gemm_fp8_amd/csrc/tiles.h", "dense_tiled_gemm_fp8_amd/csrc/plan.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bf16_4096cube.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--workload", default=None, help="time only this workload name (detail)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes 5 times "
+                         "(reference kernel for scaling the HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_reference(nbytes: int) -> None:
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy reference: 5 x %d bytes" % nbytes)
+
+
+class Case:
+    """Device-resident operands of one workload shape (with rotation copies
+    for HBM-bound shapes) and a callable that runs one step."""
+
+    def __init__(self, w, si, torch, g, inputs):
+        self.w, self.si = w, si
+        ops = inputs.workload_operands(w, si)
+        self.ops = ops
+        self.M, self.N, self.K, self.batch = ops.M, ops.N, ops.K, ops.batch
+        self.fmt = w.fmt
+        view = __import__("numpy").int16 if w.fmt == "bf16" else __import__("numpy").uint8
+        esize = 2 if w.fmt == "bf16" else 1
+        in_bytes = ops.A.nbytes + ops.B.nbytes
+        self.copies = 1
+        flops = 2.0 * self.M * self.N * self.K * self.batch
+        out_es = 2 if w.out == "bf16" else 4
+        self.alg_bytes = in_bytes + self.M * self.N * self.batch * out_es
+        self.flops = flops
+        ai = flops / self.alg_bytes
+        self.hbm_bound = ai < (PEAK_TFLOPS[w.fmt] * 1e12) / (PEAK_HBM_GBS * 1e9)
+        if self.hbm_bound:
+            self.copies = max(1, math.ceil(2 * MALL_BYTES / in_bytes))
+        A = torch.from_numpy(ops.A.view(view)).cuda()
+        B = torch.from_numpy(ops.B.view(view)).cuda()
+        self.As = [A] + [A.clone() for _ in range(self.copies - 1)]
+        self.Bs = [B] + [B.clone() for _ in range(self.copies - 1)]
+        shape = (self.batch, self.M, self.N) if self.batch > 1 else (self.M, self.N)
+        self.C = torch.empty(shape, dtype=torch.bfloat16 if w.out == "bf16" else torch.float32,
+                             device="cuda")
+        self.sa = torch.tensor(ops.scale_a, dtype=torch.float32, device="cuda") if w.fmt == "e4m3" else None
+        self.sb = torch.tensor(ops.scale_b, dtype=torch.float32, device="cuda") if w.fmt == "e4m3" else None
+        dt = {("bf16", "f32"): g.BF16_F32, ("bf16", "bf16"): g.BF16_BF16,
+              ("e4m3", "f32"): g.E4M3_F32, ("e4m3", "bf16"): g.E4M3_BF16}[(w.fmt, w.out)]
+        self.args = []
+        for i in range(self.copies):
+            a = g.make_args(self.M, self.N, self.K, A=self.As[i], B=self.Bs[i], C=self.C, dtype=dt,
+                            batch=self.batch, stride_a=self.M * self.K, stride_b=self.N * self.K,
+                            stride_c=self.M * self.N, scale_a=self.sa, scale_b=self.sb)
+            self.args.append(a)
+        self.plan = g.gemm355_plan(self.args[0])
+        if self.plan["workspace_bytes"]:
+            self.ws = torch.empty(self.plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+            for a in self.args:
+                a.workspace = self.ws.data_ptr()
+                a.workspace_bytes = self.plan["workspace_bytes"]
+        self.g = g
+        self.i = 0
+
+    def step(self, stream):
+        a = self.args[self.i % self.copies]
+        self.i += 1
+        self.g.gemm355_gemm_ex(a, stream)
+
+    def name(self):
+        shp = "%dx%dx%d" % (self.M, self.N, self.K)
+        if self.batch > 1:
+            shp = "%dx(%s)" % (self.batch, shp)
+        return "%s %s" % (self.w.name, shp)
+
+
+def time_case(case, torch, steps, warmup):
+    """Warm up, then time `steps` calls: wall clock around the whole region
+    (synchronised on both sides) and one HIP event pair per call on the
+    launch stream."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for _ in range(warmup):
+        case.step(sp)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        case.step(sp)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+    return wall, per
+
+
+def cpu_baseline(torch, budget_s=15.0):
+    """The oracle (as it stands) on a bounded sample of the headline product:
+    the first R rows of A against all of B, R sized from a short probe to
+    take roughly budget_s seconds."""
+    import numpy as np
+    from dense_tiled_gemm_fp8_amd import inputs
+    from oracle import reference as oracle
+    w = inputs.WORKLOADS[1]
+    ops = inputs.workload_operands(w)
+    M, N, K = ops.M, ops.N, ops.K
+    # two probes separate the fixed cost (decoding all of B) from the per-row cost
+    times = []
+    for r in (16, 48):
+        t0 = time.perf_counter()
+        oracle.gemm(r, N, K, ops.A[:r].reshape(-1), K, ops.B.reshape(-1), K)
+        times.append(time.perf_counter() - t0)
+    per_row = max((times[1] - times[0]) / 32, 1e-6)
+    fixed = max(times[0] - 16 * per_row, 0.0)
+    rows = int(min(M, max(16, (budget_s - fixed) / per_row)))
+    rows = max(16, rows // 16 * 16)
+    t0 = time.perf_counter()
+    oracle.gemm(rows, N, K, ops.A[:rows].reshape(-1), K, ops.B.reshape(-1), K)
+    t = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": "rows 0..%d of the bf16 4096x4096x4096 product (%d x 4096 x 4096 multiply-adds, "
+                      "binary64 triple loop, decode of all of B included), %.1f s" % (rows - 1, rows, t)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(the path would shard by output tiles, see the design notes)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.copy_bytes:
+        copy_reference(args.copy_bytes)
+        return
+    import numpy as np
+    import torch
+    from dense_tiled_gemm_fp8_amd import gemm355 as g
+    from dense_tiled_gemm_fp8_amd import inputs
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+
+    head_w = inputs.WORKLOADS[1]
+    log("bench: building inputs for", head_w.name)
+    head = Case(head_w, 0, torch, g, inputs)
+    log("bench: plan", {k: head.plan[k] for k in ("tile", "T_M", "T_N", "T_K", "G", "grid", "split")})
+    torch.cuda.synchronize()
+    # timed region: barrier (single rank) + synchronize on both sides
+    wall, per = time_case(head, torch, args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    value = head.flops * args.steps / wall / 1e12
+    kern_avg = sum(per) / len(per)
+    achieved = head.flops / kern_avg / 1e12
+    log("bench: %.3f ms/step wall, kernel avg %.2f us, %.1f TFLOP/s" % (ms_per_step, kern_avg * 1e6, achieved))
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    detail = []
+    if not args.no_detail:
+        for w in inputs.WORKLOADS:
+            for si in range(len(w.shapes)):
+                if args.workload and args.workload != w.name:
+                    continue
+                log("bench: detail", w.name, w.shapes[si])
+                c = head if (w is head_w and si == 0) else Case(w, si, torch, g, inputs)
+                _, pc = time_case(c, torch, max(10, args.steps // 2), max(3, args.warmup // 2))
+                med = pc[len(pc) // 2]
+                p = c.plan
+                detail.append({
+                    "workload": c.name(), "dtype": w.fmt, "out": w.out,
+                    "us_median": round(med * 1e6, 2), "us_min": round(pc[0] * 1e6, 2),
+                    "tflops": round(c.flops / med / 1e12, 1),
+                    "pct_mfma_peak": round(100 * c.flops / med / 1e12 / PEAK_TFLOPS[w.fmt], 1),
+                    "hbm_gbs": round(c.alg_bytes / med / 1e9, 1),
+                    "bound": "hbm" if c.hbm_bound else "mfma", "rotated_copies": c.copies,
+                    "tile": [p["T_M"], p["T_N"], p["T_K"]], "b": p["b"], "split": p["split"],
+                    "persistent": p["persistent"], "tail": [p["tail_tiles"], p["tail_split"]],
+                    "grid": p["grid"], "units": p["units"],
+                    "eta_wave": [p["eta_wave_num"], p["eta_wave_den"]],
+                    "eta_pad": [p["eta_pad_num"], p["eta_pad_den"]],
+                    "eta_sched": [p["eta_sched_num"], p["eta_sched_den"]],
+                })
+                if c is not head:
+                    del c
+                    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(torch)
+
+    p = head.plan
+    line = {
+        "metric": "GEMM TFLOP/s and % of MFMA peak (bf16 4096^3; skinny split-K shapes)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "bf16 GEMM 4096x4096x4096, A row-major, B column-major, C bf16, "
+                               "fp32 accumulate, entries N(0,1) rounded to bf16",
+                   "M": 4096, "N": 4096, "K": 4096, "tile": [p["T_M"], p["T_N"], p["T_K"]],
+                   "grid": p["grid"], "split_k": p["split"],
+                   "eta_wave": p["eta_wave_num"] / p["eta_wave_den"],
+                   "eta_pad": p["eta_pad_num"] / p["eta_pad_den"]},
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic, "kernel_us": round(kern_avg * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

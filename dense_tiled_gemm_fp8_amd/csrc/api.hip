@@ -1,0 +1,432 @@
+/*
+ * api.hip -- the C ABI of libgemm355 (declared in include/gemm355.h).
+ *
+ * A call validates and plans on the host (plans are cached per argument
+ * shape), then enqueues on the caller's stream: optional operand repacks,
+ * the main MFMA kernel over the plan's work units, and for split-K (or a
+ * split tail of a persistent grid) the combine kernel.  Nothing here blocks
+ * the host except the first use of a device (property query) and the growth
+ * of library-owned scratch.
+ */
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <unordered_map>
+
+#include "../../include/gemm355.h"
+#include "kernels.h"
+#include "plan.h"
+#include "tiles.h"
+
+using namespace g355;
+
+namespace {
+
+std::mutex g_mu;
+
+int32_t device_cus()
+{
+    static std::map<int, int32_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    hipDeviceProp_t prop;
+    int32_t cus = 256;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+        cus = prop.multiProcessorCount;
+    cache[dev] = cus;
+    return cus;
+}
+
+int32_t planning_cus(const gemm355_args &a)
+{
+    if (a.cus > 0) return a.cus;
+    if (a.cus < 0) return -1;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return device_cus();
+}
+
+/* Plan cache: the plan depends on the shape arguments, the knobs and the
+ * 16-byte alignment of A and B, never on the data. */
+struct PlanKey {
+    int64_t v[16];
+    bool operator==(const PlanKey &o) const { return memcmp(v, o.v, sizeof v) == 0; }
+};
+struct PlanKeyHash {
+    size_t operator()(const PlanKey &k) const
+    {
+        uint64_t h = 1469598103934665603ull;
+        for (int64_t x : k.v) {
+            h ^= (uint64_t)x;
+            h *= 1099511628211ull;
+        }
+        return (size_t)h;
+    }
+};
+std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
+
+PlanKey key_of(const gemm355_args &a, int32_t S)
+{
+    PlanKey k;
+    memset(&k, 0, sizeof k);
+    k.v[0] = a.M;
+    k.v[1] = a.N;
+    k.v[2] = a.K;
+    k.v[3] = a.lda;
+    k.v[4] = a.ldb;
+    k.v[5] = a.ldc;
+    k.v[6] = a.stride_a;
+    k.v[7] = a.stride_b;
+    k.v[8] = a.stride_c;
+    k.v[9] = a.batch;
+    k.v[10] = ((int64_t)a.dtype << 8) | (int64_t)a.layout;
+    k.v[11] = ((int64_t)a.split_k << 32) | (uint32_t)(a.persistent + 1);
+    k.v[12] = ((int64_t)a.tile << 32) | (uint32_t)S;
+    k.v[13] = (int64_t)(((uintptr_t)a.A & 15u) | (((uintptr_t)a.B & 15u) << 4) |
+                        (((uintptr_t)a.C & 15u) << 8) | (((uintptr_t)a.scale_a & 3u) << 12) |
+                        (((uintptr_t)a.scale_b & 3u) << 14));
+    /* null-ness matters for validation */
+    k.v[14] = (a.A ? 1 : 0) | (a.B ? 2 : 0) | (a.C ? 4 : 0);
+    return k;
+}
+
+gemm355_status get_plan(const gemm355_args &a, Plan &out)
+{
+    const int32_t S = planning_cus(a);
+    if (S < 1) return GEMM355_EINVAL;
+    const PlanKey k = key_of(a, S);
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_plans.find(k);
+        if (it != g_plans.end()) {
+            out = it->second;
+            return check_pointers(a);
+        }
+    }
+    gemm355_status st = make_plan(a, S, out);
+    if (st != GEMM355_OK) return st;
+    /* pointer overlap is not part of the key: check_pointers runs on hits */
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_plans.size() > 4096) g_plans.clear();
+    g_plans.emplace(k, out);
+    return GEMM355_OK;
+}
+
+/* Library-owned scratch, one buffer per (device, stream), grown on demand. */
+struct Scratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, void *>, Scratch> g_scratch;
+
+gemm355_status library_scratch(size_t need, void *stream, void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM355_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Scratch &s = g_scratch[{dev, stream}];
+    if (s.bytes < need) {
+        if (s.ptr) {
+            /* earlier calls on this stream may still read the old buffer */
+            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GEMM355_EHIP;
+            (void)hipFree(s.ptr);
+            s.ptr = nullptr;
+            s.bytes = 0;
+        }
+        size_t grow = need + need / 4;
+        if (hipMalloc(&s.ptr, grow) != hipSuccess) {
+            (void)hipGetLastError();
+            s.ptr = nullptr;
+            return GEMM355_ENOMEM;
+        }
+        s.bytes = grow;
+    }
+    *out = s.ptr;
+    return GEMM355_OK;
+}
+
+struct ScratchReaper {
+    ~ScratchReaper()
+    {
+        for (auto &kv : g_scratch)
+            if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    }
+} g_reaper;
+
+gemm355_status run(const gemm355_args &a, void *stream)
+{
+    Plan P;
+    gemm355_status st = get_plan(a, P);
+    if (st != GEMM355_OK) return st;
+    if (a.M == 0 || a.N == 0) return GEMM355_OK;
+    hipStream_t hs = (hipStream_t)stream;
+
+    if (a.K == 0) {
+        if (launch_zero(a.C, (int32_t)a.M, (int32_t)a.N, a.ldc, a.stride_c, (int32_t)a.batch,
+                        P.out_esize, hs) != hipSuccess)
+            return GEMM355_EHIP;
+        return GEMM355_OK;
+    }
+
+    uint8_t *ws = nullptr;
+    if (P.pub.workspace_bytes) {
+        if (a.workspace) {
+            if (a.workspace_bytes < P.pub.workspace_bytes) return GEMM355_ENOMEM;
+            if (((uintptr_t)a.workspace & 255u) != 0) return GEMM355_EALIGN;
+            ws = (uint8_t *)a.workspace;
+        } else {
+            void *p = nullptr;
+            st = library_scratch(P.pub.workspace_bytes, stream, &p);
+            if (st != GEMM355_OK) return st;
+            ws = (uint8_t *)p;
+        }
+    }
+
+    const uint8_t *Aop = (const uint8_t *)a.A;
+    const uint8_t *Bop = (const uint8_t *)a.B;
+    const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
+    const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
+    if (P.pack_a) {
+        PackParams pk;
+        pk.src = a.A;
+        pk.dst = ws + P.ws_pack_a_off;
+        pk.ld = a.lda;
+        pk.stride = a.stride_a;
+        pk.ldd_bytes = P.lda_b;
+        pk.dst_stride_bytes = P.stride_a_b;
+        pk.rows = (int32_t)a.M;
+        pk.K = (int32_t)a.K;
+        pk.batch = (int32_t)a.batch;
+        pk.esize = P.esize;
+        pk.kmajor = a_row ? 1 : 0;
+        if (launch_pack(pk, hs) != hipSuccess) return GEMM355_EHIP;
+        Aop = pk.dst;
+    }
+    if (P.pack_b) {
+        PackParams pk;
+        pk.src = a.B;
+        pk.dst = ws + P.ws_pack_b_off;
+        pk.ld = a.ldb;
+        pk.stride = a.stride_b;
+        pk.ldd_bytes = P.ldb_b;
+        pk.dst_stride_bytes = P.stride_b_b;
+        pk.rows = (int32_t)a.N;
+        pk.K = (int32_t)a.K;
+        pk.batch = (int32_t)a.batch;
+        pk.esize = P.esize;
+        pk.kmajor = b_col ? 1 : 0;
+        if (launch_pack(pk, hs) != hipSuccess) return GEMM355_EHIP;
+        Bop = pk.dst;
+    }
+
+    GemmParams gp;
+    gp.A = Aop;
+    gp.B = Bop;
+    gp.C = a.C;
+    gp.ws = (float *)(ws ? ws + P.ws_partial_off : nullptr);
+    gp.lda = P.lda_b;
+    gp.ldb = P.ldb_b;
+    gp.stride_a = P.stride_a_b;
+    gp.stride_b = P.stride_b_b;
+    gp.ldc = a.ldc;
+    gp.stride_c = a.stride_c;
+    gp.scale_a = a.scale_a;
+    gp.scale_b = a.scale_b;
+    gp.M = (int32_t)a.M;
+    gp.N = (int32_t)a.N;
+    gp.Kb = P.Kb;
+    gp.out_bf16 = P.out_esize == 2 ? 1 : 0;
+    gp.s = P.s;
+    if (P.s.grid > 0 && launch_gemm(P.pub.tile, gp, hs) != hipSuccess) return GEMM355_EHIP;
+
+    if (P.reduce_tiles > 0) {
+        ReduceParams rp;
+        rp.ws = gp.ws;
+        rp.C = a.C;
+        rp.ldc = a.ldc;
+        rp.stride_c = a.stride_c;
+        rp.scale_a = a.scale_a;
+        rp.scale_b = a.scale_b;
+        rp.M = (int32_t)a.M;
+        rp.N = (int32_t)a.N;
+        rp.TM = P.pub.T_M;
+        rp.TN = P.pub.T_N;
+        rp.out_bf16 = gp.out_bf16;
+        rp.tail = P.reduce_tail;
+        rp.s = P.s;
+        if (launch_reduce(rp, P.reduce_tiles, hs) != hipSuccess) return GEMM355_EHIP;
+    }
+    return GEMM355_OK;
+}
+
+} /* namespace */
+
+extern "C" {
+
+gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                            const void *B, int64_t ldb, void *C, int64_t ldc, gemm355_dtype dtype,
+                            gemm355_layout layout, int32_t split_k, int32_t persistent,
+                            void *stream)
+{
+    gemm355_args a;
+    memset(&a, 0, sizeof a);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = A;
+    a.lda = lda;
+    a.B = B;
+    a.ldb = ldb;
+    a.C = C;
+    a.ldc = ldc;
+    a.batch = 1;
+    a.dtype = dtype;
+    a.layout = layout;
+    a.split_k = split_k;
+    a.persistent = persistent;
+    a.tile = -1;
+    return run(a, stream);
+}
+
+gemm355_status gemm355_gemm_ex(const gemm355_args *args, void *stream)
+{
+    if (!args) return GEMM355_EINVAL;
+    return run(*args, stream);
+}
+
+gemm355_status gemm355_plan(const gemm355_args *args, gemm355_plan_t *out)
+{
+    if (!args || !out) return GEMM355_EINVAL;
+    Plan P;
+    gemm355_status st = get_plan(*args, P);
+    if (st != GEMM355_OK) return st;
+    *out = P.pub;
+    return GEMM355_OK;
+}
+
+double gemm355_eta_wave(int64_t G, int32_t S, int32_t b)
+{
+    if (G < 1 || S < 1 || b < 1) return NAN;
+    const uint64_t cap = (uint64_t)S * (uint64_t)b;
+    const uint64_t waves = ((uint64_t)G + cap - 1) / cap;
+    const uint64_t den = waves * cap;
+    uint64_t num = (uint64_t)G, d = den, x = num, y = d;
+    while (y) {
+        const uint64_t t = x % y;
+        x = y;
+        y = t;
+    }
+    return rational_to_double(num / x, d / x);
+}
+
+double gemm355_eta_pad(int64_t M, int64_t N, int64_t K, int64_t T_M, int64_t T_N, int64_t T_K)
+{
+    if (M < 1 || N < 1 || K < 1 || T_M < 1 || T_N < 1 || T_K < 1) return NAN;
+    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return NAN;
+    /* reduce each factor, then cross-reduce, to keep the rational in 64 bits */
+    uint64_t num[3] = {(uint64_t)M, (uint64_t)N, (uint64_t)K};
+    uint64_t den[3] = {(uint64_t)((M + T_M - 1) / T_M * T_M), (uint64_t)((N + T_N - 1) / T_N * T_N),
+                       (uint64_t)((K + T_K - 1) / T_K * T_K)};
+    auto gcd = [](uint64_t x, uint64_t y) {
+        while (y) {
+            const uint64_t t = x % y;
+            x = y;
+            y = t;
+        }
+        return x;
+    };
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            const uint64_t g = gcd(num[i], den[j]);
+            num[i] /= g;
+            den[j] /= g;
+        }
+    unsigned __int128 n = (unsigned __int128)num[0] * num[1] * num[2];
+    unsigned __int128 d = (unsigned __int128)den[0] * den[1] * den[2];
+    /* exact (nearest binary64) whenever the reduced denominator fits in 64
+     * bits, i.e. always when M'N'K' < 2^64; beyond that within one ulp */
+    if (d >> 64) return (double)((long double)n / (long double)d);
+    return rational_to_double((uint64_t)n, (uint64_t)d);
+}
+
+gemm355_status gemm355_kslice(int64_t nK, int32_t s, int32_t i, int64_t *begin, int64_t *end)
+{
+    if (!begin || !end || nK < 0 || s < 1 || i < 0 || i >= s) return GEMM355_EINVAL;
+    *begin = (int64_t)(((unsigned __int128)i * (uint64_t)nK) / (uint64_t)s);
+    *end = (int64_t)(((unsigned __int128)(i + 1) * (uint64_t)nK) / (uint64_t)s);
+    return GEMM355_OK;
+}
+
+gemm355_status gemm355_unit(const gemm355_args *args, int64_t u, int64_t *batch, int64_t *tile_m,
+                            int64_t *tile_n, int64_t *kt_begin, int64_t *kt_end)
+{
+    if (!args || !batch || !tile_m || !tile_n || !kt_begin || !kt_end) return GEMM355_EINVAL;
+    Plan P;
+    gemm355_status st = get_plan(*args, P);
+    if (st != GEMM355_OK) return st;
+    if (u < 0 || u >= P.s.units) return GEMM355_EINVAL;
+    const Unit un = decode_unit(P.s, (int32_t)u);
+    *batch = un.batch;
+    *tile_m = un.tile_m;
+    *tile_n = un.tile_n;
+    *kt_begin = un.kt_begin;
+    *kt_end = un.kt_end;
+    return GEMM355_OK;
+}
+
+int32_t gemm355_num_tiles(void) { return kNumTiles; }
+
+gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_M, int32_t *T_N,
+                                 int32_t *T_K, int32_t *stages, int32_t *waves, int32_t *lds_bytes,
+                                 int32_t *b_max)
+{
+    if (tile < 0 || tile >= kNumTiles) return GEMM355_EINVAL;
+    const TileCfg &c = kTiles[tile];
+    if (dtype_class) *dtype_class = c.dtype_class;
+    if (T_M) *T_M = c.TM;
+    if (T_N) *T_N = c.TN;
+    if (T_K) *T_K = c.TK;
+    if (stages) *stages = c.stages;
+    if (waves) *waves = c.waves_m * c.waves_n;
+    if (lds_bytes) *lds_bytes = c.lds_bytes;
+    if (b_max) *b_max = resident_workgroups(tile);
+    return GEMM355_OK;
+}
+
+gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu)
+{
+    if (tile < 0 || tile >= kNumTiles || !blocks_per_cu) return GEMM355_EINVAL;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel_symbol(tile), 256, 0) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM355_EHIP;
+    }
+    *blocks_per_cu = n;
+    return GEMM355_OK;
+}
+
+const char *gemm355_status_string(gemm355_status status)
+{
+    switch (status) {
+    case GEMM355_OK: return "ok";
+    case GEMM355_EINVAL: return "invalid argument";
+    case GEMM355_EALIGN: return "misaligned pointer";
+    case GEMM355_EUNSUPPORTED: return "unsupported size";
+    case GEMM355_ENOMEM: return "workspace too small or allocation failed";
+    case GEMM355_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+} /* extern "C" */

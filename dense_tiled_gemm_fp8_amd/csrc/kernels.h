@@ -1,0 +1,61 @@
+/*
+ * kernels.h -- launch interface between the host side of libgemm355 and its
+ * gfx950 kernels.  Internal; not part of the C ABI.
+ */
+#ifndef GEMM355_KERNELS_H
+#define GEMM355_KERNELS_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sched.h"
+
+namespace g355 {
+
+/* Main loop.  A and B are K-contiguous: row r of the A tile (column r of B)
+ * starts lda (ldb) bytes after row r-1; both 16-byte aligned. */
+struct GemmParams {
+    const uint8_t *A;
+    const uint8_t *B;
+    void *C;
+    float *ws;                    /* partial slots [slot][TM*TN] fp32      */
+    int64_t lda, ldb;             /* bytes                                  */
+    int64_t stride_a, stride_b;   /* bytes between batch entries            */
+    int64_t ldc, stride_c;        /* elements of C                          */
+    const float *scale_a, *scale_b;
+    int32_t M, N, Kb;             /* Kb: K in bytes (multiple of 16)        */
+    int32_t out_bf16;
+    Sched s;
+};
+
+struct ReduceParams {
+    const float *ws;
+    void *C;
+    int64_t ldc, stride_c;
+    const float *scale_a, *scale_b;
+    int32_t M, N, TM, TN;
+    int32_t out_bf16;
+    int32_t tail;                 /* 1: reduce the tail tiles, 0: all tiles */
+    Sched s;
+};
+
+struct PackParams {
+    const void *src;
+    uint8_t *dst;
+    int64_t ld, stride;           /* source, elements                       */
+    int64_t ldd_bytes;            /* destination row pitch, multiple of 16  */
+    int64_t dst_stride_bytes;
+    int32_t rows, K, batch, esize;
+    int32_t kmajor;               /* 1: source K-contiguous                 */
+};
+
+hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream);
+const void *gemm_kernel_symbol(int32_t tile);
+hipError_t launch_reduce(const ReduceParams &r, int32_t tiles, hipStream_t stream);
+hipError_t launch_pack(const PackParams &pk, hipStream_t stream);
+hipError_t launch_zero(void *C, int32_t M, int32_t N, int64_t ldc, int64_t stride_c,
+                       int32_t batch, int32_t esize, hipStream_t stream);
+
+} /* namespace g355 */
+
+#endif

@@ -1,0 +1,47 @@
+/*
+ * plan.h -- the host planner of libgemm355 (internal).
+ */
+#ifndef GEMM355_PLAN_H
+#define GEMM355_PLAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gemm355.h"
+#include "sched.h"
+
+namespace g355 {
+
+struct Plan {
+    gemm355_plan_t pub;
+    Sched s;
+    int32_t esize;              /* input element bytes (2 bf16, 1 E4M3)     */
+    int32_t out_esize;          /* 4 fp32, 2 bf16                           */
+    int32_t Kb;                 /* K bytes seen by the main loop            */
+    int32_t pack_a, pack_b;
+    /* operand views the main loop reads (bytes) */
+    int64_t lda_b, ldb_b, stride_a_b, stride_b_b;
+    /* workspace carve-up (byte offsets) */
+    size_t ws_partial_off, ws_partial_bytes;
+    size_t ws_pack_a_off, ws_pack_a_bytes;
+    size_t ws_pack_b_off, ws_pack_b_bytes;
+    int32_t reduce_tiles;       /* blocks of the combine kernel (0: none)   */
+    int32_t reduce_tail;        /* 1: combine the tail tiles                */
+};
+
+/* Validate `a` and plan it for S compute units.  Never touches a device. */
+gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &out);
+
+/* Null, alignment and overlap checks of the pointers in `a` (run on every
+ * call, also when the plan comes from the cache). */
+gemm355_status check_pointers(const gemm355_args &a);
+
+/* Exact rational -> nearest binary64 (ties to even). */
+double rational_to_double(uint64_t num, uint64_t den);
+
+/* Resident workgroups per compute unit for a tile-table entry. */
+int32_t resident_workgroups(int32_t tile);
+
+} /* namespace g355 */
+
+#endif

@@ -1,0 +1,56 @@
+/*
+ * tiles.h -- the tile-shape table.
+ *
+ * Each entry is one instantiation of the MFMA main loop: output tile
+ * T_M x T_N, K-step T_K, LDS ring depth, wavefront grid, and the resources
+ * that fix how many workgroups a compute unit holds (page "Grid 24 is not
+ * headroom", section "The question I never asked": resident workgroups are
+ * the minimum over shared memory and the register file).
+ *
+ * Every entry stages 128 bytes of K per tile row per stage (64 bf16 or 128
+ * E4M3 values), so the LDS layout and the copy pattern are the same for both
+ * input types.
+ */
+#ifndef GEMM355_TILES_H
+#define GEMM355_TILES_H
+
+#include <stdint.h>
+
+namespace g355 {
+
+struct TileCfg {
+    int32_t dtype_class;   /* 0 bf16 inputs, 1 E4M3 inputs                  */
+    int32_t TM, TN, TK;
+    int32_t stages;
+    int32_t waves_m, waves_n;
+    int32_t lds_bytes;     /* stages * (TM + TN) * 128                       */
+    int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
+    int32_t vgpr_budget;   /* 512 / min_blocks (one wave per SIMD per group) */
+    /* planning prior: fraction of a compute unit's dense MFMA peak the tile
+     * sustains with 1, 2, 3, 4 of its workgroups resident on the unit */
+    float mfma_eff[4];
+};
+
+/* gfx950 compute-unit resources used by the occupancy arithmetic. */
+constexpr int32_t kLdsPerCu = 160 * 1024;
+constexpr int32_t kRegsPerLanePerSimd = 512;
+constexpr int32_t kRegGranule = 8;
+constexpr int32_t kSimdsPerCu = 4;
+constexpr int32_t kWaveSize = 64;
+constexpr int32_t kMaxWavesPerSimd = 8;
+
+constexpr TileCfg kTiles[] = {
+    /* bf16 */
+    {0, 256, 256, 64, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
+    {0, 128, 128, 64, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
+    {0, 64, 64, 64, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+    /* E4M3 */
+    {1, 256, 256, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
+    {1, 128, 128, 128, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
+    {1, 64, 64, 128, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+};
+constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
+
+} /* namespace g355 */
+
+#endif

@@ -1,0 +1,196 @@
+"""ctypes binding of libgemm355 (include/gemm355.h): argument marshalling only.
+
+Every function here has the name of the C entry point it wraps and does no
+arithmetic of its own: all work runs in the library's HIP kernels.  Pointers
+may be passed as torch tensors (their ``data_ptr()``) or plain integers;
+``stream=None`` means torch's current stream on the current device.
+
+Importing this module loads ``libgemm355.so`` and raises ImportError if it
+has not been built (``python -m dense_tiled_gemm_fp8_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Any, Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm355.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgemm355.so is not built; run python -m dense_tiled_gemm_fp8_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# status codes
+OK, EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP = range(6)
+# dtypes (input -> output)
+BF16_F32, BF16_BF16, E4M3_F32, E4M3_BF16 = range(4)
+# layouts
+A_ROW_B_COL, A_ROW_B_ROW, A_COL_B_COL, A_COL_B_ROW = range(4)
+
+_i64, _i32, _vp, _f64, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double, ctypes.c_size_t
+
+
+class gemm355_args(ctypes.Structure):
+    _fields_ = [
+        ("M", _i64), ("N", _i64), ("K", _i64),
+        ("A", _vp), ("lda", _i64), ("stride_a", _i64),
+        ("B", _vp), ("ldb", _i64), ("stride_b", _i64),
+        ("C", _vp), ("ldc", _i64), ("stride_c", _i64),
+        ("batch", _i64),
+        ("scale_a", _vp), ("scale_b", _vp),
+        ("dtype", ctypes.c_int), ("layout", ctypes.c_int),
+        ("split_k", _i32), ("persistent", _i32), ("tile", _i32), ("cus", _i32),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
+class gemm355_plan_t(ctypes.Structure):
+    _fields_ = [
+        ("tile", _i32), ("T_M", _i32), ("T_N", _i32), ("T_K", _i32),
+        ("stages", _i32), ("waves", _i32), ("lds_bytes", _i32), ("vgpr_budget", _i32),
+        ("S", _i32), ("b", _i32),
+        ("G", _i64), ("nK", _i64), ("M_pad", _i64), ("N_pad", _i64), ("K_pad", _i64),
+        ("split", _i32), ("persistent", _i32),
+        ("tail_tiles", _i64), ("tail_split", _i32), ("repack", _i32),
+        ("units", _i64), ("grid", _i64),
+        ("eta_wave_num", _i64), ("eta_wave_den", _i64),
+        ("eta_pad_num", _i64), ("eta_pad_den", _i64),
+        ("eta_sched_num", _i64), ("eta_sched_den", _i64),
+        ("workspace_bytes", _sz),
+    ]
+
+
+_lib.gemm355_gemm.restype = ctypes.c_int
+_lib.gemm355_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                              ctypes.c_int, ctypes.c_int, _i32, _i32, _vp]
+_lib.gemm355_gemm_ex.restype = ctypes.c_int
+_lib.gemm355_gemm_ex.argtypes = [ctypes.POINTER(gemm355_args), _vp]
+_lib.gemm355_plan.restype = ctypes.c_int
+_lib.gemm355_plan.argtypes = [ctypes.POINTER(gemm355_args), ctypes.POINTER(gemm355_plan_t)]
+_lib.gemm355_eta_wave.restype = _f64
+_lib.gemm355_eta_wave.argtypes = [_i64, _i32, _i32]
+_lib.gemm355_eta_pad.restype = _f64
+_lib.gemm355_eta_pad.argtypes = [_i64] * 6
+_lib.gemm355_kslice.restype = ctypes.c_int
+_lib.gemm355_kslice.argtypes = [_i64, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+_lib.gemm355_unit.restype = ctypes.c_int
+_lib.gemm355_unit.argtypes = [ctypes.POINTER(gemm355_args), _i64] + [ctypes.POINTER(_i64)] * 5
+_lib.gemm355_num_tiles.restype = _i32
+_lib.gemm355_num_tiles.argtypes = []
+_lib.gemm355_tile_info.restype = ctypes.c_int
+_lib.gemm355_tile_info.argtypes = [_i32] + [ctypes.POINTER(_i32)] * 8
+_lib.gemm355_tile_occupancy.restype = ctypes.c_int
+_lib.gemm355_tile_occupancy.argtypes = [_i32, ctypes.POINTER(_i32)]
+_lib.gemm355_status_string.restype = ctypes.c_char_p
+_lib.gemm355_status_string.argtypes = [ctypes.c_int]
+
+EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_plan", "gemm355_eta_wave",
+            "gemm355_eta_pad", "gemm355_kslice", "gemm355_unit", "gemm355_num_tiles",
+            "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_status_string")
+
+
+class Gemm355Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, gemm355_status_string(status), status))
+
+
+def _ptr(x: Any) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream: Any) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return int(torch.cuda.current_stream().cuda_stream)
+        return None
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Gemm355Error(status, where)
+
+
+def gemm355_status_string(status: int) -> str:
+    return _lib.gemm355_status_string(status).decode()
+
+
+def gemm355_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, layout=A_ROW_B_COL, split_k=0,
+                 persistent=-1, stream=None) -> None:
+    _check(_lib.gemm355_gemm(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, dtype, layout,
+                             split_k, persistent, _stream(stream)), "gemm355_gemm")
+
+
+def make_args(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, dtype=BF16_F32,
+              layout=A_ROW_B_COL, batch=1, stride_a=0, stride_b=0, stride_c=0, scale_a=None,
+              scale_b=None, split_k=0, persistent=-1, tile=-1, cus=0, workspace=None,
+              workspace_bytes=0) -> gemm355_args:
+    """Fill a gemm355_args; leading dimensions default to the packed ones."""
+    a_row = layout in (A_ROW_B_COL, A_ROW_B_ROW)
+    b_col = layout in (A_ROW_B_COL, A_COL_B_COL)
+    if lda is None:
+        lda = max(1, K if a_row else M)
+    if ldb is None:
+        ldb = max(1, K if b_col else N)
+    if ldc is None:
+        ldc = max(1, N)
+    return gemm355_args(M, N, K, _ptr(A), lda, stride_a, _ptr(B), ldb, stride_b, _ptr(C), ldc,
+                        stride_c, batch, _ptr(scale_a), _ptr(scale_b), dtype, layout, split_k,
+                        persistent, tile, cus, _ptr(workspace), workspace_bytes)
+
+
+def gemm355_gemm_ex(args: gemm355_args, stream=None) -> None:
+    _check(_lib.gemm355_gemm_ex(ctypes.byref(args), _stream(stream)), "gemm355_gemm_ex")
+
+
+def gemm355_plan(args: gemm355_args) -> Dict[str, int]:
+    out = gemm355_plan_t()
+    _check(_lib.gemm355_plan(ctypes.byref(args), ctypes.byref(out)), "gemm355_plan")
+    return {name: getattr(out, name) for name, _ in gemm355_plan_t._fields_}
+
+
+def gemm355_eta_wave(G: int, S: int, b: int) -> float:
+    return _lib.gemm355_eta_wave(G, S, b)
+
+
+def gemm355_eta_pad(M: int, N: int, K: int, T_M: int, T_N: int, T_K: int) -> float:
+    return _lib.gemm355_eta_pad(M, N, K, T_M, T_N, T_K)
+
+
+def gemm355_kslice(nK: int, s: int, i: int):
+    b, e = _i64(), _i64()
+    _check(_lib.gemm355_kslice(nK, s, i, ctypes.byref(b), ctypes.byref(e)), "gemm355_kslice")
+    return b.value, e.value
+
+
+def gemm355_unit(args: gemm355_args, u: int):
+    vals = [_i64() for _ in range(5)]
+    _check(_lib.gemm355_unit(ctypes.byref(args), u, *[ctypes.byref(v) for v in vals]),
+           "gemm355_unit")
+    return tuple(v.value for v in vals)   # batch, tile_m, tile_n, kt_begin, kt_end
+
+
+def gemm355_num_tiles() -> int:
+    return _lib.gemm355_num_tiles()
+
+
+def gemm355_tile_info(tile: int) -> Dict[str, int]:
+    vals = [_i32() for _ in range(8)]
+    _check(_lib.gemm355_tile_info(tile, *[ctypes.byref(v) for v in vals]), "gemm355_tile_info")
+    names = ("dtype_class", "T_M", "T_N", "T_K", "stages", "waves", "lds_bytes", "b_max")
+    return dict(zip(names, (v.value for v in vals)))
+
+
+def gemm355_tile_occupancy(tile: int) -> int:
+    n = _i32()
+    _check(_lib.gemm355_tile_occupancy(tile, ctypes.byref(n)), "gemm355_tile_occupancy")
+    return n.value

@@ -1,0 +1,221 @@
+/*
+ * gemm355.h -- C ABI of libgemm355, a tiled dense matrix product for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation (page "10. Tensor Cores, shapes, and tile alignment", section
+ * "Shape the operation", the problem statement and the FLOPs equation):
+ *
+ *     C[M x N] = alpha * A[M x K] * B[K x N]        (useful work 2MNK)
+ *
+ * with low-precision inputs and an fp32 accumulator (page "The Tensor Core",
+ * the input/accumulate table: BF16 in the Ampere row, FP8 E4M3 in the Hopper
+ * row, both accumulating in FP32).  C is overwritten (no beta term).  alpha
+ * is 1 unless per-tensor scales are passed (scale_a[g] * scale_b[g] for
+ * batch entry g), which is how E4M3 operands are dequantised.
+ *
+ * Conventions for every entry point:
+ *   - Dimensions, leading dimensions and strides are counted in ELEMENTS of
+ *     the operand's type.  C is row-major: C(i,j) is at C[i*ldc + j].
+ *   - A, B, C, the scales and any workspace are device memory owned by the
+ *     caller.  The library never frees them and keeps no reference after the
+ *     call returns.  A and B are only read; C is only written.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL means the null
+ *     stream).  Argument errors are reported before anything is launched;
+ *     faults inside kernels surface at the caller's next synchronisation.
+ *   - No entry point aborts, prints or throws; each returns a status code.
+ *   - All entry points are thread-safe.
+ */
+#ifndef GEMM355_H
+#define GEMM355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM355_API __attribute__((visibility("default")))
+
+typedef enum gemm355_status {
+    GEMM355_OK = 0,
+    GEMM355_EINVAL = 1,        /* bad size, leading dimension, pointer, enum,
+                                  split factor, or C overlapping A/B */
+    GEMM355_EALIGN = 2,        /* pointer not aligned to its element size */
+    GEMM355_EUNSUPPORTED = 3,  /* extents beyond the 32-bit offsets the
+                                  kernels use, or an unknown tile id */
+    GEMM355_ENOMEM = 4,        /* caller workspace smaller than the plan's
+                                  workspace_bytes, or allocation failed */
+    GEMM355_EHIP = 5           /* a HIP runtime call failed (no device,
+                                  launch failure) */
+} gemm355_status;
+
+/* Element types, input -> output. */
+typedef enum gemm355_dtype {
+    GEMM355_BF16_F32 = 0,   /* bf16 A, B; fp32 C                              */
+    GEMM355_BF16_BF16 = 1,  /* bf16 A, B; bf16 C (fp32 result rounded to
+                               nearest even)                                  */
+    GEMM355_E4M3_F32 = 2,   /* OCP E4M3FN A, B (max 448, no infinities); fp32 C */
+    GEMM355_E4M3_BF16 = 3   /* OCP E4M3FN A, B; bf16 C                        */
+} gemm355_dtype;
+
+/* Operand storage (the row/column vocabulary of the sweep command in
+ * section "Practical shape sweep"):
+ *   A row-major:    a(i,k) = A[i*lda + k], lda >= K
+ *   A column-major: a(i,k) = A[k*lda + i], lda >= M
+ *   B column-major: b(k,j) = B[j*ldb + k], ldb >= K
+ *   B row-major:    b(k,j) = B[k*ldb + j], ldb >= N
+ * A row-major with B column-major (both K-contiguous) is the native layout;
+ * the other three are first repacked into it on the device (counted in the
+ * call's time). */
+typedef enum gemm355_layout {
+    GEMM355_A_ROW_B_COL = 0,
+    GEMM355_A_ROW_B_ROW = 1,
+    GEMM355_A_COL_B_COL = 2,
+    GEMM355_A_COL_B_ROW = 3
+} gemm355_layout;
+
+/* Full argument set (strided batch, scales, workspace, tuning knobs). */
+typedef struct gemm355_args {
+    int64_t M, N, K;
+    const void *A;  int64_t lda; int64_t stride_a;  /* stride_*: elements  */
+    const void *B;  int64_t ldb; int64_t stride_b;  /* between consecutive */
+    void *C;        int64_t ldc; int64_t stride_c;  /* batch entries       */
+    int64_t batch;                 /* >= 1 independent products           */
+    const float *scale_a;          /* device fp32 [batch] or NULL (= 1.0)  */
+    const float *scale_b;          /* device fp32 [batch] or NULL (= 1.0)  */
+    gemm355_dtype dtype;
+    gemm355_layout layout;
+    int32_t split_k;     /* 0: automatic; 1: off; s >= 2: cut K into s slices
+                            (clamped to the number of K-tiles)             */
+    int32_t persistent;  /* -1: automatic; 0: one workgroup per work unit;
+                            1: grid of resident capacity looping over units,
+                            with the last partial round split along K      */
+    int32_t tile;        /* -1: automatic; else an index of the tile table */
+    int32_t cus;         /* compute units S used for planning; 0: query the
+                            current device (256 when no device is present) */
+    void *workspace;          /* device scratch for split-K partial sums and
+                                 repacked operands, 256-byte aligned
+                                 (EALIGN otherwise); NULL: library-owned  */
+    size_t workspace_bytes;   /* size of `workspace`                      */
+} gemm355_args;
+
+/* Everything the planner decided for one call.  Efficiencies are exact
+ * rationals num/den in lowest terms. */
+typedef struct gemm355_plan_t {
+    int32_t tile;                 /* tile-table index                      */
+    int32_t T_M, T_N, T_K;        /* output tile and K-step of the loop    */
+    int32_t stages, waves;        /* LDS ring depth; wavefronts per group  */
+    int32_t lds_bytes;            /* LDS per workgroup                     */
+    int32_t vgpr_budget;          /* VGPR+AGPR per lane the kernel may use */
+    int32_t S;                    /* compute units                         */
+    int32_t b;                    /* resident workgroups per CU            */
+    int64_t G;                    /* output tiles, all batch entries       */
+    int64_t nK;                   /* K-tiles: ceil(K / T_K)                */
+    int64_t M_pad, N_pad, K_pad;  /* ceil(X / T_X) * T_X                   */
+    int32_t split;                /* uniform K-split (1 = none)            */
+    int32_t persistent;           /* 1 if the grid loops over units        */
+    int64_t tail_tiles;           /* tiles of the last partial round that
+                                     are split along K (0 = none)          */
+    int32_t tail_split;           /* slices per tail tile                  */
+    int32_t repack;               /* bit 0: A repacked, bit 1: B repacked  */
+    int64_t units;                /* work units (tile, K-range)            */
+    int64_t grid;                 /* workgroups launched by the main kernel */
+    int64_t eta_wave_num, eta_wave_den;    /* G / (ceil(G/(S b)) S b)      */
+    int64_t eta_pad_num, eta_pad_den;      /* MNK / (M'N'K')               */
+    int64_t eta_sched_num, eta_sched_den;  /* sum of unit work over S*b
+                                              times the busiest workgroup's */
+    size_t workspace_bytes;       /* scratch this call needs               */
+} gemm355_plan_t;
+
+/*
+ * gemm355_gemm -- C = A*B for one product, fp32 accumulate.
+ *   M, N, K >= 0.  M == 0 or N == 0: nothing is done.  K == 0: C = 0.
+ *   split_k: 0 automatic, 1 off, s >= 2 forced (clamped to ceil(K/T_K)).
+ *   persistent: -1 automatic, 0 off, 1 on.
+ * Split-K (page "10. Tensor Cores, ...", section "When shape alone can't fix
+ * wave efficiency") writes fp32 partial sums into scratch and combines them
+ * in a second kernel, summing slices in ascending order.  The persistent
+ * mode (same section) launches S*b workgroups that loop over the work units.
+ * Scratch is library-owned here (allocated on first use per device, grown
+ * when needed, freed at unload).
+ * Errors: EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP as listed above.
+ */
+GEMM355_API gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda,
+                            const void *B, int64_t ldb,
+                            void *C, int64_t ldc,
+                            gemm355_dtype dtype, gemm355_layout layout,
+                            int32_t split_k, int32_t persistent, void *stream);
+
+/*
+ * gemm355_gemm_ex -- the same operation with the full argument set: a strided
+ * batch of independent products in one launch, per-entry fp32 scales
+ * (alpha_g = scale_a[g] * scale_b[g]), a forced tile, and caller-provided
+ * scratch (needs at least plan.workspace_bytes; ENOMEM otherwise).
+ * The batch strides must keep entries from overlapping C with A or B.
+ */
+GEMM355_API gemm355_status gemm355_gemm_ex(const gemm355_args *args, void *stream);
+
+/*
+ * gemm355_plan -- what gemm355_gemm_ex would do with `args` (pointers are
+ * only inspected for alignment, never dereferenced).  Pure host arithmetic;
+ * needs no device when args->cus > 0.
+ */
+GEMM355_API gemm355_status gemm355_plan(const gemm355_args *args, gemm355_plan_t *out);
+
+/*
+ * Wave efficiency G / (ceil(G/(S*b)) * S * b) for G tiles on S compute units
+ * holding b workgroups each (page "10. Tensor Cores, ...", section "Shape the
+ * operation", wave-efficiency equation).  Returns the binary64 value nearest
+ * the exact rational, or NaN if G < 1, S < 1 or b < 1.
+ */
+GEMM355_API double gemm355_eta_wave(int64_t G, int32_t S, int32_t b);
+
+/*
+ * Padding efficiency MNK / (M'N'K') with X' = ceil(X/T_X)*T_X (section
+ * "Padding efficiency" of the same page).  Returns the binary64 value nearest
+ * the exact rational, or NaN if any argument is < 1.
+ */
+GEMM355_API double gemm355_eta_pad(int64_t M, int64_t N, int64_t K,
+                       int64_t T_M, int64_t T_N, int64_t T_K);
+
+/*
+ * K-tile range [*begin, *end) of split-K slice i when nK K-tiles are cut into
+ * s slices: begin = floor(i*nK/s), end = floor((i+1)*nK/s).
+ * EINVAL unless nK >= 0, s >= 1 and 0 <= i < s.
+ */
+GEMM355_API gemm355_status gemm355_kslice(int64_t nK, int32_t s, int32_t i,
+                              int64_t *begin, int64_t *end);
+
+/*
+ * Work unit u of a plan, decoded by the same function the kernels use:
+ * batch entry, tile row and column, and K-tile range.  EINVAL if u is out of
+ * range.  (Host-side view of the persistent tile queue, for inspection.)
+ */
+GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
+                            int64_t *batch, int64_t *tile_m, int64_t *tile_n,
+                            int64_t *kt_begin, int64_t *kt_end);
+
+/* Number of entries in the tile table, and one entry's parameters.
+ * dtype_class: 0 = bf16 inputs, 1 = E4M3 inputs. */
+GEMM355_API int32_t gemm355_num_tiles(void);
+GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
+                                 int32_t *T_M, int32_t *T_N, int32_t *T_K,
+                                 int32_t *stages, int32_t *waves,
+                                 int32_t *lds_bytes, int32_t *b_max);
+
+/* Workgroups of a tile's main-loop kernel that fit on one compute unit of
+ * the current device, as the HIP runtime reports it
+ * (hipOccupancyMaxActiveBlocksPerMultiprocessor at 256 threads).  Needs a
+ * device; EHIP otherwise. */
+GEMM355_API gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu);
+
+/* Static description of a status code. */
+GEMM355_API const char *gemm355_status_string(gemm355_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM355_H */

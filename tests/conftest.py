@@ -13,6 +13,15 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU-side check")
 
 
+def pytest_sessionstart(session):
+    """Build the HIP library in-tree when it is missing (a fresh checkout);
+    an existing build is used as is."""
+    lib = os.path.join(ROOT, "dense_tiled_gemm_fp8_amd", "libgemm355.so")
+    if not os.path.exists(lib):
+        from dense_tiled_gemm_fp8_amd import build
+        build.build()
+
+
 @pytest.fixture(scope="session")
 def oracle_lib():
     from oracle import reference

@@ -1,0 +1,126 @@
+"""Helpers for the GPU parity tests: move raw operand codes to the device,
+call libgemm355 through its C ABI, bring C back, compare with the oracle.
+
+Tolerances (per element, W = |alpha| sum_k |a_ik b_kj| from the oracle):
+  bf16 inputs:  |C_gpu - C_ref| <= 1e-3 W + 1e-6
+  E4M3 inputs:  |C_gpu - C_ref| <= 2e-2 W
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from dense_tiled_gemm_fp8_amd import gemm355 as g
+from dense_tiled_gemm_fp8_amd import inputs
+from oracle import reference as oracle
+
+TOL = {"bf16": (1e-3, 1e-6), "e4m3": (2e-2, 0.0)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(codes: np.ndarray) -> torch.Tensor:
+    """Raw codes -> device tensor holding the same bytes."""
+    c = np.ascontiguousarray(codes)
+    if c.dtype == np.uint16:
+        t = torch.from_numpy(c.view(np.int16))
+    else:
+        t = torch.from_numpy(c.view(np.uint8))
+    return t.to("cuda")
+
+
+def out_dtype(fmt: str, out: str) -> int:
+    if fmt == "bf16":
+        return g.BF16_BF16 if out == "bf16" else g.BF16_F32
+    return g.E4M3_BF16 if out == "bf16" else g.E4M3_F32
+
+
+def empty_c(batch: int, M: int, N: int, out: str, fill: float = float("nan")) -> torch.Tensor:
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    shape = (batch, M, N) if batch > 1 else (M, N)
+    return torch.full(shape, fill, dtype=dt, device="cuda")
+
+
+def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: int = -1,
+        tile: int = -1, layout: int = g.A_ROW_B_COL, A_dev=None, B_dev=None, lda=None, ldb=None,
+        scales: bool = True, workspace=None, C=None) -> np.ndarray:
+    """Run one (batched) product on the device in the storage convention of
+    the inputs module (A row-major M x K, B column-major given as N x K)."""
+    M, N, K, batch = ops.M, ops.N, ops.K, ops.batch
+    A_dev = dev(ops.A) if A_dev is None else A_dev
+    B_dev = dev(ops.B) if B_dev is None else B_dev
+    if C is None:
+        C = empty_c(batch, M, N, out)
+    sa = sb = None
+    if scales and ops.fmt == "e4m3":
+        sa = torch.tensor(ops.scale_a, dtype=torch.float32, device="cuda")
+        sb = torch.tensor(ops.scale_b, dtype=torch.float32, device="cuda")
+    ws = None
+    args = g.make_args(M, N, K, A=A_dev, lda=lda, B=B_dev, ldb=ldb, C=C, dtype=out_dtype(ops.fmt, out),
+                       layout=layout, batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N,
+                       scale_a=sa, scale_b=sb, split_k=split_k, persistent=persistent, tile=tile)
+    if workspace == "caller":
+        p = g.gemm355_plan(args)
+        if p["workspace_bytes"]:
+            ws = torch.empty(p["workspace_bytes"], dtype=torch.uint8, device="cuda")
+            args.workspace = ws.data_ptr()
+            args.workspace_bytes = p["workspace_bytes"]
+    g.gemm355_gemm_ex(args)
+    torch.cuda.synchronize()
+    return C.float().cpu().numpy().astype(np.float64)
+
+
+def alpha_of(ops: inputs.Operands, bi: int = 0) -> float:
+    if ops.fmt == "e4m3":
+        return float(np.float32(ops.scale_a[bi]) * np.float32(ops.scale_b[bi]))
+    return 1.0
+
+
+def oracle_full(ops: inputs.Operands, bi: int = 0, alpha=None):
+    A = ops.A[bi] if ops.A.ndim == 3 else ops.A
+    B = ops.B[bi] if ops.B.ndim == 3 else ops.B
+    if alpha is None:
+        alpha = alpha_of(ops, bi)
+    return oracle.gemm(ops.M, ops.N, ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, alpha=alpha)
+
+
+def oracle_entries(ops: inputs.Operands, rows, cols, bi: int = 0):
+    A = ops.A[bi] if ops.A.ndim == 3 else ops.A
+    B = ops.B[bi] if ops.B.ndim == 3 else ops.B
+    return oracle.gemm_entries(ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, rows, cols,
+                               alpha=alpha_of(ops, bi))
+
+
+def check(C_gpu: np.ndarray, C_ref: np.ndarray, W: np.ndarray, fmt: str, what: str = ""):
+    rel, absol = TOL[fmt]
+    err = np.abs(C_gpu - C_ref)
+    bound = rel * W + absol
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d outside tolerance; first %s: gpu %s ref %s W %s" % (
+            what, int(bad.sum()), bad.size, idx.tolist(),
+            [C_gpu[tuple(i)] for i in idx], [C_ref[tuple(i)] for i in idx], [W[tuple(i)] for i in idx]))
+
+
+def sample_positions(M: int, N: int, n: int, seed: int):
+    """Random positions plus the four corners and the last row/column
+    stretches (ragged edges)."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    rows = list(r.integers(0, M, n))
+    cols = list(r.integers(0, N, n))
+    for (i, j) in [(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)]:
+        rows.append(i)
+        cols.append(j)
+    edge = min(64, N)
+    rows += [M - 1] * edge
+    cols += list(range(N - edge, N))
+    edge = min(64, M)
+    rows += list(range(M - edge, M))
+    cols += [N - 1] * edge
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)

@@ -1,0 +1,265 @@
+"""Host-side checks of libgemm355 through its C ABI (no kernel launches).
+
+* every symbol include/gemm355.h declares is exported;
+* the wave- and padding-efficiency queries equal the exact rationals of the
+  bookkeeping oracle bit for bit;
+* K-slices, tile grid, padded sizes, resident workgroups and schedule
+  efficiency of the plans equal the oracle's;
+* the work units a plan hands to the kernels cover every (tile, K-tile) once;
+* argument errors are reported before anything is launched.
+"""
+import os
+import random
+import re
+import struct
+from fractions import Fraction
+
+import pytest
+
+from oracle import bookkeeping as bk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def g():
+    from dense_tiled_gemm_fp8_amd import gemm355
+    return gemm355
+
+
+def bits(x: float) -> bytes:
+    return struct.pack("<d", x)
+
+
+def test_header_symbols_exported(g):
+    hdr = open(os.path.join(ROOT, "include", "gemm355.h")).read()
+    declared = set(re.findall(r"GEMM355_API\s+[\w\s\*]+?\b(gemm355_\w+)\s*\(", hdr))
+    assert declared, "no declarations found"
+    assert declared == set(g.EXPORTED)
+    for name in declared:
+        assert hasattr(g._lib, name), name
+
+
+def test_eta_wave_bit_exact(g):
+    rnd = random.Random(0)
+    cases = [(24, 148, 1), (12, 148, 1), (256, 256, 1), (272, 256, 1), (1, 256, 1), (752, 256, 4)]
+    cases += [(rnd.randint(1, 10 ** 7), rnd.randint(1, 512), rnd.randint(1, 8)) for _ in range(3000)]
+    for G, S, b in cases:
+        assert bits(g.gemm355_eta_wave(G, S, b)) == bits(float(bk.eta_wave(G, S, b))), (G, S, b)
+
+
+def test_eta_pad_bit_exact(g):
+    rnd = random.Random(1)
+    cases = [(4096, 4096, 4096, 256, 256, 64), (4000, 4000, 4000, 256, 256, 64),
+             (4097, 4095, 4104, 256, 256, 64), (1000, 3000, 777, 64, 64, 64)]
+    cases += [(rnd.randint(1, 1 << 20), rnd.randint(1, 1 << 20), rnd.randint(1, 1 << 20),
+               rnd.choice([16, 32, 64, 128, 256]), rnd.choice([16, 64, 256]),
+               rnd.choice([32, 64, 128])) for _ in range(3000)]
+    for c in cases:
+        assert bits(g.gemm355_eta_pad(*c)) == bits(float(bk.eta_pad(*c))), c
+
+
+def test_eta_queries_reject_invalid(g):
+    import math
+    assert math.isnan(g.gemm355_eta_wave(0, 256, 1))
+    assert math.isnan(g.gemm355_eta_wave(5, 0, 1))
+    assert math.isnan(g.gemm355_eta_pad(0, 1, 1, 1, 1, 1))
+    assert math.isnan(g.gemm355_eta_pad(1, 1, 1, 1, 0, 1))
+
+
+def test_kslice_matches_oracle(g):
+    rnd = random.Random(2)
+    for _ in range(2000):
+        nK = rnd.randint(0, 1 << 22)
+        s = rnd.randint(1, 256)
+        i = rnd.randrange(s)
+        assert g.gemm355_kslice(nK, s, i) == bk.kslice(nK, s, i)
+    with pytest.raises(g.Gemm355Error):
+        g.gemm355_kslice(10, 0, 0)
+    with pytest.raises(g.Gemm355Error):
+        g.gemm355_kslice(10, 4, 4)
+
+
+# shapes: the named workloads plus ragged and degenerate ones
+PLAN_SHAPES = [
+    (256, 256, 256, 1, 0), (4096, 4096, 4096, 1, 1), (4000, 4000, 4000, 1, 0),
+    (4097, 4095, 4104, 1, 0), (1000, 3000, 777, 1, 0), (256, 256, 65536, 1, 0),
+    (128, 512, 131072, 1, 0), (64, 64, 262144, 1, 0), (8192, 8192, 8192, 1, 2),
+    (512, 1024, 4096, 64, 2), (1, 1, 1, 1, 0), (17, 300, 40, 3, 2), (5000, 33, 9000, 1, 0),
+]
+
+KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1, persistent=1),
+         dict(split_k=5, persistent=1), dict(tile=1), dict(tile=2, persistent=1, split_k=1)]
+
+
+def _plan_and_check(g, M, N, K, batch, dtype, knobs):
+    if "tile" in knobs and dtype == g.E4M3_F32:
+        knobs = dict(knobs, tile=knobs["tile"] + 3)
+    a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, dtype=dtype,
+                    batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N, cus=256, **knobs)
+    p = g.gemm355_plan(a)
+    info = g.gemm355_tile_info(p["tile"])
+    S, b = 256, p["b"]
+    assert p["S"] == S
+    # tile grid, padding, K-tiles (equations for G and the padded dimensions)
+    tm, tn = bk.ceil_div(M, p["T_M"]), bk.ceil_div(N, p["T_N"])
+    assert p["G"] == batch * bk.tile_grid(M, N, p["T_M"], p["T_N"])
+    assert p["nK"] == bk.ceil_div(K, p["T_K"])
+    assert (p["M_pad"], p["N_pad"], p["K_pad"]) == (bk.padded(M, p["T_M"]), bk.padded(N, p["T_N"]),
+                                                    bk.padded(K, p["T_K"]))
+    assert Fraction(p["eta_wave_num"], p["eta_wave_den"]) == bk.eta_wave(p["G"], S, b)
+    assert Fraction(p["eta_pad_num"], p["eta_pad_den"]) == bk.eta_pad(M, N, K, p["T_M"], p["T_N"], p["T_K"])
+    # resident workgroups: the launched b never exceeds the oracle's bound
+    # gfx950 unit: 160 KiB LDS, 4 SIMDs x 64 lanes x 512 registers, granule
+    # 8, at most 8 waves per SIMD
+    bmax = bk.resident_per_sm(info["lds_bytes"], 160 * 1024, p["vgpr_budget"], 8,
+                              64 * info["waves"], 4 * 64 * 512, max_ctas=32 // info["waves"])["b"]
+    assert info["b_max"] == bmax
+    assert 1 <= b <= bmax
+    # schedule: rebuild the unit list from the oracle's policy
+    if p["split"] > 1:
+        units = bk.schedule_units(p["G"], p["nK"], s=p["split"])
+    elif p["tail_tiles"]:
+        units = bk.schedule_units(p["G"], p["nK"], tail_split=True, P=S * b)
+        assert bk.tail_split_factor(p["G"], p["nK"], S * b) == p["tail_split"]
+    else:
+        units = bk.schedule_units(p["G"], p["nK"])
+    assert len(units) == p["units"]
+    assert Fraction(p["eta_sched_num"], p["eta_sched_den"]) == bk.eta_sched_units(units, S, b, grid=p["grid"])
+    if p["persistent"]:
+        assert p["grid"] == min(p["units"], S * b)
+    else:
+        assert p["grid"] == p["units"]
+    return a, p
+
+
+@pytest.mark.parametrize("M,N,K,batch,dt", PLAN_SHAPES)
+def test_plan_bookkeeping(g, M, N, K, batch, dt):
+    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32][dt]
+    for knobs in KNOBS:
+        _plan_and_check(g, M, N, K, batch, dtype, knobs)
+
+
+@pytest.mark.parametrize("M,N,K,batch,dt", [s for s in PLAN_SHAPES if s[0] * s[1] * s[3] <= 5000 * 5000])
+def test_units_cover_every_k_tile_once(g, M, N, K, batch, dt):
+    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32][dt]
+    for knobs in KNOBS:
+        a, p = _plan_and_check(g, M, N, K, batch, dtype, knobs)
+        if p["units"] > 20000:
+            continue
+        tm, tn = bk.ceil_div(M, p["T_M"]), bk.ceil_div(N, p["T_N"])
+        seen = {}
+        for u in range(p["units"]):
+            bt, i, j, kb, ke = g.gemm355_unit(a, u)
+            assert 0 <= bt < batch and 0 <= i < tm and 0 <= j < tn and 0 <= kb < ke <= p["nK"]
+            key = (bt, i, j)
+            seen.setdefault(key, []).append((kb, ke))
+        assert len(seen) == p["G"]
+        for ranges in seen.values():
+            ranges.sort()
+            assert ranges[0][0] == 0 and ranges[-1][1] == p["nK"]
+            for (b0, e0), (b1, e1) in zip(ranges, ranges[1:]):
+                assert e0 == b1
+            if p["split"] > 1:
+                assert ranges == bk.kslices(p["nK"], p["split"])
+        with pytest.raises(g.Gemm355Error):
+            g.gemm355_unit(a, p["units"])
+
+
+def test_plan_reports_efficiency_levers(g):
+    """The named ragged and split-K shapes are planned with a persistent tail
+    split or a K-split that fills the device."""
+    for (M, N, K) in [(4097, 4095, 4104), (256, 256, 65536), (128, 512, 131072), (64, 64, 262144)]:
+        a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
+        p = g.gemm355_plan(a)
+        assert p["split"] > 1 or p["tail_tiles"] > 0
+        assert Fraction(p["eta_sched_num"], p["eta_sched_den"]) >= Fraction(95, 100)
+    a = g.make_args(4096, 4096, 4096, A=0x10000, B=0x1000000000, C=0x200000000000,
+                    dtype=g.BF16_BF16, cus=256)
+    p = g.gemm355_plan(a)
+    assert (p["T_M"], p["T_N"], p["G"], p["eta_wave_num"], p["eta_wave_den"]) == (256, 256, 256, 1, 1)
+
+
+def test_repack_decisions(g):
+    base = dict(A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
+    assert g.gemm355_plan(g.make_args(1000, 3000, 777, **base))["repack"] == 3     # rows 2-byte aligned
+    assert g.gemm355_plan(g.make_args(1000, 3000, 776, **base))["repack"] == 0
+    assert g.gemm355_plan(g.make_args(64, 64, 64, layout=g.A_COL_B_COL, **base))["repack"] == 1
+    assert g.gemm355_plan(g.make_args(64, 64, 64, layout=g.A_ROW_B_ROW, **base))["repack"] == 2
+    b2 = dict(base, A=0x10002)
+    assert g.gemm355_plan(g.make_args(64, 64, 64, **b2))["repack"] == 1
+    assert g.gemm355_plan(g.make_args(64, 64, 128, dtype=g.E4M3_F32, **base))["repack"] == 0
+    assert g.gemm355_plan(g.make_args(64, 64, 120, dtype=g.E4M3_F32, **base))["repack"] == 3
+
+
+def test_argument_errors(g):
+    P = dict(A=0x10000, B=0x1000000000, C=0x200000000000)
+
+    def status(**kw):
+        args = dict(P)
+        args.update(kw)
+        M, N, K = args.pop("M", 64), args.pop("N", 64), args.pop("K", 64)
+        try:
+            g.gemm355_gemm_ex(g.make_args(M, N, K, **args), stream=0)
+            return g.OK
+        except g.Gemm355Error as e:
+            return e.status
+
+    assert status(M=-1) == g.EINVAL
+    assert status(K=-5) == g.EINVAL
+    assert status(lda=10) == g.EINVAL
+    assert status(ldb=10) == g.EINVAL
+    assert status(ldc=10) == g.EINVAL
+    assert status(A=None) == g.EINVAL
+    assert status(C=None) == g.EINVAL
+    assert status(A=0x10001) == g.EALIGN
+    assert status(C=0x200000000002) == g.EALIGN            # fp32 C
+    assert status(scale_a=0x3001) == g.EALIGN
+    assert status(dtype=7) == g.EINVAL
+    assert status(layout=9) == g.EINVAL
+    assert status(tile=99) == g.EINVAL
+    assert status(tile=3) == g.EINVAL                      # E4M3 tile for bf16 inputs
+    assert status(persistent=2) == g.EINVAL
+    assert status(split_k=-1) == g.EINVAL
+    assert status(batch=0) == g.EINVAL
+    assert status(cus=-3) == g.EINVAL
+    assert status(C=0x10000 + 64) == g.EINVAL              # C overlaps A
+    assert status(lda=(1 << 24)) == g.EUNSUPPORTED         # 32-bit tile offsets
+    # split-K needs scratch: a caller workspace that is too small
+    assert status(K=65536, split_k=8, workspace=0x300000000000, workspace_bytes=16) == g.ENOMEM
+    assert status(K=65536, split_k=8, workspace=0x300000000010, workspace_bytes=1 << 30) == g.EALIGN
+    # nothing to do: M or N zero is accepted without touching the device
+    assert status(M=0) == g.OK
+    assert status(N=0, C=None) == g.OK
+    assert g.gemm355_status_string(g.ENOMEM).startswith("workspace")
+
+
+def test_tile_table(g):
+    n = g.gemm355_num_tiles()
+    assert n >= 6
+    seen = set()
+    for t in range(n):
+        info = g.gemm355_tile_info(t)
+        assert info["lds_bytes"] == info["stages"] * (info["T_M"] + info["T_N"]) * 128
+        assert info["lds_bytes"] <= 160 * 1024
+        assert info["T_K"] * (1 if info["dtype_class"] else 2) == 128
+        seen.add((info["dtype_class"], info["T_M"], info["T_N"]))
+    assert (0, 256, 256) in seen and (1, 256, 256) in seen
+    with pytest.raises(g.Gemm355Error):
+        g.gemm355_tile_info(n)
+
+
+def test_main_loop_uses_mfma(tmp_path):
+    """The compiler emitted the matrix-core instruction family for every
+    main-loop instantiation (bf16 and E4M3), not a scalar fallback."""
+    from dense_tiled_gemm_fp8_amd import build
+    asm = open(build.device_asm("kernels.hip")).read()
+    bodies = re.split(r"\n(?=_ZN4g35516gemm_tile_kernel\w+:)", asm)
+    kernels = [b for b in bodies if re.match(r"_ZN4g35516gemm_tile_kernel\w+:", b)]
+    assert len(kernels) == 6
+    for body in kernels:
+        name = body.split(":")[0]
+        fp8 = "Lb1E" in name
+        want = "v_mfma_f32_32x32x64_f8f6f4" if fp8 else "v_mfma_f32_32x32x16_bf16"
+        assert want in body, name
+        assert "v_fma_f32" not in body.split("s_endpgm")[0] or want in body

@@ -1,0 +1,301 @@
+"""GPU parity: libgemm355 (called through its C ABI) against the CPU oracle.
+
+Small and medium shapes are compared element by element on every output;
+the full-size workloads, in the launch configuration the benchmark times
+(automatic plan), on sampled outputs plus the ragged edges.  Exact-integer
+inputs make every summation order give the same bits, so those cases demand
+bit-identical results through every tile, split, schedule, layout and batch
+path (a dropped, duplicated or stale tile, K-slice or LDS stage changes bits).
+"""
+import numpy as np
+import pytest
+import torch
+
+from dense_tiled_gemm_fp8_amd import gemm355 as g
+from dense_tiled_gemm_fp8_amd import inputs
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+BF16_TILES = [0, 1, 2]
+E4M3_TILES = [3, 4, 5]
+
+
+def ops_from(M, N, K, fmt, seed, dist="uniform", batch=0):
+    return inputs.make_operands(M, N, K, fmt, dist, seed, seed + 1, batch=batch)
+
+
+def int_ops(M, N, K, fmt, seed, batch=0, lo=-4, hi=4):
+    ga, gb = inputs.rng(seed), inputs.rng(seed + 1)
+    nb = max(batch, 1)
+    A = np.stack([inputs.small_int_codes(ga, (M, K), fmt, lo, hi) for _ in range(nb)])
+    B = np.stack([inputs.small_int_codes(gb, (N, K), fmt, lo, hi) for _ in range(nb)])
+    if not batch:
+        A, B = A[0], B[0]
+    sc = [1.0] * nb
+    return inputs.Operands(M, N, K, fmt, A, B, list(sc), list(sc), (seed, seed + 1))
+
+
+def test_device_is_gfx950():
+    assert torch.cuda.is_available()
+    props = torch.cuda.get_device_properties(0)
+    H.say("device", props.name, getattr(props, "gcnArchName", "?"), props.multi_processor_count)
+    assert "gfx950" in getattr(props, "gcnArchName", "gfx950")
+
+
+@pytest.mark.parametrize("tile", BF16_TILES + E4M3_TILES)
+def test_runtime_occupancy_covers_plan(tile):
+    info = g.gemm355_tile_info(tile)
+    n = g.gemm355_tile_occupancy(tile)
+    H.say("tile", tile, info, "runtime occupancy", n)
+    assert n >= info["b_max"]
+
+
+def test_workload_256_cube_full():
+    w = inputs.WORKLOADS[0]
+    ops = inputs.workload_operands(w)
+    H.say("256^3 bf16 -> f32, seeds", ops.seeds, "sha", inputs.sha256(ops.A, ops.B)[:16])
+    C_ref, W = H.oracle_full(ops)
+    for knobs in (dict(), dict(split_k=1, persistent=0), dict(split_k=4), dict(persistent=1)):
+        H.say("  knobs", knobs)
+        C = H.run(ops, out="f32", **knobs)
+        H.check(C, C_ref, W, "bf16", "256^3 %s" % knobs)
+
+
+BF16_SHAPES = [(300, 520, 200), (64, 64, 64), (257, 129, 136), (1, 1, 8), (33, 65, 8), (70, 90, 77),
+               (513, 260, 1000)]
+E4M3_SHAPES = [(300, 520, 256), (64, 64, 128), (257, 129, 144), (1, 1, 16), (70, 90, 77), (513, 260, 1008)]
+
+
+@pytest.mark.parametrize("tile", BF16_TILES)
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+def test_bf16_tiles_ragged_full(tile, shape):
+    M, N, K = shape
+    ops = ops_from(M, N, K, "bf16", 100 + M + N + K)
+    C_ref, W = H.oracle_full(ops)
+    for knobs in (dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1, persistent=1)):
+        H.say("bf16 tile", tile, shape, knobs)
+        C = H.run(ops, out="f32", tile=tile, **knobs)
+        H.check(C, C_ref, W, "bf16", "bf16 tile %d %s %s" % (tile, shape, knobs))
+
+
+@pytest.mark.parametrize("tile", E4M3_TILES)
+@pytest.mark.parametrize("shape", E4M3_SHAPES)
+def test_e4m3_tiles_ragged_full(tile, shape):
+    M, N, K = shape
+    ops = ops_from(M, N, K, "e4m3", 200 + M + N + K, dist="normal")
+    C_ref, W = H.oracle_full(ops)
+    for knobs in (dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1, persistent=1)):
+        H.say("e4m3 tile", tile, shape, knobs)
+        C = H.run(ops, out="f32", tile=tile, **knobs)
+        H.check(C, C_ref, W, "e4m3", "e4m3 tile %d %s %s" % (tile, shape, knobs))
+
+
+@pytest.mark.parametrize("fmt,tiles", [("bf16", BF16_TILES), ("e4m3", E4M3_TILES)])
+def test_exact_integers_every_path(fmt, tiles):
+    """Integers in [-4, 4]: sums are exact in fp32 in any order, so every
+    tile, split, schedule and batch path must give the oracle's bits."""
+    M, N, K, batch = 300, 270, 384, 3
+    ops = int_ops(M, N, K, fmt, 7, batch=batch)
+    refs = [H.oracle_full(ops, bi, alpha=1.0)[0] for bi in range(batch)]
+    for tile in tiles:
+        for knobs in (dict(split_k=1, persistent=0), dict(split_k=2, persistent=0),
+                      dict(split_k=3, persistent=1), dict(split_k=1, persistent=1),
+                      dict(split_k=5, persistent=0)):
+            H.say(fmt, "ints tile", tile, knobs)
+            C = H.run(ops, out="f32", tile=tile, **knobs)
+            for bi in range(batch):
+                assert np.array_equal(C[bi], refs[bi]), (tile, knobs, bi)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_exact_bf16_output(fmt):
+    """bf16 output: integer results with |C| <= 256 are representable, so the
+    rounded output is exact."""
+    M, N, K = 200, 300, 64
+    ops = int_ops(M, N, K, fmt, 11, lo=-2, hi=2)
+    ref, _ = H.oracle_full(ops, alpha=1.0)
+    assert np.abs(ref).max() <= 256
+    for knobs in (dict(split_k=1), dict(split_k=2), dict(persistent=1)):
+        H.say(fmt, "bf16-out ints", knobs)
+        C = H.run(ops, out="bf16", **knobs)
+        assert np.array_equal(C, ref), knobs
+
+
+def test_power_of_two_scales_exact():
+    M, N, K = 128, 192, 256
+    ops = int_ops(M, N, K, "e4m3", 13)
+    ops.scale_a, ops.scale_b = [0.25], [8.0]
+    ref, _ = H.oracle_full(ops, alpha=2.0)
+    H.say("e4m3 scales 0.25 x 8")
+    C = H.run(ops, out="f32")
+    assert np.array_equal(C, ref)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_all_layouts(fmt):
+    """Every storage layout (repacked on the device) against the oracle, and
+    the transpose identity (A B)^T = B^T A^T through the layout flags."""
+    M, N, K = 150, 98, 136
+    ops = ops_from(M, N, K, fmt, 17, dist="normal")
+    a_log = ops.A                       # M x K logical
+    b_log = np.ascontiguousarray(ops.B.T)  # K x N logical
+    C_ref, W = H.oracle_full(ops)
+    alpha = H.alpha_of(ops)
+    for layout in (g.A_ROW_B_COL, g.A_ROW_B_ROW, g.A_COL_B_COL, g.A_COL_B_ROW):
+        a_row = layout in (g.A_ROW_B_COL, g.A_ROW_B_ROW)
+        b_col = layout in (g.A_ROW_B_COL, g.A_COL_B_COL)
+        A_st = a_log if a_row else np.ascontiguousarray(a_log.T)
+        B_st = np.ascontiguousarray(b_log.T) if b_col else b_log
+        lda = K if a_row else M
+        ldb = K if b_col else N
+        H.say(fmt, "layout", layout)
+        C = H.run(ops, out="f32", layout=layout, A_dev=H.dev(A_st), B_dev=H.dev(B_st), lda=lda, ldb=ldb)
+        H.check(C, C_ref, W, fmt, "layout %d" % layout)
+    # transpose identity with exact integers: N x M result from swapped roles
+    iops = int_ops(M, N, K, fmt, 19)
+    C1 = H.run(iops, out="f32")
+    swapped = inputs.Operands(N, M, K, fmt, iops.B, iops.A, [1.0], [1.0])
+    C2 = H.run(swapped, out="f32")
+    assert np.array_equal(C1, C2.T)
+
+
+def test_persistent_on_off_bit_identical():
+    """Same tile and the same uniform split: the persistent loop only changes
+    which workgroup runs a unit, so results are bit-identical."""
+    M, N, K = 1100, 700, 1500
+    ops = ops_from(M, N, K, "bf16", 23, dist="normal")
+    for tile, s in ((0, 1), (1, 2), (2, 3)):
+        H.say("persistent on/off tile", tile, "split", s)
+        C0 = H.run(ops, out="f32", tile=tile, split_k=s, persistent=0)
+        C1 = H.run(ops, out="f32", tile=tile, split_k=s, persistent=1 if s > 1 else 0)
+        assert np.array_equal(C0, C1)
+    C_ref, W = H.oracle_full(ops)
+    H.check(C0, C_ref, W, "bf16", "persistent")
+
+
+def test_split_invariant_float():
+    M, N, K = 256, 192, 8192
+    ops = ops_from(M, N, K, "bf16", 29, dist="normal_sqrtk")
+    C_ref, W = H.oracle_full(ops)
+    base = H.run(ops, out="f32", split_k=1, persistent=0)
+    H.check(base, C_ref, W, "bf16", "split 1")
+    for s in (2, 7, 32, 128):
+        H.say("split", s)
+        C = H.run(ops, out="f32", split_k=s)
+        H.check(C, C_ref, W, "bf16", "split %d" % s)
+        assert np.all(np.abs(C - base) <= 2e-3 * W + 2e-6)
+
+
+def test_leading_dims_offsets_and_workspace():
+    M, N, K = 200, 136, 96
+    ops = ops_from(M, N, K, "bf16", 31)
+    C_ref, W = H.oracle_full(ops)
+    # padded leading dimensions (16-byte aligned rows: main loop reads directly)
+    Aw = np.zeros((M, K + 24), dtype=np.uint16)
+    Aw[:, :K] = ops.A
+    Bw = np.zeros((N, K + 40), dtype=np.uint16)
+    Bw[:, :K] = ops.B
+    H.say("ld padded")
+    C = H.run(ops, out="f32", A_dev=H.dev(Aw), B_dev=H.dev(Bw), lda=K + 24, ldb=K + 40)
+    H.check(C, C_ref, W, "bf16", "padded ld")
+    # an A that starts one element past a 16-byte boundary (repack path)
+    buf = H.dev(np.concatenate([np.zeros(1, np.uint16), ops.A.reshape(-1)]))
+    H.say("misaligned A")
+    C = H.run(ops, out="f32", A_dev=buf[1:])
+    H.check(C, C_ref, W, "bf16", "misaligned A")
+    # output with ldc > N
+    Cbig = torch.full((M, N + 8), 7.0, dtype=torch.float32, device="cuda")
+    args = g.make_args(M, N, K, A=H.dev(ops.A), B=H.dev(ops.B), C=Cbig, ldc=N + 8)
+    H.say("ldc padded")
+    g.gemm355_gemm_ex(args)
+    torch.cuda.synchronize()
+    out = Cbig.cpu().numpy().astype(np.float64)
+    H.check(out[:, :N], C_ref, W, "bf16", "ldc")
+    assert np.all(out[:, N:] == 7.0)
+    # caller workspace and library scratch give the same bits
+    for knobs in (dict(split_k=4), dict(persistent=1, tile=1)):
+        H.say("workspace", knobs)
+        C1 = H.run(ops, out="f32", workspace="caller", **knobs)
+        C2 = H.run(ops, out="f32", **knobs)
+        assert np.array_equal(C1, C2)
+
+
+def test_degenerate_sizes():
+    ops = ops_from(5, 7, 0, "bf16", 37)
+    H.say("K = 0")
+    C = H.run(ops, out="f32", A_dev=H.dev(np.zeros(8, np.uint16)), B_dev=H.dev(np.zeros(8, np.uint16)))
+    assert np.all(C == 0.0)
+    H.say("M = 0")
+    Cz = torch.full((1, 4), 3.0, device="cuda")
+    g.gemm355_gemm(0, 4, 16, H.dev(np.zeros(64, np.uint16)), 16, H.dev(np.zeros(64, np.uint16)), 16,
+                   Cz, 4, g.BF16_F32)
+    torch.cuda.synchronize()
+    assert torch.all(Cz == 3.0)
+    H.say("1x1x1")
+    one = ops_from(1, 1, 1, "bf16", 41)
+    C_ref, W = H.oracle_full(one)
+    C = H.run(one, out="f32")
+    H.check(C, C_ref, W, "bf16", "1x1x1")
+    H.say("gemm355_gemm entry point")
+    ops = ops_from(130, 70, 48, "bf16", 43)
+    C_ref, W = H.oracle_full(ops)
+    Cg = torch.full((130, 70), float("nan"), device="cuda")
+    g.gemm355_gemm(130, 70, 48, H.dev(ops.A), 48, H.dev(ops.B), 48, Cg, 70, g.BF16_F32)
+    torch.cuda.synchronize()
+    H.check(Cg.cpu().numpy().astype(np.float64), C_ref, W, "bf16", "gemm355_gemm")
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def _sampled(ops, out, n=3000, batch_entries=(0,), what=""):
+    H.say(what, "sha", inputs.sha256(ops.A, ops.B)[:16])
+    A_dev, B_dev = H.dev(ops.A), H.dev(ops.B)
+    C = H.run(ops, out=out, A_dev=A_dev, B_dev=B_dev)
+    Cb = C if ops.batch > 1 else C[None]
+    assert np.all(np.isfinite(Cb))
+    for bi in batch_entries:
+        rows, cols = H.sample_positions(ops.M, ops.N, n, seed=bi + 5)
+        c, w = H.oracle_entries(ops, rows, cols, bi)
+        H.check(Cb[bi][rows, cols], c, w, ops.fmt, "%s entry %d" % (what, bi))
+    return C
+
+
+def test_workload_4096_cube_bf16_out():
+    w = inputs.WORKLOADS[1]
+    ops = inputs.workload_operands(w)
+    _sampled(ops, "bf16", what="4096^3 bf16->bf16")
+
+
+@pytest.mark.parametrize("si", [0, 1, 2])
+def test_workload_ragged(si):
+    w = inputs.WORKLOADS[2]
+    ops = inputs.workload_operands(w, si)
+    _sampled(ops, "f32", what="ragged %s" % (w.shapes[si],))
+
+
+@pytest.mark.parametrize("si", [0, 1, 2])
+def test_workload_split_k(si):
+    w = inputs.WORKLOADS[3]
+    ops = inputs.workload_operands(w, si)
+    if ops.M * ops.N <= 65536:
+        # small outputs: every element
+        H.say("split-K full", w.shapes[si])
+        C = H.run(ops, out="f32")
+        C_ref, W = H.oracle_full(ops)
+        H.check(C, C_ref, W, "bf16", "split-K %s" % (w.shapes[si],))
+    else:
+        _sampled(ops, "f32", what="split-K %s" % (w.shapes[si],))
+
+
+def test_workload_e4m3_8192_cube():
+    w = inputs.WORKLOADS[4]
+    ops = inputs.workload_operands(w)
+    _sampled(ops, "f32", n=2000, what="e4m3 8192^3")
+
+
+def test_workload_e4m3_batch64():
+    w = inputs.WORKLOADS[5]
+    ops = inputs.workload_operands(w)
+    assert ops.batch == 64 and len(set(ops.scale_a)) > 1
+    _sampled(ops, "f32", n=400, batch_entries=(0, 1, 31, 63), what="e4m3 batch 64x(512,1024,4096)")
