@@ -20,7 +20,7 @@ SOURCES = ["kernels.hip", "plan.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC",
     "-fvisibility=hidden",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -20,6 +20,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "kernels.h"
 #include "sched.h"
 #include "tiles.h"
@@ -38,7 +41,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
  * K are read through offset kOOB. */
 constexpr uint32_t kNumRecords = 0x7FFFFF00u;
 constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kRowBytes = 128;           /* K bytes per tile row per stage */
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
 {
@@ -63,17 +65,35 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
 }
 
-/* One direct-to-LDS copy: each lane fetches 16 bytes at voffset from the
- * buffer and the wavefront writes them to LDS at lds .. lds + 1023 (lane l at
- * lds + 16 l).  Issued as inline assembly so that the compiler neither waits
- * for it before unrelated LDS reads nor counts it: completion is awaited
- * explicitly in stage_barrier(). */
-__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds, uint32_t voffset)
+/* Compile-time unrolling: f(integral_constant<int, t>) for t = 0 .. N-1. */
+template <int... T, class F>
+__device__ __forceinline__ void unroll_seq(std::integer_sequence<int, T...>, F &&f)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
+    (f(std::integral_constant<int, T>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unroll(F &&f)
+{
+    unroll_seq(std::make_integer_sequence<int, N>{}, static_cast<F &&>(f));
+}
+
+/* One direct-to-LDS copy: each lane fetches 16 bytes at voffset from the
+ * buffer and the wavefront writes them to LDS at lds_base + OFF .. + 1023
+ * (lane l at + 16 l).  Issued as inline assembly so that the compiler neither
+ * waits for it before unrelated LDS reads nor counts it (completion is
+ * awaited explicitly), and so that the LDS address is formed in M0 right at
+ * the load from one base register and an immediate. */
+template <int OFF>
+__device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds_base, uint32_t voffset)
+{
+    /* s_add writes SCC: declared clobbered, or the compiler could keep a
+     * comparison result in SCC across this statement */
+    int m0_out;
+    asm volatile("s_add_u32 m0, %2, %4\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds"
+                 : "={m0}"(m0_out)
+                 : "v"(voffset), "s"(lds_base), "s"(rsrc), "n"(OFF)
+                 : "memory", "scc");
+    (void)m0_out;
 }
 
 /* All of this wave's direct-to-LDS copies have landed, then the workgroup
@@ -86,6 +106,18 @@ __device__ __forceinline__ void stage_barrier()
     asm volatile("" ::: "memory");
 }
 
+/* Wait until at most N vector-memory operations of this wave are
+ * outstanding (loads complete in issue order). */
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <bool FP8> struct FragType { typedef bf16x8 type; };
+template <> struct FragType<true> { typedef i32x8 type; };
+
 __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
 {
     float a = 1.0f;
@@ -96,37 +128,56 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
 
 /*
  * One workgroup of 4 wavefronts (2 x 2) computes a TM x TN tile; wavefront
- * (wm, wn) owns a (TM/2) x (TN/2) block made of 32 x 32 MFMA blocks.
+ * (wm, wn) owns a (TM/2) x (TN/2) block made of 32 x 32 MFMA blocks.  A
+ * K-tile is RB bytes of K per row (64 or 128: 32/64 bf16 or 64/128 E4M3
+ * values); the LDS holds a ring of STAGES K-tiles.
  *
- * LDS layout of one stage of A (B alike): TM rows of 128 bytes (the tile's
- * K-chunk of that row), row r's 16-byte chunk c stored at chunk position
- * c ^ (r % 8), so that the 8 rows read together by a fragment load hit 8
- * different bank groups.  A direct-to-LDS load instruction writes 1024
- * contiguous bytes per wavefront (lane l -> bytes 16 l .. 16 l + 15), i.e.
- * 8 rows; lane l therefore fetches row l / 8, chunk (l % 8) ^ (l / 8).
+ * LDS layout of one stage of A (B alike): TM rows of RB bytes.  The LDS
+ * serves a 128-bit read 16 lanes at a time from 64 four-byte banks, i.e. one
+ * 256-byte line holding RPL = 256 / RB consecutive rows, so the 16 rows read
+ * together by a fragment load must land on 16 different 16-byte slots of it.
+ * Row r's 16-byte chunk c (of CPR = RB / 16) is stored at chunk position
+ * c ^ ((r / RPL) % CPR): rows with different r % RPL use different parts of
+ * the line, and the 16 / RPL = CPR rows sharing r % RPL get distinct chunks.
+ * A direct-to-LDS load writes 1024 contiguous bytes per wavefront (lane l at
+ * bytes 16 l .. 16 l + 15), i.e. 1024 / RB rows; lane l fetches row l / CPR
+ * of its group and the logical chunk that belongs at position l % CPR.
+ *
+ * Pipeline: a ring of STAGES K-tiles.  Within a K-tile the fragments of MFMA
+ * K-step ks+1 are read while the MFMAs of step ks run (fragments double
+ * buffered in registers).  One barrier per K-tile, before its last step:
+ * by then every wave has read all of this stage and the copy of the next
+ * K-tile has landed; right after it, the copy of the K-tile STAGES ahead is
+ * issued into the stage just freed, and the last step's MFMAs overlap the
+ * reads of the next tile's first fragments.
  */
-template <int TM, int TN, bool FP8, int MINB>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES>
 __global__ __launch_bounds__(256, MINB) void gemm_tile_kernel(GemmParams p)
 {
     constexpr int NW = 4, WN = 2;
     constexpr int WTM = TM / 2, WTN = TN / 2;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_BYTES = TM * kRowBytes, B_BYTES = TN * kRowBytes;
-    constexpr int A_LOADS = TM / 8 / NW, B_LOADS = TN / 8 / NW;
-    constexpr int KSTEPS = FP8 ? 2 : 4;   /* MFMA K-steps per stage: 64 or 16 deep */
-    static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1, "tile too small");
+    constexpr int CPR = RB / 16, RPL = 256 / RB, ROWS_PER_DMA = 1024 / RB;
+    constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB, STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_LOADS = TM / ROWS_PER_DMA / NW, B_LOADS = TN / ROWS_PER_DMA / NW;
+    constexpr int LOADS = A_LOADS + B_LOADS;
+    /* MFMA K-steps per K-tile: bf16 steps are 16 deep (32 bytes), E4M3 64 */
+    constexpr int KSTEPS = FP8 ? RB / 64 : RB / 32;
+    using Frag = typename FragType<FP8>::type;
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1 && KSTEPS >= 1, "tile");
+    static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "ring depth");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const int prow = lane >> 3;
-    const int lchunk = (lane & 7) ^ prow;
-    const int frow = lane & 31, hi = lane >> 5, sw = lane & 7;
+    const int drow = lane / CPR;
+    /* copy group of load d is d * NW + wave; its rows' (r / RPL) % CPR
+     * depends only on the wave (d * NW * ROWS_PER_DMA / RPL = 16 d) */
+    const int lchunk = (lane % CPR) ^ (((wave * ROWS_PER_DMA + drow) / RPL) % CPR);
+    const int frow = lane & 31, hi = lane >> 5, sw = (frow / RPL) % CPR;
+    const uint32_t smem_base = lds_addr(smem);
 
     int32_t first = blockIdx.x;
     if (p.s.xcd_remap) first = xcd_remap(first, p.s.grid);
@@ -140,24 +191,48 @@ __global__ __launch_bounds__(256, MINB) void gemm_tile_kernel(GemmParams p)
         uint32_t aoff[A_LOADS], boff[B_LOADS];
 #pragma unroll
         for (int i = 0; i < A_LOADS; ++i) {
-            const int r = (i * NW + wave) * 8 + prow;
+            const int r = (i * NW + wave) * ROWS_PER_DMA + drow;
             aoff[i] = (m0 + r < p.M) ? (uint32_t)(r * p.lda + lchunk * 16) : kOOB;
         }
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
-            const int r = (i * NW + wave) * 8 + prow;
+            const int r = (i * NW + wave) * ROWS_PER_DMA + drow;
             boff[i] = (n0 + r < p.N) ? (uint32_t)(r * p.ldb + lchunk * 16) : kOOB;
         }
 
-        auto issue = [&](uint8_t *sa, uint8_t *sb, int32_t kt) {
-            const uint32_t kb = (uint32_t)kt * kRowBytes;
-            const bool kval = (int32_t)(kb + lchunk * 16) < p.Kb;
-#pragma unroll
-            for (int i = 0; i < A_LOADS; ++i)
-                dma16(ra, lds_addr(sa) + (i * NW + wave) * 1024, kval ? aoff[i] + kb : kOOB);
-#pragma unroll
-            for (int i = 0; i < B_LOADS; ++i)
-                dma16(rb, lds_addr(sb) + (i * NW + wave) * 1024, kval ? boff[i] + kb : kOOB);
+        /* Copy of K-tile kt into the stage at LDS byte offset so: chunks past
+         * K, and every chunk of a K-tile past the unit's range, read zero, so
+         * copies can be issued unconditionally (a masked copy only rewrites
+         * LDS rows this wave owns and nobody reads before they are copied
+         * again). */
+        auto kvalid = [&](int32_t kt) __attribute__((always_inline)) {
+            return ((int32_t)((uint32_t)kt * RB + lchunk * 16) < p.Kb) && (kt < un.kt_end);
+        };
+        auto dma = [&](auto dc, uint32_t so, uint32_t kb, bool kv) __attribute__((always_inline)) {
+            constexpr int d = decltype(dc)::value;
+            const uint32_t dst = smem_base + so + wave * 1024;
+            if constexpr (d < A_LOADS)
+                dma16<d * NW * 1024>(ra, dst, kv ? aoff[d] + kb : kOOB);
+            else
+                dma16<A_BYTES + (d - A_LOADS) * NW * 1024>(rb, dst, kv ? boff[d - A_LOADS] + kb : kOOB);
+        };
+        auto copy_tile = [&](uint32_t so, int32_t kt) __attribute__((always_inline)) {
+            const bool kv = kvalid(kt);
+            const uint32_t kb = (uint32_t)kt * RB;
+            unroll<LOADS>([&](auto dc) __attribute__((always_inline)) { dma(dc, so, kb, kv); });
+        };
+
+        /* Fragment of MFMA K-step ks for block blk of this wave, from the
+         * operand rows starting at `rows` (A or B part of a stage). */
+        auto frag = [&](const uint8_t *rows, int ks, int blk) __attribute__((always_inline)) -> Frag {
+            const uint8_t *row = rows + (blk * 32 + frow) * RB;
+            if constexpr (!FP8) {
+                return *(const bf16x8 *)(row + (((2 * ks + hi) ^ sw) * 16));
+            } else {
+                const i32x4 lo = *(const i32x4 *)(row + (((4 * ks + 2 * hi) ^ sw) * 16));
+                const i32x4 up = *(const i32x4 *)(row + (((4 * ks + 2 * hi + 1) ^ sw) * 16));
+                return i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+            }
         };
 
         f32x16 acc[FM][FN];
@@ -167,73 +242,103 @@ __global__ __launch_bounds__(256, MINB) void gemm_tile_kernel(GemmParams p)
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = f32x16{};
 
-        auto compute = [&](const uint8_t *sa, const uint8_t *sb) {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                if constexpr (!FP8) {
-                    const int chunk = (2 * ks + hi) ^ sw;
-                    bf16x8 a[FM], b[FN];
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-                        a[i] = *(const bf16x8 *)(sa + (wm * WTM + i * 32 + frow) * kRowBytes + chunk * 16);
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        b[j] = *(const bf16x8 *)(sb + (wn * WTN + j * 32 + frow) * kRowBytes + chunk * 16);
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-                } else {
-                    const int c0 = (4 * ks + 2 * hi) ^ sw, c1 = (4 * ks + 2 * hi + 1) ^ sw;
-                    i32x8 a[FM], b[FN];
-#pragma unroll
-                    for (int i = 0; i < FM; ++i) {
-                        const uint8_t *row = sa + (wm * WTM + i * 32 + frow) * kRowBytes;
-                        const i32x4 lo = *(const i32x4 *)(row + c0 * 16);
-                        const i32x4 up = *(const i32x4 *)(row + c1 * 16);
-                        a[i] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-                    }
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const uint8_t *row = sb + (wn * WTN + j * 32 + frow) * kRowBytes;
-                        const i32x4 lo = *(const i32x4 *)(row + c0 * 16);
-                        const i32x4 up = *(const i32x4 *)(row + c1 * 16);
-                        b[j] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-                    }
-                    /* format fields 0/0: both operands E4M3; zero scales select
-                     * the unscaled instruction */
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-                }
-            }
-        };
+        /* Fragments double-buffered by K-step parity. */
+        Frag fa[2][FM], fb[2][FN];
 
-        /* Two-stage ring: stage 0 holds even K-tiles of the unit, stage 1
-         * odd ones.  The copy of tile k+1 is issued before tile k's MFMAs;
-         * one barrier per K-tile both publishes the copy and retires the
-         * stage that the next copy overwrites. */
-        const int32_t nkt = un.kt_end - un.kt_begin;
-        if (nkt > 0) {
+        /* One K-step: the FM x FN MFMAs on buffer CUR, interleaved slot by
+         * slot with the fragment reads of step nks of the stage at `ns` into
+         * buffer CUR^1 and, when DMA, with the copies of K-tile dkt into the
+         * stage at byte offset dso.  The scheduling barriers keep this
+         * interleave as written. */
+        auto step = [&](auto cur_c, auto dma_c, const uint8_t *ns, int nks, uint32_t dso,
+                        int32_t dkt) __attribute__((always_inline)) {
+            constexpr int CUR = decltype(cur_c)::value;
+            constexpr bool DMA = decltype(dma_c)::value;
+            constexpr int NM = FM * FN, NR = FM + FN, ND = DMA ? LOADS : 0;
+            constexpr int SLOTS = NM > (NR > ND ? NR : ND) ? NM : (NR > ND ? NR : ND);
+            const uint32_t kb = (uint32_t)dkt * RB;
+            const bool kv = DMA ? kvalid(dkt) : false;
+            /* this step's fragments (read during the previous step) are in;
+             * nothing else is outstanding on the LDS counter here */
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            unroll<SLOTS>([&](auto tc) __attribute__((always_inline)) {
+                constexpr int t = decltype(tc)::value;
+                if constexpr (t < NM) {
+                    constexpr int i = t / FN, j = t % FN;
+                    if constexpr (!FP8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                    else /* format fields 0/0: both operands E4M3; zero scales
+                          * select the unscaled instruction */
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                }
+                if constexpr (t < FM)
+                    fa[CUR ^ 1][t] = frag(ns + wm * WTM * RB, nks, t);
+                else if constexpr (t < NR)
+                    fb[CUR ^ 1][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
+                if constexpr (t < ND) dma(tc, dso, kb, kv);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        using BT = std::true_type;
+        using BF = std::false_type;
+
+        /* One K-tile in the stage at byte offset so; nso is the next tile's
+         * stage.  Fragment buffers alternate by K-step; with an odd number of
+         * K-steps per tile the parity P of the tile shifts them. */
+        auto tile = [&](auto pc, uint32_t so, uint32_t nso, int32_t kt) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
+            const uint8_t *cs = smem + so;
+            unroll<KSTEPS - 1>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int ks = decltype(kc)::value;
+                step(std::integral_constant<int, (ks + P) & 1>{}, BF{}, cs, ks + 1, 0u, 0);
+            });
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            /* tile kt+1 landed: at most STAGES-2 newer tiles still in flight */
+            wait_vmcnt<(STAGES - 2) * LOADS>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            step(std::integral_constant<int, (KSTEPS - 1 + P) & 1>{}, BT{}, smem + nso, 0, so,
+                 kt + STAGES);
+        };
+        auto next_stage = [](uint32_t so) __attribute__((always_inline)) {
+            return so + STAGE_BYTES == STAGES * STAGE_BYTES ? 0u : so + STAGE_BYTES;
+        };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+
+        if (un.kt_begin < un.kt_end) {
             int32_t kt = un.kt_begin;
-            issue(sA0, sB0, kt);
-            stage_barrier();
-            for (int32_t pair = 0; pair < (nkt >> 1); ++pair) {
-                issue(sA1, sB1, kt + 1);
-                compute(sA0, sB0);
-                stage_barrier();
-                if (kt + 2 < un.kt_end) issue(sA0, sB0, kt + 2);
-                compute(sA1, sB1);
-                stage_barrier();
-                kt += 2;
-            }
-            if (nkt & 1) {
-                compute(sA0, sB0);
-                stage_barrier();
+            unroll<STAGES>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int st = decltype(sc)::value;
+                copy_tile(st * STAGE_BYTES, kt + st);
+            });
+            wait_vmcnt<(STAGES - 1) * LOADS>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[0][i] = frag(smem + wm * WTM * RB, 0, i);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[0][j] = frag(smem + A_BYTES + wn * WTN * RB, 0, j);
+            uint32_t so = 0;
+            if constexpr (KSTEPS % 2 == 0) {
+                /* one loop body; the stage advances around the ring */
+                for (; kt < un.kt_end; ++kt) {
+                    const uint32_t nso = next_stage(so);
+                    tile(P0{}, so, nso, kt);
+                    so = nso;
+                }
+            } else {
+                for (;;) {
+                    uint32_t nso = next_stage(so);
+                    tile(P0{}, so, nso, kt);
+                    so = nso;
+                    if (++kt >= un.kt_end) break;
+                    nso = next_stage(so);
+                    tile(P1{}, so, nso, kt);
+                    so = nso;
+                    if (++kt >= un.kt_end) break;
+                }
             }
         }
 
@@ -265,35 +370,55 @@ __global__ __launch_bounds__(256, MINB) void gemm_tile_kernel(GemmParams p)
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, voff,
                                                               ((e >> 2) * 8 + (e & 3)) * TN * 4, 0);
                     }
+                    /* one block at a time keeps the epilogue's registers few */
+                    __builtin_amdgcn_sched_barrier(0);
                 }
         } else {
             const float alpha = unit_alpha(p, un.batch);
-            const int esz = p.out_bf16 ? 2 : 4;
-            const __amdgpu_buffer_rsrc_t rc = make_rsrc(
-                (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * esz);
             const int32_t mrem = p.M - m0, nrem = p.N - n0;
-            const int32_t ldcb = (int32_t)p.ldc * esz;
+            if (p.out_bf16) {
+                const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+                    (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 2);
+                const int32_t ldcb = (int32_t)p.ldc * 2;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = wn * WTN + j * 32 + ecol;
-                    const int row0 = wm * WTM + i * 32 + ehi * 4;
-                    const uint32_t voff = (uint32_t)(row0 * ldcb + col * esz);
+                    for (int j = 0; j < FN; ++j) {
+                        const int col = wn * WTN + j * 32 + ecol;
+                        const int row0 = wm * WTM + i * 32 + ehi * 4;
+                        const uint32_t voff = (uint32_t)(row0 * ldcb + col * 2);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int dr = (e >> 2) * 8 + (e & 3);
-                        const bool ok = (row0 + dr < mrem) && (col < nrem);
-                        const float v = alpha * acc[i][j][e];
-                        if (p.out_bf16)
-                            __builtin_amdgcn_raw_buffer_store_b16(
-                                __builtin_bit_cast(uint16_t, (__bf16)v), rc, ok ? voff : kOOB,
-                                dr * ldcb, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b32(
-                                __builtin_bit_cast(uint32_t, v), rc, ok ? voff : kOOB, dr * ldcb, 0);
+                        for (int e = 0; e < 16; ++e) {
+                            const int dr = (e >> 2) * 8 + (e & 3);
+                            const bool ok = (row0 + dr < mrem) && (col < nrem);
+                            const float v = alpha * acc[i][j][e];
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc,
+                                                                  ok ? voff : kOOB, dr * ldcb, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                }
+            } else {
+                const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+                    (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
+                const int32_t ldcb = (int32_t)p.ldc * 4;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int col = wn * WTN + j * 32 + ecol;
+                        const int row0 = wm * WTM + i * 32 + ehi * 4;
+                        const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int dr = (e >> 2) * 8 + (e & 3);
+                            const bool ok = (row0 + dr < mrem) && (col < nrem);
+                            const float v = alpha * acc[i][j][e];
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc,
+                                                                  ok ? voff : kOOB, dr * ldcb, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
         }
     }
 }
@@ -401,23 +526,34 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, bool FP8, int MINB>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES>
 static hipError_t launch_tile(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB>), dim3(p.s.grid), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES>), dim3(p.s.grid), dim3(256),
+                       0, stream, p);
     return hipGetLastError();
 }
+
+/* Instantiations, in tile-table order (csrc/tiles.h). */
+#define GEMM355_TILES(X)                                                                          \
+    X(0, 256, 256, false, 1, 128, 2)                                                             \
+    X(1, 128, 128, false, 2, 128, 2)                                                             \
+    X(2, 64, 64, false, 4, 128, 2)                                                               \
+    X(3, 256, 256, true, 1, 128, 2)                                                              \
+    X(4, 128, 128, true, 2, 128, 2)                                                              \
+    X(5, 64, 64, true, 4, 128, 2)                                                                \
+    X(6, 256, 256, false, 1, 64, 4)                                                              \
+    X(7, 256, 256, false, 1, 64, 5)                                                              \
+    X(8, 256, 256, true, 1, 64, 4)                                                               \
+    X(9, 256, 256, true, 1, 64, 5)
 
 hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 {
     switch (tile) {
-    case 0: return launch_tile<256, 256, false, 1>(p, stream);
-    case 1: return launch_tile<128, 128, false, 2>(p, stream);
-    case 2: return launch_tile<64, 64, false, 4>(p, stream);
-    case 3: return launch_tile<256, 256, true, 1>(p, stream);
-    case 4: return launch_tile<128, 128, true, 2>(p, stream);
-    case 5: return launch_tile<64, 64, true, 4>(p, stream);
+#define X(id, tm, tn, f8, mb, rb, st) \
+    case id: return launch_tile<tm, tn, f8, mb, rb, st>(p, stream);
+        GEMM355_TILES(X)
+#undef X
     default: return hipErrorInvalidValue;
     }
 }
@@ -425,12 +561,10 @@ hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 const void *gemm_kernel_symbol(int32_t tile)
 {
     switch (tile) {
-    case 0: return (const void *)gemm_tile_kernel<256, 256, false, 1>;
-    case 1: return (const void *)gemm_tile_kernel<128, 128, false, 2>;
-    case 2: return (const void *)gemm_tile_kernel<64, 64, false, 4>;
-    case 3: return (const void *)gemm_tile_kernel<256, 256, true, 1>;
-    case 4: return (const void *)gemm_tile_kernel<128, 128, true, 2>;
-    case 5: return (const void *)gemm_tile_kernel<64, 64, true, 4>;
+#define X(id, tm, tn, f8, mb, rb, st) \
+    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st>;
+        GEMM355_TILES(X)
+#undef X
     default: return nullptr;
     }
 }

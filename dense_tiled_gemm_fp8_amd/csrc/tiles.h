@@ -7,9 +7,10 @@
  * headroom", section "The question I never asked": resident workgroups are
  * the minimum over shared memory and the register file).
  *
- * Every entry stages 128 bytes of K per tile row per stage (64 bf16 or 128
- * E4M3 values), so the LDS layout and the copy pattern are the same for both
- * input types.
+ * An entry stages RB bytes of K per tile row per stage (RB = 128: 64 bf16 or
+ * 128 E4M3 values; RB = 64: half that), so the LDS layout and the copy
+ * pattern are the same for both input types; `stages` K-tiles are in the
+ * ring.
  */
 #ifndef GEMM355_TILES_H
 #define GEMM355_TILES_H
@@ -21,9 +22,10 @@ namespace g355 {
 struct TileCfg {
     int32_t dtype_class;   /* 0 bf16 inputs, 1 E4M3 inputs                  */
     int32_t TM, TN, TK;
+    int32_t row_bytes;     /* RB: K bytes per tile row per stage             */
     int32_t stages;
     int32_t waves_m, waves_n;
-    int32_t lds_bytes;     /* stages * (TM + TN) * 128                       */
+    int32_t lds_bytes;     /* stages * (TM + TN) * RB                        */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
     int32_t vgpr_budget;   /* 512 / min_blocks (one wave per SIMD per group) */
     /* planning prior: fraction of a compute unit's dense MFMA peak the tile
@@ -40,14 +42,19 @@ constexpr int32_t kWaveSize = 64;
 constexpr int32_t kMaxWavesPerSimd = 8;
 
 constexpr TileCfg kTiles[] = {
-    /* bf16 */
-    {0, 256, 256, 64, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
-    {0, 128, 128, 64, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
-    {0, 64, 64, 64, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
-    /* E4M3 */
-    {1, 256, 256, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
-    {1, 128, 128, 128, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
-    {1, 64, 64, 128, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+    /* bf16, 128-byte K-tiles, 2 stages */
+    {0, 256, 256, 64, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
+    {0, 128, 128, 64, 128, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
+    {0, 64, 64, 64, 128, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+    /* E4M3, 128-byte K-tiles, 2 stages */
+    {1, 256, 256, 128, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
+    {1, 128, 128, 128, 128, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
+    {1, 64, 64, 128, 128, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+    /* 256 x 256 with 64-byte K-tiles and a deeper ring */
+    {0, 256, 256, 32, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {0, 256, 256, 32, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}},
+    {1, 256, 256, 64, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {1, 256, 256, 64, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 
