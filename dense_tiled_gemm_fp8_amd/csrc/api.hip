@@ -407,7 +407,8 @@ gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu)
 {
     if (tile < 0 || tile >= kNumTiles || !blocks_per_cu) return GEMM355_EINVAL;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel_symbol(tile), 256, 0) !=
+    const int threads = kTiles[tile].waves_m * kTiles[tile].waves_n * kWaveSize;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel_symbol(tile), threads, 0) !=
         hipSuccess) {
         (void)hipGetLastError();
         return GEMM355_EHIP;

@@ -127,8 +127,10 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
 }
 
 /*
- * One workgroup of 4 wavefronts (2 x 2) computes a TM x TN tile; wavefront
- * (wm, wn) owns a (TM/2) x (TN/2) block made of 32 x 32 MFMA blocks.  A
+ * One workgroup of WGM x WGN wavefronts (4 or 8) computes a TM x TN tile;
+ * wavefront (wm, wn) owns a (TM/WGM) x (TN/WGN) block made of 32 x 32 MFMA
+ * blocks.  With 8 wavefronts two share each SIMD, so one issues MFMAs while
+ * the other waits on LDS or at the barrier.  A
  * K-tile is RB bytes of K per row (64 or 128: 32/64 bf16 or 64/128 E4M3
  * values); the LDS holds a ring of STAGES K-tiles.
  *
@@ -151,11 +153,11 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * issued into the stage just freed, and the last step's MFMAs overlap the
  * reads of the next tile's first fragments.
  */
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES>
-__global__ __launch_bounds__(256, MINB) void gemm_tile_kernel(GemmParams p)
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
-    constexpr int NW = 4, WN = 2;
-    constexpr int WTM = TM / 2, WTN = TN / 2;
+    constexpr int NW = WGM * WGN, WN = WGN;
+    constexpr int WTM = TM / WGM, WTN = TN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int CPR = RB / 16, RPL = 256 / RB, ROWS_PER_DMA = 1024 / RB;
     constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB, STAGE_BYTES = A_BYTES + B_BYTES;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_tile_kernel(GemmParams p)
     const int wm = wave / WN, wn = wave % WN;
     const int drow = lane / CPR;
     /* copy group of load d is d * NW + wave; its rows' (r / RPL) % CPR
-     * depends only on the wave (d * NW * ROWS_PER_DMA / RPL = 16 d) */
+     * depends only on the wave (d * NW * ROWS_PER_DMA / RPL = 4 NW d) */
     const int lchunk = (lane % CPR) ^ (((wave * ROWS_PER_DMA + drow) / RPL) % CPR);
     const int frow = lane & 31, hi = lane >> 5, sw = (frow / RPL) % CPR;
     const uint32_t smem_base = lds_addr(smem);
@@ -526,32 +528,37 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN>
 static hipError_t launch_tile(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES>), dim3(p.s.grid), dim3(256),
-                       0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN>), dim3(p.s.grid),
+                       dim3(WGM * WGN * 64), 0, stream, p);
     return hipGetLastError();
 }
 
-/* Instantiations, in tile-table order (csrc/tiles.h). */
+/* Instantiations, in tile-table order (csrc/tiles.h):
+ * id, TM, TN, E4M3, groups per CU, K-tile bytes, stages, waves along M, N */
 #define GEMM355_TILES(X)                                                                          \
-    X(0, 256, 256, false, 1, 128, 2)                                                             \
-    X(1, 128, 128, false, 2, 128, 2)                                                             \
-    X(2, 64, 64, false, 4, 128, 2)                                                               \
-    X(3, 256, 256, true, 1, 128, 2)                                                              \
-    X(4, 128, 128, true, 2, 128, 2)                                                              \
-    X(5, 64, 64, true, 4, 128, 2)                                                                \
-    X(6, 256, 256, false, 1, 64, 4)                                                              \
-    X(7, 256, 256, false, 1, 64, 5)                                                              \
-    X(8, 256, 256, true, 1, 64, 4)                                                               \
-    X(9, 256, 256, true, 1, 64, 5)
+    X(0, 256, 256, false, 1, 128, 2, 2, 2)                                                       \
+    X(1, 128, 128, false, 2, 128, 2, 2, 2)                                                       \
+    X(2, 64, 64, false, 4, 128, 2, 2, 2)                                                         \
+    X(3, 256, 256, true, 1, 128, 2, 2, 2)                                                        \
+    X(4, 128, 128, true, 2, 128, 2, 2, 2)                                                        \
+    X(5, 64, 64, true, 4, 128, 2, 2, 2)                                                          \
+    X(6, 256, 256, false, 1, 64, 4, 2, 2)                                                        \
+    X(7, 256, 256, false, 1, 64, 5, 2, 2)                                                        \
+    X(8, 256, 256, true, 1, 64, 4, 2, 2)                                                         \
+    X(9, 256, 256, true, 1, 64, 5, 2, 2)                                                         \
+    X(10, 256, 256, false, 1, 128, 2, 2, 4)                                                      \
+    X(11, 256, 256, false, 1, 64, 4, 2, 4)                                                       \
+    X(12, 256, 256, true, 1, 128, 2, 2, 4)                                                       \
+    X(13, 256, 256, true, 1, 64, 4, 2, 4)
 
 hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st) \
-    case id: return launch_tile<tm, tn, f8, mb, rb, st>(p, stream);
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn) \
+    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn>(p, stream);
         GEMM355_TILES(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -561,8 +568,8 @@ hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 const void *gemm_kernel_symbol(int32_t tile)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st) \
-    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st>;
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn) \
+    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn>;
         GEMM355_TILES(X)
 #undef X
     default: return nullptr;

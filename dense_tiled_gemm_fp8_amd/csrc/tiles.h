@@ -27,7 +27,8 @@ struct TileCfg {
     int32_t waves_m, waves_n;
     int32_t lds_bytes;     /* stages * (TM + TN) * RB                        */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
-    int32_t vgpr_budget;   /* 512 / min_blocks (one wave per SIMD per group) */
+    int32_t vgpr_budget;   /* 512 / (min_blocks * waves / 4): registers per
+                              lane one wave may hold                        */
     /* planning prior: fraction of a compute unit's dense MFMA peak the tile
      * sustains with 1, 2, 3, 4 of its workgroups resident on the unit */
     float mfma_eff[4];
@@ -55,6 +56,11 @@ constexpr TileCfg kTiles[] = {
     {0, 256, 256, 32, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}},
     {1, 256, 256, 64, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.79f, 0.79f, 0.79f, 0.79f}},
     {1, 256, 256, 64, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}},
+    /* 256 x 256 with 8 wavefronts (2 x 4, two per SIMD) */
+    {0, 256, 256, 64, 128, 2, 2, 4, 2 * (256 + 256) * 128, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {0, 256, 256, 32, 64, 4, 2, 4, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {1, 256, 256, 128, 128, 2, 2, 4, 2 * (256 + 256) * 128, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {1, 256, 256, 64, 64, 4, 2, 4, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

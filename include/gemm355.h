@@ -207,7 +207,8 @@ GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
 
 /* Workgroups of a tile's main-loop kernel that fit on one compute unit of
  * the current device, as the HIP runtime reports it
- * (hipOccupancyMaxActiveBlocksPerMultiprocessor at 256 threads).  Needs a
+ * (hipOccupancyMaxActiveBlocksPerMultiprocessor at the tile's workgroup
+ * size: 64 threads per wavefront).  Needs a
  * device; EHIP otherwise. */
 GEMM355_API gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu);
 

@@ -257,7 +257,7 @@ def test_main_loop_uses_mfma(tmp_path):
     asm = open(build.device_asm("kernels.hip")).read()
     bodies = re.split(r"\n(?=_ZN4g35516gemm_tile_kernel\w+:)", asm)
     kernels = [b for b in bodies if re.match(r"_ZN4g35516gemm_tile_kernel\w+:", b)]
-    assert len(kernels) == 10
+    assert len(kernels) == 14
     for body in kernels:
         name = body.split(":")[0]
         fp8 = "Lb1E" in name

@@ -17,8 +17,8 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-BF16_TILES = [0, 1, 2, 6, 7]
-E4M3_TILES = [3, 4, 5, 8, 9]
+BF16_TILES = [0, 1, 2, 6, 7, 10, 11]
+E4M3_TILES = [3, 4, 5, 8, 9, 12, 13]
 
 
 def ops_from(M, N, K, fmt, seed, dist="uniform", batch=0):
