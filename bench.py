@@ -132,25 +132,25 @@ class Case:
 
 
 def time_case(case, torch, steps, warmup):
-    """Warm up, then time `steps` calls: wall clock around the whole region
-    (synchronised on both sides) and one HIP event pair per call on the
-    launch stream."""
+    """Warm up, then time `steps` back-to-back calls: wall clock around the
+    whole region (synchronised on both sides) and one HIP event pair on the
+    launch stream around the same calls.  Returns (wall seconds, event
+    seconds), both for all `steps` calls."""
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     for _ in range(warmup):
         case.step(sp)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         case.step(sp)
-        e1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
-    return wall, per
+    return wall, e0.elapsed_time(e1) * 1e-3
 
 
 def cpu_baseline(torch, budget_s=15.0):
@@ -205,10 +205,10 @@ def main():
     log("bench: plan", {k: head.plan[k] for k in ("tile", "T_M", "T_N", "T_K", "G", "grid", "split")})
     torch.cuda.synchronize()
     # timed region: barrier (single rank) + synchronize on both sides
-    wall, per = time_case(head, torch, args.steps, args.warmup)
+    wall, ev = time_case(head, torch, args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
     value = head.flops * args.steps / wall / 1e12
-    kern_avg = sum(per) / len(per)
+    kern_avg = ev / args.steps
     achieved = head.flops / kern_avg / 1e12
     log("bench: %.3f ms/step wall, kernel avg %.2f us, %.1f TFLOP/s" % (ms_per_step, kern_avg * 1e6, achieved))
 
@@ -227,12 +227,18 @@ def main():
                     continue
                 log("bench: detail", w.name, w.shapes[si])
                 c = head if (w is head_w and si == 0) else Case(w, si, torch, g, inputs)
-                _, pc = time_case(c, torch, max(10, args.steps // 2), max(3, args.warmup // 2))
-                med = pc[len(pc) // 2]
+                # three timed repetitions; the median of their per-call averages
+                reps = []
+                for _ in range(3):
+                    n = max(10, args.steps // 2)
+                    _, ev_c = time_case(c, torch, n, max(3, args.warmup // 2))
+                    reps.append(ev_c / n)
+                reps.sort()
+                med = reps[1]
                 p = c.plan
                 detail.append({
                     "workload": c.name(), "dtype": w.fmt, "out": w.out,
-                    "us_median": round(med * 1e6, 2), "us_min": round(pc[0] * 1e6, 2),
+                    "us_median": round(med * 1e6, 2), "us_min": round(reps[0] * 1e6, 2),
                     "tflops": round(c.flops / med / 1e12, 1),
                     "pct_mfma_peak": round(100 * c.flops / med / 1e12 / PEAK_TFLOPS[w.fmt], 1),
                     "hbm_gbs": round(c.alg_bytes / med / 1e9, 1),

@@ -44,22 +44,22 @@ constexpr int32_t kMaxWavesPerSimd = 8;
 
 constexpr TileCfg kTiles[] = {
     /* bf16, 128-byte K-tiles, 2 stages */
-    {0, 256, 256, 64, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
+    {0, 256, 256, 64, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
     {0, 128, 128, 64, 128, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
     {0, 64, 64, 64, 128, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
     /* E4M3, 128-byte K-tiles, 2 stages */
-    {1, 256, 256, 128, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}},
+    {1, 256, 256, 128, 128, 2, 2, 2, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
     {1, 128, 128, 128, 128, 2, 2, 2, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
     {1, 64, 64, 128, 128, 2, 2, 2, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
     /* 256 x 256 with 64-byte K-tiles and a deeper ring */
-    {0, 256, 256, 32, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.79f, 0.79f, 0.79f, 0.79f}},
-    {0, 256, 256, 32, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}},
-    {1, 256, 256, 64, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.79f, 0.79f, 0.79f, 0.79f}},
-    {1, 256, 256, 64, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}},
+    {0, 256, 256, 32, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
+    {0, 256, 256, 32, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
+    {1, 256, 256, 64, 64, 4, 2, 2, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
+    {1, 256, 256, 64, 64, 5, 2, 2, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
     /* 256 x 256 with 8 wavefronts (2 x 4, two per SIMD) */
-    {0, 256, 256, 64, 128, 2, 2, 4, 2 * (256 + 256) * 128, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {0, 256, 256, 64, 128, 2, 2, 4, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}},
     {0, 256, 256, 32, 64, 4, 2, 4, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
-    {1, 256, 256, 128, 128, 2, 2, 4, 2 * (256 + 256) * 128, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {1, 256, 256, 128, 128, 2, 2, 4, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}},
     {1, 256, 256, 64, 64, 4, 2, 4, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
