@@ -36,6 +36,7 @@ struct ReduceParams {
     int32_t M, N, TM, TN;
     int32_t out_bf16;
     int32_t tail;                 /* 1: reduce the tail tiles, 0: all tiles */
+    int32_t sg_log2, chunks;      /* set by launch_reduce                   */
     Sched s;
 };
 

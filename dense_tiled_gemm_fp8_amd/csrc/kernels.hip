@@ -115,6 +115,8 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+template <int V> using IC = std::integral_constant<int, V>;
+
 template <bool FP8> struct FragType { typedef bf16x8 type; };
 template <> struct FragType<true> { typedef i32x8 type; };
 
@@ -153,7 +155,7 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * issued into the stage just freed, and the last step's MFMAs overlap the
  * reads of the next tile's first fragments.
  */
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
     constexpr int NW = WGM * WGN, WN = WGN;
@@ -167,7 +169,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     constexpr int KSTEPS = FP8 ? RB / 64 : RB / 32;
     using Frag = typename FragType<FP8>::type;
     static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1 && KSTEPS >= 1, "tile");
-    static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "ring depth");
+    static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "ring depth");
+    static_assert(!SPREAD || STAGES >= 3, "spread copies need a third stage");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -175,9 +178,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int drow = lane / CPR;
-    /* copy group of load d is d * NW + wave; its rows' (r / RPL) % CPR
-     * depends only on the wave (d * NW * ROWS_PER_DMA / RPL = 4 NW d) */
-    const int lchunk = (lane % CPR) ^ (((wave * ROWS_PER_DMA + drow) / RPL) % CPR);
+    /* Copy d of a stage part is copy group d * NW + wave; the lane's row is
+     * r = (d * NW + wave) * ROWS_PER_DMA + drow, and ROWS_PER_DMA = 4 RPL,
+     * so (r / RPL) % CPR = (4 (d NW + wave) + drow / RPL) % CPR: with
+     * 4 NW a multiple of CPR it is the same for every d, otherwise (CPR = 8,
+     * NW odd) it alternates with the parity of d.  lchunk[d & 1] is the
+     * logical chunk the lane fetches. */
+    constexpr bool TWO = (4 * NW) % CPR != 0;
+    int lchunk[2];
+    lchunk[0] = (lane % CPR) ^ ((4 * wave + drow / RPL) % CPR);
+    lchunk[1] = (lane % CPR) ^ ((4 * (NW + wave) + drow / RPL) % CPR);
     const int frow = lane & 31, hi = lane >> 5, sw = (frow / RPL) % CPR;
     const uint32_t smem_base = lds_addr(smem);
 
@@ -194,12 +204,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
 #pragma unroll
         for (int i = 0; i < A_LOADS; ++i) {
             const int r = (i * NW + wave) * ROWS_PER_DMA + drow;
-            aoff[i] = (m0 + r < p.M) ? (uint32_t)(r * p.lda + lchunk * 16) : kOOB;
+            aoff[i] = (m0 + r < p.M) ? (uint32_t)(r * p.lda + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
         }
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
             const int r = (i * NW + wave) * ROWS_PER_DMA + drow;
-            boff[i] = (n0 + r < p.N) ? (uint32_t)(r * p.ldb + lchunk * 16) : kOOB;
+            boff[i] = (n0 + r < p.N) ? (uint32_t)(r * p.ldb + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
         }
 
         /* Copy of K-tile kt into the stage at LDS byte offset so: chunks past
@@ -207,20 +217,34 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
          * copies can be issued unconditionally (a masked copy only rewrites
          * LDS rows this wave owns and nobody reads before they are copied
          * again). */
-        auto kvalid = [&](int32_t kt) __attribute__((always_inline)) {
-            return ((int32_t)((uint32_t)kt * RB + lchunk * 16) < p.Kb) && (kt < un.kt_end);
+        /* per parity class of the copy index (one class unless TWO) */
+        struct KV {
+            bool v[2];
         };
-        auto dma = [&](auto dc, uint32_t so, uint32_t kb, bool kv) __attribute__((always_inline)) {
+        /* iteration i of the unit's loop works on K-tile kt_begin + i */
+        const int32_t nkt = un.kt_end - un.kt_begin;
+        auto ktile = [&](int32_t i) __attribute__((always_inline)) { return un.kt_begin + i; };
+        /* copies of iteration i; iterations past the range read zero */
+        auto kvalid = [&](int32_t i) __attribute__((always_inline)) {
+            const uint32_t kb = (uint32_t)ktile(i) * RB;
+            KV k;
+            k.v[0] = ((int32_t)(kb + lchunk[0] * 16) < p.Kb) && (i < nkt);
+            k.v[1] = TWO ? ((int32_t)(kb + lchunk[1] * 16) < p.Kb) && (i < nkt) : k.v[0];
+            return k;
+        };
+        auto dma = [&](auto dc, uint32_t so, uint32_t kb, const KV &kv) __attribute__((always_inline)) {
             constexpr int d = decltype(dc)::value;
+            constexpr int di = d < A_LOADS ? d : d - A_LOADS;
+            const bool ok = kv.v[TWO ? di & 1 : 0];
             const uint32_t dst = smem_base + so + wave * 1024;
             if constexpr (d < A_LOADS)
-                dma16<d * NW * 1024>(ra, dst, kv ? aoff[d] + kb : kOOB);
+                dma16<d * NW * 1024>(ra, dst, ok ? aoff[d] + kb : kOOB);
             else
-                dma16<A_BYTES + (d - A_LOADS) * NW * 1024>(rb, dst, kv ? boff[d - A_LOADS] + kb : kOOB);
+                dma16<A_BYTES + (d - A_LOADS) * NW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
         };
-        auto copy_tile = [&](uint32_t so, int32_t kt) __attribute__((always_inline)) {
-            const bool kv = kvalid(kt);
-            const uint32_t kb = (uint32_t)kt * RB;
+        auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
+            const KV kv = kvalid(i);
+            const uint32_t kb = (uint32_t)ktile(i) * RB;
             unroll<LOADS>([&](auto dc) __attribute__((always_inline)) { dma(dc, so, kb, kv); });
         };
 
@@ -249,17 +273,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
 
         /* One K-step: the FM x FN MFMAs on buffer CUR, interleaved slot by
          * slot with the fragment reads of step nks of the stage at `ns` into
-         * buffer CUR^1 and, when DMA, with the copies of K-tile dkt into the
-         * stage at byte offset dso.  The scheduling barriers keep this
-         * interleave as written. */
-        auto step = [&](auto cur_c, auto dma_c, const uint8_t *ns, int nks, uint32_t dso,
-                        int32_t dkt) __attribute__((always_inline)) {
+         * buffer CUR^1 and with copies D0 .. D0+DN-1 of the K-tile at byte
+         * kb into the stage at byte offset dso, copy j at slot
+         * j * SLOTS / DN.  The scheduling barriers keep this interleave as
+         * written. */
+        auto step = [&](auto cur_c, auto d0_c, auto dn_c, const uint8_t *ns, int nks, uint32_t dso,
+                        uint32_t kb, const KV &kv) __attribute__((always_inline)) {
             constexpr int CUR = decltype(cur_c)::value;
-            constexpr bool DMA = decltype(dma_c)::value;
-            constexpr int NM = FM * FN, NR = FM + FN, ND = DMA ? LOADS : 0;
-            constexpr int SLOTS = NM > (NR > ND ? NR : ND) ? NM : (NR > ND ? NR : ND);
-            const uint32_t kb = (uint32_t)dkt * RB;
-            const bool kv = DMA ? kvalid(dkt) : false;
+            constexpr int D0 = decltype(d0_c)::value, DN = decltype(dn_c)::value;
+            constexpr int NM = FM * FN, NR = FM + FN;
+            constexpr int SLOTS = NM > (NR > DN ? NR : DN) ? NM : (NR > DN ? NR : DN);
             /* this step's fragments (read during the previous step) are in;
              * nothing else is outstanding on the LDS counter here */
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -278,30 +301,54 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                     fa[CUR ^ 1][t] = frag(ns + wm * WTM * RB, nks, t);
                 else if constexpr (t < NR)
                     fb[CUR ^ 1][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
-                if constexpr (t < ND) dma(tc, dso, kb, kv);
+                if constexpr (DN > 0) {
+                    constexpr int j = (t * DN + SLOTS - 1) / SLOTS;
+                    if constexpr (j < DN && (j * SLOTS) / DN == t)
+                        dma(std::integral_constant<int, D0 + j>{}, dso, kb, kv);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        using BT = std::true_type;
-        using BF = std::false_type;
 
         /* One K-tile in the stage at byte offset so; nso is the next tile's
          * stage.  Fragment buffers alternate by K-step; with an odd number of
-         * K-steps per tile the parity P of the tile shifts them. */
-        auto tile = [&](auto pc, uint32_t so, uint32_t nso, int32_t kt) __attribute__((always_inline)) {
+         * K-steps per tile the parity P of the tile shifts them.
+         *
+         * Copies: without SPREAD, K-tile kt+STAGES goes into this tile's own
+         * stage during its last step (the stage is free once the barrier
+         * shows every wave has read it).  With SPREAD, K-tile kt+STAGES-1
+         * goes into the stage dso of tile kt-1 (free since the previous
+         * barrier), its copies spread evenly over all K-steps, so the copy
+         * queue never receives a whole K-tile at once. */
+        auto tile = [&](auto pc, uint32_t so, uint32_t nso, uint32_t dso, int32_t kt) __attribute__((always_inline)) {
+            /* kt: the iteration index within the unit */
             constexpr int P = decltype(pc)::value;
+            constexpr int LPRE = SPREAD ? (KSTEPS - 1) * LOADS / KSTEPS : 0;
             const uint8_t *cs = smem + so;
+            KV kv{{false, false}};
+            uint32_t kb = 0;
+            if constexpr (SPREAD) {
+                kv = kvalid(kt + STAGES - 1);
+                kb = (uint32_t)ktile(kt + STAGES - 1) * RB;
+            }
             unroll<KSTEPS - 1>([&](auto kc) __attribute__((always_inline)) {
                 constexpr int ks = decltype(kc)::value;
-                step(std::integral_constant<int, (ks + P) & 1>{}, BF{}, cs, ks + 1, 0u, 0);
+                constexpr int D0 = SPREAD ? ks * LOADS / KSTEPS : 0;
+                constexpr int DN = SPREAD ? (ks + 1) * LOADS / KSTEPS - D0 : 0;
+                step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, ks + 1, dso, kb, kv);
             });
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            /* tile kt+1 landed: at most STAGES-2 newer tiles still in flight */
-            wait_vmcnt<(STAGES - 2) * LOADS>();
+            /* tile kt+1 landed: later copies may still be in flight */
+            wait_vmcnt<SPREAD ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            step(std::integral_constant<int, (KSTEPS - 1 + P) & 1>{}, BT{}, smem + nso, 0, so,
-                 kt + STAGES);
+            if constexpr (SPREAD) {
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, 0, dso, kb, kv);
+            } else {
+                kv = kvalid(kt + STAGES);
+                kb = (uint32_t)ktile(kt + STAGES) * RB;
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, 0, so, kb, kv);
+            }
         };
         auto next_stage = [](uint32_t so) __attribute__((always_inline)) {
             return so + STAGE_BYTES == STAGES * STAGE_BYTES ? 0u : so + STAGE_BYTES;
@@ -309,37 +356,42 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
 
-        if (un.kt_begin < un.kt_end) {
-            int32_t kt = un.kt_begin;
-            unroll<STAGES>([&](auto sc) __attribute__((always_inline)) {
+        if (nkt > 0) {
+            int32_t kt = 0;
+            /* prologue: the first PRE K-tiles of the unit */
+            constexpr int PRE = SPREAD ? STAGES - 1 : STAGES;
+            unroll<PRE>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int st = decltype(sc)::value;
                 copy_tile(st * STAGE_BYTES, kt + st);
             });
-            wait_vmcnt<(STAGES - 1) * LOADS>();
+            wait_vmcnt<(PRE - 1) * LOADS>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[0][i] = frag(smem + wm * WTM * RB, 0, i);
 #pragma unroll
             for (int j = 0; j < FN; ++j) fb[0][j] = frag(smem + A_BYTES + wn * WTN * RB, 0, j);
-            uint32_t so = 0;
+            uint32_t so = 0, dso = (STAGES - 1) * STAGE_BYTES;
             if constexpr (KSTEPS % 2 == 0) {
                 /* one loop body; the stage advances around the ring */
-                for (; kt < un.kt_end; ++kt) {
+                for (; kt < nkt; ++kt) {
                     const uint32_t nso = next_stage(so);
-                    tile(P0{}, so, nso, kt);
+                    tile(P0{}, so, nso, dso, kt);
+                    dso = so;
                     so = nso;
                 }
             } else {
                 for (;;) {
                     uint32_t nso = next_stage(so);
-                    tile(P0{}, so, nso, kt);
+                    tile(P0{}, so, nso, dso, kt);
+                    dso = so;
                     so = nso;
-                    if (++kt >= un.kt_end) break;
+                    if (++kt >= nkt) break;
                     nso = next_stage(so);
-                    tile(P1{}, so, nso, kt);
+                    tile(P1{}, so, nso, dso, kt);
+                    dso = so;
                     so = nso;
-                    if (++kt >= un.kt_end) break;
+                    if (++kt >= nkt) break;
                 }
             }
         }
@@ -430,9 +482,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
  * tail tile x), 256 threads x 4 consecutive elements per step over the
  * TM x TN partial tile.  Slices are summed in ascending order in fp32.
  */
+/*
+ * Split-K combine.  Block x = (reduce tile q, chunk of P float4 positions of
+ * the tile); its 256 threads are SG slice groups of P = 256 / SG positions.
+ * Group g sums slices [g nsl / SG, (g + 1) nsl / SG) of its position in
+ * ascending order; the group sums are then added in ascending group order,
+ * so the result is the same on every run.
+ */
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
 {
-    const int32_t q = blockIdx.x;
+    __shared__ f32x4 part[256];
+    const int32_t q = blockIdx.x / r.chunks, chunk = blockIdx.x % r.chunks;
     int32_t tile, nsl;
     if (r.tail) {
         tile = r.s.tail_first + q;
@@ -444,30 +504,48 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
     Unit un;
     tile_coords(r.s, tile, un);
     const int32_t m0 = un.tile_m * r.TM, n0 = un.tile_n * r.TN;
+    const int32_t SG = 1 << r.sg_log2, P = 256 >> r.sg_log2;
+    const int32_t g = (int32_t)threadIdx.x / P, pos = (int32_t)threadIdx.x % P;
+    const int64_t tile_f4 = (int64_t)r.TM * r.TN / 4;
+    const int64_t e4 = (int64_t)chunk * P + pos;
+    const bool live = e4 < tile_f4;
+    const int32_t s_lo = (int32_t)((int64_t)g * nsl / SG), s_hi = (int32_t)((int64_t)(g + 1) * nsl / SG);
+    f32x4 sum = f32x4{};
+    if (live) {
+        const f32x4 *src = (const f32x4 *)(r.ws + (int64_t)q * nsl * r.TM * r.TN) + e4;
+        int32_t i = s_lo;
+        for (; i + 4 <= s_hi; i += 4) {
+            const f32x4 v0 = src[(int64_t)i * tile_f4], v1 = src[(int64_t)(i + 1) * tile_f4];
+            const f32x4 v2 = src[(int64_t)(i + 2) * tile_f4], v3 = src[(int64_t)(i + 3) * tile_f4];
+            sum += v0;
+            sum += v1;
+            sum += v2;
+            sum += v3;
+        }
+        for (; i < s_hi; ++i) sum += src[(int64_t)i * tile_f4];
+    }
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    if (g != 0 || !live) return;
+    for (int32_t h = 1; h < SG; ++h) sum += part[h * P + pos];
+
     float alpha = 1.0f;
     if (r.scale_a) alpha *= r.scale_a[un.batch];
     if (r.scale_b) alpha *= r.scale_b[un.batch];
-    const int64_t tile_elems = (int64_t)r.TM * r.TN;
-    const float *src = r.ws + (int64_t)q * nsl * tile_elems;
-    const int64_t cbase = (int64_t)un.batch * r.stride_c;
-    for (int64_t e = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * 4; e < tile_elems;
-         e += (int64_t)gridDim.y * blockDim.x * 4) {
-        f32x4 s = *(const f32x4 *)(src + e);
-        for (int32_t i = 1; i < nsl; ++i) s += *(const f32x4 *)(src + i * tile_elems + e);
-        const int32_t row = m0 + (int32_t)(e / r.TN);
-        const int32_t col0 = n0 + (int32_t)(e % r.TN);
-        if (row >= r.M) continue;
+    const int64_t e = e4 * 4;
+    const int32_t row = m0 + (int32_t)(e / r.TN);
+    const int32_t col0 = n0 + (int32_t)(e % r.TN);
+    if (row >= r.M) return;
+    const int64_t cbase = (int64_t)un.batch * r.stride_c + (int64_t)row * r.ldc;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int32_t col = col0 + c;
-            if (col < r.N) {
-                const float v = alpha * s[c];
-                const int64_t idx = cbase + (int64_t)row * r.ldc + col;
-                if (r.out_bf16)
-                    ((__bf16 *)r.C)[idx] = (__bf16)v;
-                else
-                    ((float *)r.C)[idx] = v;
-            }
+    for (int c = 0; c < 4; ++c) {
+        const int32_t col = col0 + c;
+        if (col < r.N) {
+            const float v = alpha * sum[c];
+            if (r.out_bf16)
+                ((__bf16 *)r.C)[cbase + col] = (__bf16)v;
+            else
+                ((float *)r.C)[cbase + col] = v;
         }
     }
 }
@@ -528,37 +606,70 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD>
 static hipError_t launch_tile(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN>), dim3(p.s.grid),
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD>), dim3(p.s.grid),
                        dim3(WGM * WGN * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 /* Instantiations, in tile-table order (csrc/tiles.h):
- * id, TM, TN, E4M3, groups per CU, K-tile bytes, stages, waves along M, N */
+ * id, TM, TN, E4M3, groups per CU, K-tile bytes, stages, waves along M, N,
+ * copies spread over the K-steps */
 #define GEMM355_TILES(X)                                                                          \
-    X(0, 256, 256, false, 1, 128, 2, 2, 2)                                                       \
-    X(1, 128, 128, false, 2, 128, 2, 2, 2)                                                       \
-    X(2, 64, 64, false, 4, 128, 2, 2, 2)                                                         \
-    X(3, 256, 256, true, 1, 128, 2, 2, 2)                                                        \
-    X(4, 128, 128, true, 2, 128, 2, 2, 2)                                                        \
-    X(5, 64, 64, true, 4, 128, 2, 2, 2)                                                          \
-    X(6, 256, 256, false, 1, 64, 4, 2, 2)                                                        \
-    X(7, 256, 256, false, 1, 64, 5, 2, 2)                                                        \
-    X(8, 256, 256, true, 1, 64, 4, 2, 2)                                                         \
-    X(9, 256, 256, true, 1, 64, 5, 2, 2)                                                         \
-    X(10, 256, 256, false, 1, 128, 2, 2, 4)                                                      \
-    X(11, 256, 256, false, 1, 64, 4, 2, 4)                                                       \
-    X(12, 256, 256, true, 1, 128, 2, 2, 4)                                                       \
-    X(13, 256, 256, true, 1, 64, 4, 2, 4)
+    X(0, 256, 256, false, 1, 128, 2, 2, 2, 0)                                                       \
+    X(1, 128, 128, false, 2, 128, 2, 2, 2, 0)                                                       \
+    X(2, 64, 64, false, 4, 128, 2, 2, 2, 0)                                                         \
+    X(3, 256, 256, true, 1, 128, 2, 2, 2, 0)                                                        \
+    X(4, 128, 128, true, 2, 128, 2, 2, 2, 0)                                                        \
+    X(5, 64, 64, true, 4, 128, 2, 2, 2, 0)                                                          \
+    X(6, 256, 256, false, 1, 64, 4, 2, 2, 0)                                                        \
+    X(7, 256, 256, false, 1, 64, 5, 2, 2, 0)                                                        \
+    X(8, 256, 256, true, 1, 64, 4, 2, 2, 0)                                                         \
+    X(9, 256, 256, true, 1, 64, 5, 2, 2, 0)                                                         \
+    X(10, 256, 256, false, 1, 128, 2, 2, 4, 0)                                                      \
+    X(11, 256, 256, false, 1, 64, 4, 2, 4, 0)                                                       \
+    X(12, 256, 256, true, 1, 128, 2, 2, 4, 0)                                                       \
+    X(13, 256, 256, true, 1, 64, 4, 2, 4, 0)                                                        \
+    X(14, 64, 64, false, 1, 128, 8, 2, 2, 0)                                                        \
+    X(15, 64, 64, false, 2, 128, 4, 2, 2, 0)                                                        \
+    X(16, 128, 128, false, 1, 128, 4, 2, 2, 0)                                                      \
+    X(17, 64, 64, true, 1, 128, 8, 2, 2, 0)                                                         \
+    X(18, 64, 64, true, 2, 128, 4, 2, 2, 0)                                                         \
+    X(19, 128, 128, true, 1, 128, 4, 2, 2, 0)                                                       \
+    X(20, 64, 64, false, 4, 128, 2, 1, 1, 0)                                                        \
+    X(21, 64, 64, false, 2, 128, 4, 1, 1, 0)                                                        \
+    X(22, 64, 64, true, 4, 128, 2, 1, 1, 0)                                                         \
+    X(23, 64, 64, true, 2, 128, 4, 1, 1, 0)                                                         \
+    X(24, 256, 256, false, 1, 64, 4, 2, 2, 1)                                                       \
+    X(25, 256, 256, false, 1, 64, 5, 2, 2, 1)                                                       \
+    X(26, 256, 256, false, 1, 64, 4, 2, 4, 1)                                                       \
+    X(27, 256, 256, false, 1, 64, 5, 2, 4, 1)                                                       \
+    X(28, 256, 256, true, 1, 64, 4, 2, 2, 1)                                                        \
+    X(29, 256, 256, true, 1, 64, 5, 2, 2, 1)                                                        \
+    X(30, 256, 256, true, 1, 64, 4, 2, 4, 1)                                                        \
+    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1)
+
+/* every instantiation agrees with its tile-table entry */
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp)                                                      \
+    static_assert(kTiles[id].dtype_class == (f8 ? 1 : 0) && kTiles[id].TM == tm &&               \
+                      kTiles[id].TN == tn && kTiles[id].min_blocks == mb &&                      \
+                      kTiles[id].row_bytes == rb && kTiles[id].stages == st &&                   \
+                      kTiles[id].waves_m == wm && kTiles[id].waves_n == wn &&                    \
+                      kTiles[id].TK == (f8 ? rb : rb / 2) && kTiles[id].spread == sp,            \
+                  "tile table entry " #id);
+GEMM355_TILES(X)
+#undef X
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp) +1
+static_assert(0 GEMM355_TILES(X) == kNumTiles, "one instantiation per tile-table entry");
+#undef X
 
 hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn) \
-    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn>(p, stream);
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp) \
+    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp>(p, stream);
         GEMM355_TILES(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -568,22 +679,26 @@ hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 const void *gemm_kernel_symbol(int32_t tile)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn) \
-    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn>;
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp) \
+    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp>;
         GEMM355_TILES(X)
 #undef X
     default: return nullptr;
     }
 }
 
-hipError_t launch_reduce(const ReduceParams &r, int32_t tiles, hipStream_t stream)
+hipError_t launch_reduce(const ReduceParams &r0, int32_t tiles, hipStream_t stream)
 {
-    const int64_t elems = (int64_t)r.TM * r.TN;
-    int32_t ychunks = (int32_t)((elems / 4 + 255) / 256);
-    /* enough blocks to cover the device even for one tile */
-    if ((int64_t)tiles * ychunks > 4096) ychunks = (int32_t)((4096 + tiles - 1) / tiles);
-    if (ychunks < 1) ychunks = 1;
-    hipLaunchKernelGGL(reduce_kernel, dim3(tiles, ychunks), dim3(256), 0, stream, r);
+    ReduceParams r = r0;
+    const int32_t nsl = r.tail ? r.s.tail_split : r.s.split;
+    /* slice groups: about four slices per thread, at most 64 groups */
+    int32_t lg = 0;
+    while (lg < 6 && (2 << lg) * 4 <= nsl) ++lg;
+    r.sg_log2 = lg;
+    const int64_t tile_f4 = (int64_t)r.TM * r.TN / 4;
+    const int32_t P = 256 >> lg;
+    r.chunks = (int32_t)((tile_f4 + P - 1) / P);
+    hipLaunchKernelGGL(reduce_kernel, dim3((uint32_t)((int64_t)tiles * r.chunks)), dim3(256), 0, stream, r);
     return hipGetLastError();
 }
 

@@ -17,8 +17,10 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-BF16_TILES = [0, 1, 2, 6, 7, 10, 11]
-E4M3_TILES = [3, 4, 5, 8, 9, 12, 13]
+# every entry of the library's tile table, by input type
+_TILES = [(t, g.gemm355_tile_info(t)["dtype_class"]) for t in range(g.gemm355_num_tiles())]
+BF16_TILES = [t for t, c in _TILES if c == 0]
+E4M3_TILES = [t for t, c in _TILES if c == 1]
 
 
 def ops_from(M, N, K, fmt, seed, dist="uniform", batch=0):
