@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--workload", default=None, help="time only this workload name (detail)")
+    ap.add_argument("--profile", default=None, metavar="NAME[:INDEX]",
+                    help="only run warmup + steps calls of this workload shape (for counter "
+                         "collection under rocprofv3) and print its time")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -118,6 +121,26 @@ class Case:
                 a.workspace_bytes = self.plan["workspace_bytes"]
         self.g = g
         self.i = 0
+
+    def measured_eta(self, torch):
+        """One extra call with the per-unit clock hook: the summed busy time
+        of all units over (compute units x resident groups x makespan)."""
+        p = self.plan
+        if not p["units"]:
+            return None
+        stamps = torch.zeros(2 * p["units"], dtype=torch.int64, device="cuda")
+        a = self.args[0]
+        a.unit_stamps = stamps.data_ptr()
+        try:
+            self.g.gemm355_gemm_ex(a, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+        finally:
+            a.unit_stamps = None
+        st = stamps.view(-1, 2).cpu().numpy().astype("float64")
+        span = st[:, 1].max() - st[:, 0].min()
+        if span <= 0:
+            return None
+        return float((st[:, 1] - st[:, 0]).sum() / (p["S"] * p["b"] * span))
 
     def step(self, stream):
         a = self.args[self.i % self.copies]
@@ -199,6 +222,16 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.profile:
+        name, _, si = args.profile.partition(":")
+        w = next(x for x in inputs.WORKLOADS if x.name == name)
+        c = Case(w, int(si or 0), torch, g, inputs)
+        _, ev = time_case(c, torch, args.steps, args.warmup)
+        print(json.dumps({"workload": c.name(), "us_per_call": round(ev / args.steps * 1e6, 2),
+                          "tile": c.plan["tile"], "split": c.plan["split"],
+                          "tail": [c.plan["tail_tiles"], c.plan["tail_split"]]}), flush=True)
+        return
+
     head_w = inputs.WORKLOADS[1]
     log("bench: building inputs for", head_w.name)
     head = Case(head_w, 0, torch, g, inputs)
@@ -249,6 +282,7 @@ def main():
                     "eta_wave": [p["eta_wave_num"], p["eta_wave_den"]],
                     "eta_pad": [p["eta_pad_num"], p["eta_pad_den"]],
                     "eta_sched": [p["eta_sched_num"], p["eta_sched_den"]],
+                    "eta_measured": (lambda e: None if e is None else round(e, 4))(c.measured_eta(torch)),
                 })
                 if c is not head:
                     del c

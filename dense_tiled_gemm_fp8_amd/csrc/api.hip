@@ -246,6 +246,7 @@ gemm355_status run(const gemm355_args &a, void *stream)
     gp.N = (int32_t)a.N;
     gp.Kb = P.Kb;
     gp.out_bf16 = P.out_esize == 2 ? 1 : 0;
+    gp.stamps = a.unit_stamps;
     gp.s = P.s;
     if (P.s.grid > 0 && launch_gemm(P.pub.tile, gp, hs) != hipSuccess) return GEMM355_EHIP;
 

@@ -25,6 +25,7 @@ struct GemmParams {
     const float *scale_a, *scale_b;
     int32_t M, N, Kb;             /* Kb: K in bytes (multiple of 16)        */
     int32_t out_bf16;
+    uint64_t *stamps;             /* per-unit start/end clock or null       */
     Sched s;
 };
 

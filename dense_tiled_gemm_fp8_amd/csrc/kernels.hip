@@ -195,6 +195,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     if (p.s.xcd_remap) first = xcd_remap(first, p.s.grid);
 
     for (int32_t u = first; u < p.s.units; u += p.s.grid) {
+        uint64_t stamp0 = 0;
+        if (p.stamps) stamp0 = __builtin_amdgcn_s_memrealtime();
         const Unit un = decode_unit(p.s, u);
         const int32_t m0 = un.tile_m * TM, n0 = un.tile_n * TN;
         const i32x4 ra = rsrc_words(p.A + (int64_t)un.batch * p.stride_a + (int64_t)m0 * p.lda);
@@ -474,6 +476,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                     }
             }
         }
+        if (p.stamps) {
+            /* every wave's stores of this unit have completed */
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            const uint64_t stamp1 = __builtin_amdgcn_s_memrealtime();
+            if (threadIdx.x == 0) {
+                p.stamps[2 * (int64_t)u] = stamp0;
+                p.stamps[2 * (int64_t)u + 1] = stamp1;
+            }
+        }
     }
 }
 
@@ -649,7 +661,10 @@ static hipError_t launch_tile(const GemmParams &p, hipStream_t stream)
     X(28, 256, 256, true, 1, 64, 4, 2, 2, 1)                                                        \
     X(29, 256, 256, true, 1, 64, 5, 2, 2, 1)                                                        \
     X(30, 256, 256, true, 1, 64, 4, 2, 4, 1)                                                        \
-    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1)
+    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1)                                                        \
+    X(32, 256, 256, false, 1, 128, 2, 4, 4, 0)                                                      \
+    X(33, 256, 256, false, 1, 64, 4, 4, 4, 0)                                                       \
+    X(34, 256, 256, false, 1, 64, 4, 4, 4, 1)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp)                                                      \

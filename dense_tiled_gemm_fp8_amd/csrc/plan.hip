@@ -43,6 +43,7 @@ constexpr double kPeakBf16PerCu = 2516.6e12 / 256.0;   /* dense MFMA, 2.4 GHz */
 constexpr double kPeakFp8PerCu = 5033.2e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
 constexpr double kExtraPassSec = 4.0e-6;              /* a combine or repack launch */
+constexpr double kCopyBytesPerSecPerCu = 60.0e9;      /* L2 -> LDS copies per compute unit */
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -168,8 +169,11 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
     const double bytes = (double)batch * ((double)(M + N) * K * esize + (double)M * N * out_esize) +
                          2.0 * partial;
     const double spread = busiest_cu ? (double)total / ((double)S * busiest_cu) : 1.0;
-    const double t_mem = bytes / (kHbmBytesPerSec * spread);
-    c.t = std::max(t_mfma, t_mem) + (partial > 0 ? kExtraPassSec : 0.0) +
+    const double t_mem = bytes / (kHbmBytesPerSec * cfg.stream_eff * spread);
+    /* the busiest unit's copies from L2 into LDS (operand panels shared by
+     * several tiles are fetched once per tile) */
+    const double t_copy = (double)busiest_cu * (cfg.TM + cfg.TN) * cfg.row_bytes / kCopyBytesPerSecPerCu;
+    c.t = std::max(std::max(t_mfma, t_mem), t_copy) + (partial > 0 ? kExtraPassSec : 0.0) +
           pack_passes * kExtraPassSec;
 }
 
@@ -251,6 +255,7 @@ gemm355_status check_pointers(const gemm355_args &a)
     if (K > 0 && (((uintptr_t)a.A % esize) != 0 || ((uintptr_t)a.B % esize) != 0))
         return GEMM355_EALIGN;
     if (((uintptr_t)a.scale_a & 3u) != 0 || ((uintptr_t)a.scale_b & 3u) != 0) return GEMM355_EALIGN;
+    if (((uintptr_t)a.unit_stamps & 7u) != 0) return GEMM355_EALIGN;
     if (K == 0) return GEMM355_OK;
     /* C must not overlap A or B (byte ranges spanned by all batch entries) */
     const uintptr_t c_lo = (uintptr_t)a.C;

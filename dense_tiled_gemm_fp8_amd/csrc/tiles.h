@@ -34,6 +34,9 @@ struct TileCfg {
     /* planning prior: fraction of a compute unit's dense MFMA peak the tile
      * sustains with 1, 2, 3, 4 of its workgroups resident on the unit */
     float mfma_eff[4];
+    /* planning prior: fraction of the sustained HBM rate the tile reaches
+     * when the product is bound by memory (measured on the long-K shapes) */
+    float stream_eff;
 };
 
 /* gfx950 compute-unit resources used by the occupancy arithmetic. */
@@ -46,44 +49,48 @@ constexpr int32_t kMaxWavesPerSimd = 8;
 
 constexpr TileCfg kTiles[] = {
     /* bf16, 128-byte K-tiles, 2 stages */
-    {0, 256, 256, 64, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
-    {0, 128, 128, 64, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
-    {0, 64, 64, 64, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {0, 64, 64, 64, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.60f},
     /* E4M3, 128-byte K-tiles, 2 stages */
-    {1, 256, 256, 128, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
-    {1, 128, 128, 128, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}},
-    {1, 64, 64, 128, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}},
+    {1, 256, 256, 128, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
+    {1, 128, 128, 128, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {1, 64, 64, 128, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.60f},
     /* 256 x 256 with 64-byte K-tiles and a deeper ring */
-    {0, 256, 256, 32, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {0, 256, 256, 32, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
-    {1, 256, 256, 64, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {1, 256, 256, 64, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}},
+    {0, 256, 256, 32, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
     /* 256 x 256 with 8 wavefronts (2 x 4, two per SIMD) */
-    {0, 256, 256, 64, 128, 2, 2, 4, 0, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}},
-    {0, 256, 256, 32, 64, 4, 2, 4, 0, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
-    {1, 256, 256, 128, 128, 2, 2, 4, 0, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}},
-    {1, 256, 256, 64, 64, 4, 2, 4, 0, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 0, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}, 0.80f},
+    {1, 256, 256, 128, 128, 2, 2, 4, 0, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 4, 0, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}, 0.80f},
     /* small tiles with deep rings for streaming (small M, N, long K) */
-    {0, 64, 64, 64, 128, 8, 2, 2, 0, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}},
-    {0, 64, 64, 64, 128, 4, 2, 2, 0, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}},
-    {0, 128, 128, 64, 128, 4, 2, 2, 0, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}},
-    {1, 64, 64, 128, 128, 8, 2, 2, 0, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}},
-    {1, 64, 64, 128, 128, 4, 2, 2, 0, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}},
-    {1, 128, 128, 128, 128, 4, 2, 2, 0, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}},
+    {0, 64, 64, 64, 128, 8, 2, 2, 0, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}, 0.72f},
+    {0, 64, 64, 64, 128, 4, 2, 2, 0, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}, 0.75f},
+    {0, 128, 128, 64, 128, 4, 2, 2, 0, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f},
+    {1, 64, 64, 128, 128, 8, 2, 2, 0, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}, 0.72f},
+    {1, 64, 64, 128, 128, 4, 2, 2, 0, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}, 0.75f},
+    {1, 128, 128, 128, 128, 4, 2, 2, 0, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f},
     /* 64 x 64 with one wavefront (four MFMA blocks per K-step) */
-    {0, 64, 64, 64, 128, 2, 1, 1, 0, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}},
-    {0, 64, 64, 64, 128, 4, 1, 1, 0, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}},
-    {1, 64, 64, 128, 128, 2, 1, 1, 0, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}},
-    {1, 64, 64, 128, 128, 4, 1, 1, 0, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}},
+    {0, 64, 64, 64, 128, 2, 1, 1, 0, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}, 0.50f},
+    {0, 64, 64, 64, 128, 4, 1, 1, 0, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}, 0.50f},
+    {1, 64, 64, 128, 128, 2, 1, 1, 0, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}, 0.50f},
+    {1, 64, 64, 128, 128, 4, 1, 1, 0, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}, 0.50f},
     /* 256 x 256, 64-byte K-tiles, copies spread over the K-steps */
-    {0, 256, 256, 32, 64, 4, 2, 2, 1, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {0, 256, 256, 32, 64, 5, 2, 2, 1, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {0, 256, 256, 32, 64, 4, 2, 4, 1, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {0, 256, 256, 32, 64, 5, 2, 4, 1, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {1, 256, 256, 64, 64, 4, 2, 2, 1, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {1, 256, 256, 64, 64, 5, 2, 2, 1, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {1, 256, 256, 64, 64, 4, 2, 4, 1, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}},
-    {1, 256, 256, 64, 64, 5, 2, 4, 1, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}},
+    {0, 256, 256, 32, 64, 4, 2, 2, 1, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 1, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 1, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 4, 1, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 2, 1, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 5, 2, 2, 1, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 4, 1, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 5, 2, 4, 1, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    /* 256 x 256 with 16 wavefronts (4 x 4, four per SIMD, 64 x 64 each) */
+    {0, 256, 256, 64, 128, 2, 4, 4, 0, 2 * (256 + 256) * 128, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 4, 4, 0, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 4, 4, 1, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

@@ -42,6 +42,7 @@ class gemm355_args(ctypes.Structure):
         ("dtype", ctypes.c_int), ("layout", ctypes.c_int),
         ("split_k", _i32), ("persistent", _i32), ("tile", _i32), ("cus", _i32),
         ("workspace", _vp), ("workspace_bytes", _sz),
+        ("unit_stamps", _vp),
     ]
 
 
@@ -133,7 +134,7 @@ def gemm355_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, layout=A_ROW_B_COL, spl
 def make_args(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, dtype=BF16_F32,
               layout=A_ROW_B_COL, batch=1, stride_a=0, stride_b=0, stride_c=0, scale_a=None,
               scale_b=None, split_k=0, persistent=-1, tile=-1, cus=0, workspace=None,
-              workspace_bytes=0) -> gemm355_args:
+              workspace_bytes=0, unit_stamps=None) -> gemm355_args:
     """Fill a gemm355_args; leading dimensions default to the packed ones."""
     a_row = layout in (A_ROW_B_COL, A_ROW_B_ROW)
     b_col = layout in (A_ROW_B_COL, A_COL_B_COL)
@@ -145,7 +146,7 @@ def make_args(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, dty
         ldc = max(1, N)
     return gemm355_args(M, N, K, _ptr(A), lda, stride_a, _ptr(B), ldb, stride_b, _ptr(C), ldc,
                         stride_c, batch, _ptr(scale_a), _ptr(scale_b), dtype, layout, split_k,
-                        persistent, tile, cus, _ptr(workspace), workspace_bytes)
+                        persistent, tile, cus, _ptr(workspace), workspace_bytes, _ptr(unit_stamps))
 
 
 def gemm355_gemm_ex(args: gemm355_args, stream=None) -> None:

@@ -213,6 +213,7 @@ def test_argument_errors(g):
     assert status(A=None) == g.EINVAL
     assert status(C=None) == g.EINVAL
     assert status(A=0x10001) == g.EALIGN
+    assert status(unit_stamps=0x300000000004) == g.EALIGN  # stamps need 8-byte alignment
     assert status(C=0x200000000002) == g.EALIGN            # fp32 C
     assert status(scale_a=0x3001) == g.EALIGN
     assert status(dtype=7) == g.EINVAL
@@ -264,3 +265,27 @@ def test_main_loop_uses_mfma(g, tmp_path):
         want = "v_mfma_f32_32x32x64_f8f6f4" if fp8 else "v_mfma_f32_32x32x16_bf16"
         assert want in body, name
         assert "v_fma_f32" not in body.split("s_endpgm")[0] or want in body
+
+
+def test_struct_layout_matches_header(g, tmp_path):
+    """The binding's ctypes structures have the header's layout: a C
+    program built from include/gemm355.h prints sizeof and every field's
+    offsetof, which must equal ctypes' view."""
+    import ctypes
+    import subprocess
+    hdr = os.path.join(ROOT, "include")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gemm355.h"', "int main(void) {"]
+    for cls, cname in ((g.gemm355_args, "gemm355_args"), (g.gemm355_plan_t, "gemm355_plan_t")):
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
+        for name, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, name, cname, name))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", hdr, str(src), "-o", str(exe)])
+    out = dict(l.rsplit(" ", 1) for l in subprocess.check_output([str(exe)]).decode().split("\n") if l)
+    for cls, cname in ((g.gemm355_args, "gemm355_args"), (g.gemm355_plan_t, "gemm355_plan_t")):
+        assert int(out[cname]) == ctypes.sizeof(cls), cname
+        for name, _ in cls._fields_:
+            assert int(out["%s.%s" % (cname, name)]) == getattr(cls, name).offset, (cname, name)

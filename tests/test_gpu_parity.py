@@ -301,3 +301,35 @@ def test_workload_e4m3_batch64():
     ops = inputs.workload_operands(w)
     assert ops.batch == 64 and len(set(ops.scale_a)) > 1
     _sampled(ops, "f32", n=400, batch_entries=(0, 1, 31, 63), what="e4m3 batch 64x(512,1024,4096)")
+
+
+def test_unit_stamps_cover_every_unit():
+    """The per-unit clock hook: every unit of a persistent split schedule
+    records start <= end, the product is unchanged by recording, and the
+    busy fraction the stamps give lies in (0, 1]."""
+    M, N, K = 1500, 1300, 2048
+    ops = ops_from(M, N, K, "bf16", 37, dist="normal")
+    A, B = H.dev(ops.A), H.dev(ops.B)
+    C0 = H.empty_c(1, M, N, "f32")
+    C1 = H.empty_c(1, M, N, "f32")
+    for tile, split, pers in ((1, 3, 1), (0, 1, 0), (2, 1, 1)):
+        args = g.make_args(M, N, K, A=A, B=B, C=C0, dtype=g.BF16_F32, tile=tile, split_k=split,
+                           persistent=pers)
+        p = g.gemm355_plan(args)
+        H.say("stamps tile", tile, "split", split, "persistent", pers, "units", p["units"], "grid", p["grid"])
+        g.gemm355_gemm_ex(args)
+        stamps = torch.zeros(2 * p["units"], dtype=torch.int64, device="cuda")
+        args2 = g.make_args(M, N, K, A=A, B=B, C=C1, dtype=g.BF16_F32, tile=tile, split_k=split,
+                            persistent=pers, unit_stamps=stamps)
+        g.gemm355_gemm_ex(args2)
+        torch.cuda.synchronize()
+        assert torch.equal(C0, C1)
+        st = stamps.view(-1, 2).cpu().numpy()
+        assert (st[:, 0] > 0).all() and (st[:, 1] >= st[:, 0]).all()
+        busy = float((st[:, 1] - st[:, 0]).sum())
+        span = float(st[:, 1].max() - st[:, 0].min())
+        eta = busy / (p["S"] * p["b"] * span)
+        H.say("  measured busy fraction", eta)
+        assert 0.0 < eta <= 1.0
+    C_ref, W = H.oracle_full(ops)
+    H.check(C1.float().cpu().numpy().astype(np.float64), C_ref, W, "bf16", "stamps")
