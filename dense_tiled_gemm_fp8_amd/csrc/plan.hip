@@ -42,7 +42,7 @@ constexpr int32_t kMaxNK = 1 << 23;
 constexpr double kPeakBf16PerCu = 2516.6e12 / 256.0;   /* dense MFMA, 2.4 GHz */
 constexpr double kPeakFp8PerCu = 5033.2e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
-constexpr double kExtraPassSec = 4.0e-6;              /* a combine or repack launch */
+constexpr double kExtraPassSec = 4.0e-6;              /* one launch: main, combine or repack */
 constexpr double kCopyBytesPerSecPerCu = 60.0e9;      /* L2 -> LDS copies per compute unit */
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -173,21 +173,26 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
     /* the busiest unit's copies from L2 into LDS (operand panels shared by
      * several tiles are fetched once per tile) */
     const double t_copy = (double)busiest_cu * (cfg.TM + cfg.TN) * cfg.row_bytes / kCopyBytesPerSecPerCu;
-    c.t = std::max(std::max(t_mfma, t_mem), t_copy) + (partial > 0 ? kExtraPassSec : 0.0) +
+    c.t = kExtraPassSec + std::max(std::max(t_mfma, t_mem), t_copy) + (partial > 0 ? kExtraPassSec : 0.0) +
           pack_passes * kExtraPassSec;
 }
 
-/* true if x should be preferred over y */
+/* true if x should be preferred over y.  Modelled times within 20 % of each
+ * other count as equal (the model is coarser than that: on small products
+ * launch costs it only estimates dominate); among those the schedule that
+ * fills the device best (eta_sched * eta_pad) wins. */
 bool better(const Cand &x, const Cand &y)
 {
     if (y.tile < 0) return true;
-    if (x.t != y.t) return x.t < y.t;
+    const bool close = x.t <= y.t * 1.2 && y.t <= x.t * 1.2;
+    if (!close) return x.t < y.t;
     const Frac ex = reduce((unsigned __int128)x.eta_sched.num * x.eta_pad.num,
                            (unsigned __int128)x.eta_sched.den * x.eta_pad.den);
     const Frac ey = reduce((unsigned __int128)y.eta_sched.num * y.eta_pad.num,
                            (unsigned __int128)y.eta_sched.den * y.eta_pad.den);
     if (frac_less(ey, ex)) return true;
     if (frac_less(ex, ey)) return false;
+    if (x.t != y.t) return x.t < y.t;
     if (x.units != y.units) return x.units < y.units;
     if (kTiles[x.tile].TM != kTiles[y.tile].TM) return kTiles[x.tile].TM > kTiles[y.tile].TM;
     return kTiles[x.tile].TN > kTiles[y.tile].TN;
@@ -416,6 +421,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     const TileCfg &cfg = kTiles[best.tile];
     gemm355_plan_t &o = P.pub;
     o.tile = best.tile;
+    o.model_seconds = best.t;
     o.T_M = cfg.TM;
     o.T_N = cfg.TN;
     o.T_K = cfg.TK;

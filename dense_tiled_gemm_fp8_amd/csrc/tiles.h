@@ -51,11 +51,11 @@ constexpr TileCfg kTiles[] = {
     /* bf16, 128-byte K-tiles, 2 stages */
     {0, 256, 256, 64, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
     {0, 128, 128, 64, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
-    {0, 64, 64, 64, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.60f},
+    {0, 64, 64, 64, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f},
     /* E4M3, 128-byte K-tiles, 2 stages */
     {1, 256, 256, 128, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
     {1, 128, 128, 128, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
-    {1, 64, 64, 128, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.60f},
+    {1, 64, 64, 128, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f},
     /* 256 x 256 with 64-byte K-tiles and a deeper ring */
     {0, 256, 256, 32, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
     {0, 256, 256, 32, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},

@@ -59,6 +59,7 @@ class gemm355_plan_t(ctypes.Structure):
         ("eta_pad_num", _i64), ("eta_pad_den", _i64),
         ("eta_sched_num", _i64), ("eta_sched_den", _i64),
         ("workspace_bytes", _sz),
+        ("model_seconds", ctypes.c_double),
     ]
 
 

@@ -133,6 +133,8 @@ typedef struct gemm355_plan_t {
     int64_t eta_sched_num, eta_sched_den;  /* sum of unit work over S*b
                                               times the busiest workgroup's */
     size_t workspace_bytes;       /* scratch this call needs               */
+    double model_seconds;         /* the planner's time estimate (planning
+                                     model only, not a measurement)        */
 } gemm355_plan_t;
 
 /*

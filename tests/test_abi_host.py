@@ -178,6 +178,15 @@ def test_plan_reports_efficiency_levers(g):
                     dtype=g.BF16_BF16, cus=256)
     p = g.gemm355_plan(a)
     assert (p["T_M"], p["T_N"], p["G"], p["eta_wave_num"], p["eta_wave_den"]) == (256, 256, 256, 1, 1)
+    # every named shape except the single-tile-grid 256^3 call fills the device
+    # to eta_sched >= 0.95 (the tail and long-K shapes through the levers above)
+    shapes = [(4000, 4000, 4000, 1, g.BF16_F32), (1000, 3000, 777, 1, g.BF16_F32),
+              (8192, 8192, 8192, 1, g.E4M3_F32), (512, 1024, 4096, 64, g.E4M3_F32)]
+    for (M, N, K, batch, dt) in shapes:
+        a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, dtype=dt, batch=batch,
+                        stride_a=M * K, stride_b=N * K, stride_c=M * N, cus=256)
+        p = g.gemm355_plan(a)
+        assert Fraction(p["eta_sched_num"], p["eta_sched_den"]) >= Fraction(95, 100), (M, N, K)
 
 
 def test_repack_decisions(g):
