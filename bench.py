@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--profile", default=None, metavar="NAME[:INDEX]",
                     help="only run warmup + steps calls of this workload shape (for counter "
                          "collection under rocprofv3) and print its time")
+    ap.add_argument("--tile", type=int, default=-1,
+                    help="with --profile: force this tile-table entry instead of the planner's")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -78,7 +80,7 @@ class Case:
     """Device-resident operands of one workload shape (with rotation copies
     for HBM-bound shapes) and a callable that runs one step."""
 
-    def __init__(self, w, si, torch, g, inputs):
+    def __init__(self, w, si, torch, g, inputs, tile=-1):
         self.w, self.si = w, si
         ops = inputs.workload_operands(w, si)
         self.ops = ops
@@ -111,7 +113,7 @@ class Case:
         for i in range(self.copies):
             a = g.make_args(self.M, self.N, self.K, A=self.As[i], B=self.Bs[i], C=self.C, dtype=dt,
                             batch=self.batch, stride_a=self.M * self.K, stride_b=self.N * self.K,
-                            stride_c=self.M * self.N, scale_a=self.sa, scale_b=self.sb)
+                            stride_c=self.M * self.N, scale_a=self.sa, scale_b=self.sb, tile=tile)
             self.args.append(a)
         self.plan = g.gemm355_plan(self.args[0])
         if self.plan["workspace_bytes"]:
@@ -225,7 +227,7 @@ def main():
     if args.profile:
         name, _, si = args.profile.partition(":")
         w = next(x for x in inputs.WORKLOADS if x.name == name)
-        c = Case(w, int(si or 0), torch, g, inputs)
+        c = Case(w, int(si or 0), torch, g, inputs, tile=args.tile)
         _, ev = time_case(c, torch, args.steps, args.warmup)
         print(json.dumps({"workload": c.name(), "us_per_call": round(ev / args.steps * 1e6, 2),
                           "tile": c.plan["tile"], "split": c.plan["split"],

@@ -119,6 +119,9 @@ template <int V> using IC = std::integral_constant<int, V>;
 
 template <bool FP8> struct FragType { typedef bf16x8 type; };
 template <> struct FragType<true> { typedef i32x8 type; };
+/* accumulator of one MI x MI MFMA block: MI * MI / 64 fp32 per lane */
+template <int MI> struct AccType { typedef f32x16 type; };
+template <> struct AccType<16> { typedef f32x4 type; };
 
 __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
 {
@@ -155,19 +158,26 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * issued into the stage just freed, and the last step's MFMAs overlap the
  * reads of the next tile's first fragments.
  */
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
     constexpr int NW = WGM * WGN, WN = WGN;
     constexpr int WTM = TM / WGM, WTN = TN / WGN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int FM = WTM / MI, FN = WTN / MI;
     constexpr int CPR = RB / 16, RPL = 256 / RB, ROWS_PER_DMA = 1024 / RB;
     constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB, STAGE_BYTES = A_BYTES + B_BYTES;
     constexpr int A_LOADS = TM / ROWS_PER_DMA / NW, B_LOADS = TN / ROWS_PER_DMA / NW;
     constexpr int LOADS = A_LOADS + B_LOADS;
-    /* MFMA K-steps per K-tile: bf16 steps are 16 deep (32 bytes), E4M3 64 */
-    constexpr int KSTEPS = FP8 ? RB / 64 : RB / 32;
+    /* bytes of K per MFMA step: 32 x 32 blocks take 16 bf16 or 64 E4M3
+     * values, 16 x 16 blocks 32 bf16 or 128 E4M3; CPS 16-byte chunks */
+    constexpr int KB_STEP = (FP8 ? 64 : 32) * (MI == 32 ? 1 : 2);
+    constexpr int CPS = KB_STEP / 16;
+    constexpr int KSTEPS = RB / KB_STEP;
+    constexpr int ACC_N = MI * MI / 64;
     using Frag = typename FragType<FP8>::type;
+    using Acc = typename AccType<MI>::type;
+    static_assert(MI == 32 || MI == 16, "MFMA block");
+    static_assert(RB % KB_STEP == 0, "K-tile holds whole MFMA steps");
     static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1 && KSTEPS >= 1, "tile");
     static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "ring depth");
     static_assert(!SPREAD || STAGES >= 3, "spread copies need a third stage");
@@ -188,7 +198,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     int lchunk[2];
     lchunk[0] = (lane % CPR) ^ ((4 * wave + drow / RPL) % CPR);
     lchunk[1] = (lane % CPR) ^ ((4 * (NW + wave) + drow / RPL) % CPR);
-    const int frow = lane & 31, hi = lane >> 5, sw = (frow / RPL) % CPR;
+    /* fragment lanes: lane l reads row l % MI of the block and K-chunk
+     * group l / MI of the step */
+    const int frow = lane % MI, hi = lane / MI, sw = (frow / RPL) % CPR;
     const uint32_t smem_base = lds_addr(smem);
 
     int32_t first = blockIdx.x;
@@ -253,22 +265,22 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         /* Fragment of MFMA K-step ks for block blk of this wave, from the
          * operand rows starting at `rows` (A or B part of a stage). */
         auto frag = [&](const uint8_t *rows, int ks, int blk) __attribute__((always_inline)) -> Frag {
-            const uint8_t *row = rows + (blk * 32 + frow) * RB;
+            const uint8_t *row = rows + (blk * MI + frow) * RB;
             if constexpr (!FP8) {
-                return *(const bf16x8 *)(row + (((2 * ks + hi) ^ sw) * 16));
+                return *(const bf16x8 *)(row + (((CPS * ks + hi) ^ sw) * 16));
             } else {
-                const i32x4 lo = *(const i32x4 *)(row + (((4 * ks + 2 * hi) ^ sw) * 16));
-                const i32x4 up = *(const i32x4 *)(row + (((4 * ks + 2 * hi + 1) ^ sw) * 16));
+                const i32x4 lo = *(const i32x4 *)(row + (((CPS * ks + 2 * hi) ^ sw) * 16));
+                const i32x4 up = *(const i32x4 *)(row + (((CPS * ks + 2 * hi + 1) ^ sw) * 16));
                 return i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
             }
         };
 
-        f32x16 acc[FM][FN];
+        Acc acc[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = f32x16{};
+                acc[i][j] = Acc{};
 
         /* Fragments double-buffered by K-step parity. */
         Frag fa[2][FM], fb[2][FN];
@@ -292,11 +304,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                 constexpr int t = decltype(tc)::value;
                 if constexpr (t < NM) {
                     constexpr int i = t / FN, j = t % FN;
-                    if constexpr (!FP8)
+                    if constexpr (!FP8 && MI == 32)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
-                    else /* format fields 0/0: both operands E4M3; zero scales
-                          * select the unscaled instruction */
+                    else if constexpr (!FP8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                    /* format fields 0/0: both operands E4M3; zero scales
+                     * select the unscaled instruction */
+                    else if constexpr (MI == 32)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0, 0, 0, 0);
                 }
                 if constexpr (t < FM)
@@ -399,7 +417,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         }
 
         /* Epilogue.  Accumulator layout of a 32 x 32 MFMA block: lane l holds
-         * column l % 32, register 4 g + r holds row 8 g + 4 (l / 32) + r.
+         * column l % 32, register 4 g + r holds row 8 g + 4 (l / 32) + r; of a
+         * 16 x 16 block: lane l holds column l % 16, register r holds row
+         * 4 (l / 16) + r.
          * Stores go through a buffer resource based at the tile's corner: the
          * lane's column and row group in the VGPR offset, the register's row
          * in the scalar offset; elements outside M x N get VGPR offset kOOB
@@ -408,7 +428,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
          * and hold them in registers across it. */
         int lv = threadIdx.x;
         asm volatile("" : "+v"(lv));
-        const int el = lv & 63, ecol = el & 31, ehi = el >> 5;
+        const int el = lv & 63, ecol = el % MI, ehi = el / MI;
+        /* row of accumulator register e relative to the lane's first row */
+        auto erow = [](int e) __attribute__((always_inline)) { return MI == 32 ? (e >> 2) * 8 + (e & 3) : e; };
         if (un.slot >= 0) {
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (int64_t)un.slot * (TM * TN));
 #pragma unroll
@@ -416,15 +438,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const uint32_t voff =
-                        (uint32_t)(((wm * WTM + i * 32 + ehi * 4) * TN + wn * WTN + j * 32 + ecol) * 4);
+                        (uint32_t)(((wm * WTM + i * MI + ehi * 4) * TN + wn * WTN + j * MI + ecol) * 4);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
+                    for (int e = 0; e < ACC_N; ++e) {
                         /* copy the element out first: a bit_cast applied to
                          * a vector subscript directly was lowered to element
                          * 0 for every e */
                         const float v = acc[i][j][e];
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, voff,
-                                                              ((e >> 2) * 8 + (e & 3)) * TN * 4, 0);
+                                                              erow(e) * TN * 4, 0);
                     }
                     /* one block at a time keeps the epilogue's registers few */
                     __builtin_amdgcn_sched_barrier(0);
@@ -440,12 +462,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const int col = wn * WTN + j * 32 + ecol;
-                        const int row0 = wm * WTM + i * 32 + ehi * 4;
+                        const int col = wn * WTN + j * MI + ecol;
+                        const int row0 = wm * WTM + i * MI + ehi * 4;
                         const uint32_t voff = (uint32_t)(row0 * ldcb + col * 2);
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int dr = (e >> 2) * 8 + (e & 3);
+                        for (int e = 0; e < ACC_N; ++e) {
+                            const int dr = erow(e);
                             const bool ok = (row0 + dr < mrem) && (col < nrem);
                             const float v = alpha * acc[i][j][e];
                             __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc,
@@ -461,12 +483,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const int col = wn * WTN + j * 32 + ecol;
-                        const int row0 = wm * WTM + i * 32 + ehi * 4;
+                        const int col = wn * WTN + j * MI + ecol;
+                        const int row0 = wm * WTM + i * MI + ehi * 4;
                         const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int dr = (e >> 2) * 8 + (e & 3);
+                        for (int e = 0; e < ACC_N; ++e) {
+                            const int dr = erow(e);
                             const bool ok = (row0 + dr < mrem) && (col < nrem);
                             const float v = alpha * acc[i][j][e];
                             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc,
@@ -618,73 +640,80 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
 static hipError_t launch_tile(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD>), dim3(p.s.grid),
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI>), dim3(p.s.grid),
                        dim3(WGM * WGN * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 /* Instantiations, in tile-table order (csrc/tiles.h):
  * id, TM, TN, E4M3, groups per CU, K-tile bytes, stages, waves along M, N,
- * copies spread over the K-steps */
+ * copies spread over the K-steps, MFMA block edge */
 #define GEMM355_TILES(X)                                                                          \
-    X(0, 256, 256, false, 1, 128, 2, 2, 2, 0)                                                       \
-    X(1, 128, 128, false, 2, 128, 2, 2, 2, 0)                                                       \
-    X(2, 64, 64, false, 4, 128, 2, 2, 2, 0)                                                         \
-    X(3, 256, 256, true, 1, 128, 2, 2, 2, 0)                                                        \
-    X(4, 128, 128, true, 2, 128, 2, 2, 2, 0)                                                        \
-    X(5, 64, 64, true, 4, 128, 2, 2, 2, 0)                                                          \
-    X(6, 256, 256, false, 1, 64, 4, 2, 2, 0)                                                        \
-    X(7, 256, 256, false, 1, 64, 5, 2, 2, 0)                                                        \
-    X(8, 256, 256, true, 1, 64, 4, 2, 2, 0)                                                         \
-    X(9, 256, 256, true, 1, 64, 5, 2, 2, 0)                                                         \
-    X(10, 256, 256, false, 1, 128, 2, 2, 4, 0)                                                      \
-    X(11, 256, 256, false, 1, 64, 4, 2, 4, 0)                                                       \
-    X(12, 256, 256, true, 1, 128, 2, 2, 4, 0)                                                       \
-    X(13, 256, 256, true, 1, 64, 4, 2, 4, 0)                                                        \
-    X(14, 64, 64, false, 1, 128, 8, 2, 2, 0)                                                        \
-    X(15, 64, 64, false, 2, 128, 4, 2, 2, 0)                                                        \
-    X(16, 128, 128, false, 1, 128, 4, 2, 2, 0)                                                      \
-    X(17, 64, 64, true, 1, 128, 8, 2, 2, 0)                                                         \
-    X(18, 64, 64, true, 2, 128, 4, 2, 2, 0)                                                         \
-    X(19, 128, 128, true, 1, 128, 4, 2, 2, 0)                                                       \
-    X(20, 64, 64, false, 4, 128, 2, 1, 1, 0)                                                        \
-    X(21, 64, 64, false, 2, 128, 4, 1, 1, 0)                                                        \
-    X(22, 64, 64, true, 4, 128, 2, 1, 1, 0)                                                         \
-    X(23, 64, 64, true, 2, 128, 4, 1, 1, 0)                                                         \
-    X(24, 256, 256, false, 1, 64, 4, 2, 2, 1)                                                       \
-    X(25, 256, 256, false, 1, 64, 5, 2, 2, 1)                                                       \
-    X(26, 256, 256, false, 1, 64, 4, 2, 4, 1)                                                       \
-    X(27, 256, 256, false, 1, 64, 5, 2, 4, 1)                                                       \
-    X(28, 256, 256, true, 1, 64, 4, 2, 2, 1)                                                        \
-    X(29, 256, 256, true, 1, 64, 5, 2, 2, 1)                                                        \
-    X(30, 256, 256, true, 1, 64, 4, 2, 4, 1)                                                        \
-    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1)                                                        \
-    X(32, 256, 256, false, 1, 128, 2, 4, 4, 0)                                                      \
-    X(33, 256, 256, false, 1, 64, 4, 4, 4, 0)                                                       \
-    X(34, 256, 256, false, 1, 64, 4, 4, 4, 1)
+    X(0, 256, 256, false, 1, 128, 2, 2, 2, 0, 32)                                                       \
+    X(1, 128, 128, false, 2, 128, 2, 2, 2, 0, 32)                                                       \
+    X(2, 64, 64, false, 4, 128, 2, 2, 2, 0, 32)                                                         \
+    X(3, 256, 256, true, 1, 128, 2, 2, 2, 0, 32)                                                        \
+    X(4, 128, 128, true, 2, 128, 2, 2, 2, 0, 32)                                                        \
+    X(5, 64, 64, true, 4, 128, 2, 2, 2, 0, 32)                                                          \
+    X(6, 256, 256, false, 1, 64, 4, 2, 2, 0, 32)                                                        \
+    X(7, 256, 256, false, 1, 64, 5, 2, 2, 0, 32)                                                        \
+    X(8, 256, 256, true, 1, 64, 4, 2, 2, 0, 32)                                                         \
+    X(9, 256, 256, true, 1, 64, 5, 2, 2, 0, 32)                                                         \
+    X(10, 256, 256, false, 1, 128, 2, 2, 4, 0, 32)                                                      \
+    X(11, 256, 256, false, 1, 64, 4, 2, 4, 0, 32)                                                       \
+    X(12, 256, 256, true, 1, 128, 2, 2, 4, 0, 32)                                                       \
+    X(13, 256, 256, true, 1, 64, 4, 2, 4, 0, 32)                                                        \
+    X(14, 64, 64, false, 1, 128, 8, 2, 2, 0, 32)                                                        \
+    X(15, 64, 64, false, 2, 128, 4, 2, 2, 0, 32)                                                        \
+    X(16, 128, 128, false, 1, 128, 4, 2, 2, 0, 32)                                                      \
+    X(17, 64, 64, true, 1, 128, 8, 2, 2, 0, 32)                                                         \
+    X(18, 64, 64, true, 2, 128, 4, 2, 2, 0, 32)                                                         \
+    X(19, 128, 128, true, 1, 128, 4, 2, 2, 0, 32)                                                       \
+    X(20, 64, 64, false, 4, 128, 2, 1, 1, 0, 32)                                                        \
+    X(21, 64, 64, false, 2, 128, 4, 1, 1, 0, 32)                                                        \
+    X(22, 64, 64, true, 4, 128, 2, 1, 1, 0, 32)                                                         \
+    X(23, 64, 64, true, 2, 128, 4, 1, 1, 0, 32)                                                         \
+    X(24, 256, 256, false, 1, 64, 4, 2, 2, 1, 32)                                                       \
+    X(25, 256, 256, false, 1, 64, 5, 2, 2, 1, 32)                                                       \
+    X(26, 256, 256, false, 1, 64, 4, 2, 4, 1, 32)                                                       \
+    X(27, 256, 256, false, 1, 64, 5, 2, 4, 1, 32)                                                       \
+    X(28, 256, 256, true, 1, 64, 4, 2, 2, 1, 32)                                                        \
+    X(29, 256, 256, true, 1, 64, 5, 2, 2, 1, 32)                                                        \
+    X(30, 256, 256, true, 1, 64, 4, 2, 4, 1, 32)                                                        \
+    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1, 32)                                                        \
+    X(32, 256, 256, false, 1, 128, 2, 4, 4, 0, 32)                                                      \
+    X(33, 256, 256, false, 1, 64, 4, 4, 4, 0, 32)                                                       \
+    X(34, 256, 256, false, 1, 64, 4, 4, 4, 1, 32)                                                   \
+    X(35, 256, 256, false, 1, 128, 2, 2, 2, 0, 16)                                                  \
+    X(36, 256, 256, false, 1, 128, 2, 2, 4, 0, 16)                                                  \
+    X(37, 256, 256, false, 1, 64, 4, 2, 4, 0, 16)                                                   \
+    X(38, 256, 256, false, 1, 64, 4, 2, 2, 0, 16)                                                   \
+    X(39, 256, 256, false, 1, 64, 4, 2, 2, 1, 16)                                                   \
+    X(40, 256, 256, false, 1, 64, 5, 2, 2, 0, 16)
 
 /* every instantiation agrees with its tile-table entry */
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp)                                                      \
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi)                                                      \
     static_assert(kTiles[id].dtype_class == (f8 ? 1 : 0) && kTiles[id].TM == tm &&               \
                       kTiles[id].TN == tn && kTiles[id].min_blocks == mb &&                      \
                       kTiles[id].row_bytes == rb && kTiles[id].stages == st &&                   \
                       kTiles[id].waves_m == wm && kTiles[id].waves_n == wn &&                    \
-                      kTiles[id].TK == (f8 ? rb : rb / 2) && kTiles[id].spread == sp,            \
+                      kTiles[id].TK == (f8 ? rb : rb / 2) && kTiles[id].spread == sp &&          \
+                      kTiles[id].mfma == mi,                                                     \
                   "tile table entry " #id);
 GEMM355_TILES(X)
 #undef X
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp) +1
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) +1
 static_assert(0 GEMM355_TILES(X) == kNumTiles, "one instantiation per tile-table entry");
 #undef X
 
 hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp) \
-    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp>(p, stream);
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) \
+    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp, mi>(p, stream);
         GEMM355_TILES(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -694,8 +723,8 @@ hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
 const void *gemm_kernel_symbol(int32_t tile)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp) \
-    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp>;
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) \
+    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp, mi>;
         GEMM355_TILES(X)
 #undef X
     default: return nullptr;

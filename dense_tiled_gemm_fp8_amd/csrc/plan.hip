@@ -43,7 +43,7 @@ constexpr double kPeakBf16PerCu = 2516.6e12 / 256.0;   /* dense MFMA, 2.4 GHz */
 constexpr double kPeakFp8PerCu = 5033.2e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
 constexpr double kExtraPassSec = 4.0e-6;              /* one launch: main, combine or repack */
-constexpr double kCopyBytesPerSecPerCu = 60.0e9;      /* L2 -> LDS copies per compute unit */
+constexpr double kCopyBytesPerSecPerCu = 100.0e9;     /* L2 -> LDS copies per compute unit */
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -179,20 +179,27 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
 
 /* true if x should be preferred over y.  Modelled times within 20 % of each
  * other count as equal (the model is coarser than that: on small products
- * launch costs it only estimates dominate); among those the schedule that
- * fills the device best (eta_sched * eta_pad) wins. */
+ * launch costs it only estimates dominate); among those a schedule that
+ * fills the device more than 3 % better (eta_sched * eta_pad) wins, and
+ * otherwise the modelled time decides. */
 bool better(const Cand &x, const Cand &y)
 {
     if (y.tile < 0) return true;
     const bool close = x.t <= y.t * 1.2 && y.t <= x.t * 1.2;
     if (!close) return x.t < y.t;
-    const Frac ex = reduce((unsigned __int128)x.eta_sched.num * x.eta_pad.num,
-                           (unsigned __int128)x.eta_sched.den * x.eta_pad.den);
-    const Frac ey = reduce((unsigned __int128)y.eta_sched.num * y.eta_pad.num,
-                           (unsigned __int128)y.eta_sched.den * y.eta_pad.den);
-    if (frac_less(ey, ex)) return true;
-    if (frac_less(ex, ey)) return false;
+    const double ex = rational_to_double(x.eta_sched.num, x.eta_sched.den) *
+                      rational_to_double(x.eta_pad.num, x.eta_pad.den);
+    const double ey = rational_to_double(y.eta_sched.num, y.eta_sched.den) *
+                      rational_to_double(y.eta_pad.num, y.eta_pad.den);
+    if (ex > ey * 1.03) return true;
+    if (ey > ex * 1.03) return false;
     if (x.t != y.t) return x.t < y.t;
+    const Frac fx = reduce((unsigned __int128)x.eta_sched.num * x.eta_pad.num,
+                           (unsigned __int128)x.eta_sched.den * x.eta_pad.den);
+    const Frac fy = reduce((unsigned __int128)y.eta_sched.num * y.eta_pad.num,
+                           (unsigned __int128)y.eta_sched.den * y.eta_pad.den);
+    if (frac_less(fy, fx)) return true;
+    if (frac_less(fx, fy)) return false;
     if (x.units != y.units) return x.units < y.units;
     if (kTiles[x.tile].TM != kTiles[y.tile].TM) return kTiles[x.tile].TM > kTiles[y.tile].TM;
     return kTiles[x.tile].TN > kTiles[y.tile].TN;

@@ -27,6 +27,7 @@ struct TileCfg {
     int32_t waves_m, waves_n;
     int32_t spread;        /* 1: copies of a K-tile spread over the K-steps of
                               the tile before (ring of >= 3 stages)          */
+    int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
     int32_t lds_bytes;     /* stages * (TM + TN) * RB                        */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
     int32_t vgpr_budget;   /* 512 / (min_blocks * waves / 4): registers per
@@ -49,48 +50,55 @@ constexpr int32_t kMaxWavesPerSimd = 8;
 
 constexpr TileCfg kTiles[] = {
     /* bf16, 128-byte K-tiles, 2 stages */
-    {0, 256, 256, 64, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
-    {0, 128, 128, 64, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
-    {0, 64, 64, 64, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f},
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f},
     /* E4M3, 128-byte K-tiles, 2 stages */
-    {1, 256, 256, 128, 128, 2, 2, 2, 0, 2 * (256 + 256) * 128, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
-    {1, 128, 128, 128, 128, 2, 2, 2, 0, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
-    {1, 64, 64, 128, 128, 2, 2, 2, 0, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f},
+    {1, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.82f, 0.82f, 0.82f, 0.82f}, 0.80f},
+    {1, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {1, 64, 64, 128, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f},
     /* 256 x 256 with 64-byte K-tiles and a deeper ring */
-    {0, 256, 256, 32, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {0, 256, 256, 32, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
-    {1, 256, 256, 64, 64, 4, 2, 2, 0, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {1, 256, 256, 64, 64, 5, 2, 2, 0, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 0, 32, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 0, 32, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 2, 0, 32, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 5, 2, 2, 0, 32, 5 * (256 + 256) * 64, 1, 512, {0.74f, 0.74f, 0.74f, 0.74f}, 0.80f},
     /* 256 x 256 with 8 wavefronts (2 x 4, two per SIMD) */
-    {0, 256, 256, 64, 128, 2, 2, 4, 0, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
-    {0, 256, 256, 32, 64, 4, 2, 4, 0, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}, 0.80f},
-    {1, 256, 256, 128, 128, 2, 2, 4, 0, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
-    {1, 256, 256, 64, 64, 4, 2, 4, 0, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}, 0.80f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 32, 2 * (256 + 256) * 128, 1, 256, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 0, 32, 4 * (256 + 256) * 64, 1, 256, {0.72f, 0.72f, 0.72f, 0.72f}, 0.80f},
+    {1, 256, 256, 128, 128, 2, 2, 4, 0, 32, 2 * (256 + 256) * 128, 1, 256, {0.76f, 0.76f, 0.76f, 0.76f}, 0.75f},
+    {1, 256, 256, 64, 64, 4, 2, 4, 0, 32, 4 * (256 + 256) * 64, 1, 256, {0.79f, 0.79f, 0.79f, 0.79f}, 0.80f},
     /* small tiles with deep rings for streaming (small M, N, long K) */
-    {0, 64, 64, 64, 128, 8, 2, 2, 0, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}, 0.72f},
-    {0, 64, 64, 64, 128, 4, 2, 2, 0, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}, 0.75f},
-    {0, 128, 128, 64, 128, 4, 2, 2, 0, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f},
-    {1, 64, 64, 128, 128, 8, 2, 2, 0, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}, 0.72f},
-    {1, 64, 64, 128, 128, 4, 2, 2, 0, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}, 0.75f},
-    {1, 128, 128, 128, 128, 4, 2, 2, 0, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f},
+    {0, 64, 64, 64, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}, 0.72f},
+    {0, 64, 64, 64, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}, 0.75f},
+    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f},
+    {1, 64, 64, 128, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.15f, 0.15f, 0.15f, 0.15f}, 0.72f},
+    {1, 64, 64, 128, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.15f, 0.25f, 0.25f, 0.25f}, 0.75f},
+    {1, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
     /* 64 x 64 with one wavefront (four MFMA blocks per K-step) */
-    {0, 64, 64, 64, 128, 2, 1, 1, 0, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}, 0.50f},
-    {0, 64, 64, 64, 128, 4, 1, 1, 0, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}, 0.50f},
-    {1, 64, 64, 128, 128, 2, 1, 1, 0, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}, 0.50f},
-    {1, 64, 64, 128, 128, 4, 1, 1, 0, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}, 0.50f},
+    {0, 64, 64, 64, 128, 2, 1, 1, 0, 32, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}, 0.50f},
+    {0, 64, 64, 64, 128, 4, 1, 1, 0, 32, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}, 0.50f},
+    {1, 64, 64, 128, 128, 2, 1, 1, 0, 32, 2 * (64 + 64) * 128, 4, 512, {0.10f, 0.20f, 0.28f, 0.35f}, 0.50f},
+    {1, 64, 64, 128, 128, 4, 1, 1, 0, 32, 4 * (64 + 64) * 128, 2, 512, {0.10f, 0.20f, 0.20f, 0.20f}, 0.50f},
     /* 256 x 256, 64-byte K-tiles, copies spread over the K-steps */
-    {0, 256, 256, 32, 64, 4, 2, 2, 1, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {0, 256, 256, 32, 64, 5, 2, 2, 1, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {0, 256, 256, 32, 64, 4, 2, 4, 1, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {0, 256, 256, 32, 64, 5, 2, 4, 1, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {1, 256, 256, 64, 64, 4, 2, 2, 1, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {1, 256, 256, 64, 64, 5, 2, 2, 1, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {1, 256, 256, 64, 64, 4, 2, 4, 1, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {1, 256, 256, 64, 64, 5, 2, 4, 1, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 1, 32, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 1, 32, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 1, 32, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 4, 1, 32, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 2, 1, 32, 4 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 5, 2, 2, 1, 32, 5 * (256 + 256) * 64, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 4, 2, 4, 1, 32, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 256, 64, 64, 5, 2, 4, 1, 32, 5 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
     /* 256 x 256 with 16 wavefronts (4 x 4, four per SIMD, 64 x 64 each) */
-    {0, 256, 256, 64, 128, 2, 4, 4, 0, 2 * (256 + 256) * 128, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {0, 256, 256, 32, 64, 4, 4, 4, 0, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
-    {0, 256, 256, 32, 64, 4, 4, 4, 1, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 64, 128, 2, 4, 4, 0, 32, 2 * (256 + 256) * 128, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 4, 4, 0, 32, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 4, 4, 1, 32, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    /* 256 x 256 with 16 x 16 MFMA blocks */
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 16, 2 * (256 + 256) * 128, 1, 512, {0.86f, 0.86f, 0.86f, 0.86f}, 0.80f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.85f, 0.85f, 0.85f, 0.85f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 0, 16, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 0, 16, 4 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 1, 16, 4 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 0, 16, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

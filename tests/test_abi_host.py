@@ -271,7 +271,9 @@ def test_main_loop_uses_mfma(g, tmp_path):
     for body in kernels:
         name = body.split(":")[0]
         fp8 = "Lb1E" in name
-        want = "v_mfma_f32_32x32x64_f8f6f4" if fp8 else "v_mfma_f32_32x32x16_bf16"
+        mi = int(re.findall(r"ELi(\d+)E", name)[-1])      # last template argument: MFMA block edge
+        want = {(True, 32): "v_mfma_f32_32x32x64_f8f6f4", (False, 32): "v_mfma_f32_32x32x16_bf16",
+                (True, 16): "v_mfma_f32_16x16x128_f8f6f4", (False, 16): "v_mfma_f32_16x16x32_bf16"}[(fp8, mi)]
         assert want in body, name
         assert "v_fma_f32" not in body.split("s_endpgm")[0] or want in body
 
