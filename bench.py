@@ -60,6 +60,9 @@ def parse():
                          "collection under rocprofv3) and print its time")
     ap.add_argument("--tile", type=int, default=-1,
                     help="with --profile: force this tile-table entry instead of the planner's")
+    ap.add_argument("--stamps", action="store_true",
+                    help="with --profile: one more call with the per-unit clock hook; prints the "
+                         "measured eta, shader clock and MFMA cycle efficiency")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -125,12 +128,15 @@ class Case:
         self.i = 0
 
     def measured_eta(self, torch):
-        """One extra call with the per-unit clock hook: the summed busy time
-        of all units over (compute units x resident groups x makespan)."""
+        """One extra call with the per-unit clock hook.  Returns the summed
+        busy time of all units over (compute units x resident groups x
+        makespan), the shader clock over the units (MHz) and the MFMA
+        cycle efficiency inside units: the dense-MFMA cycles of the executed
+        (padded) tile work over the measured shader cycles."""
         p = self.plan
         if not p["units"]:
             return None
-        stamps = torch.zeros(2 * p["units"], dtype=torch.int64, device="cuda")
+        stamps = torch.zeros(4 * p["units"], dtype=torch.int64, device="cuda")
         a = self.args[0]
         a.unit_stamps = stamps.data_ptr()
         try:
@@ -138,11 +144,18 @@ class Case:
             torch.cuda.synchronize()
         finally:
             a.unit_stamps = None
-        st = stamps.view(-1, 2).cpu().numpy().astype("float64")
+        st = stamps.view(-1, 4).cpu().numpy().astype("float64")
         span = st[:, 1].max() - st[:, 0].min()
-        if span <= 0:
+        busy_rt = (st[:, 1] - st[:, 0]).sum()
+        cycles = (st[:, 3] - st[:, 2]).sum()
+        if span <= 0 or busy_rt <= 0 or cycles <= 0:
             return None
-        return float((st[:, 1] - st[:, 0]).sum() / (p["S"] * p["b"] * span))
+        # dense MFMA FLOPs per clock of one compute unit, shared by b groups
+        per_clk = (4096.0 if self.fmt == "bf16" else 8192.0) / p["b"]
+        ideal = 2.0 * p["T_M"] * p["T_N"] * p["T_K"] * p["G"] * p["nK"] / per_clk
+        return {"eta": float(busy_rt / (p["S"] * p["b"] * span)),
+                "sclk_mhz": float(100.0 * cycles / busy_rt),
+                "mfma_cycle_eff": float(ideal / cycles)}
 
     def step(self, stream):
         a = self.args[self.i % self.copies]
@@ -229,9 +242,11 @@ def main():
         w = next(x for x in inputs.WORKLOADS if x.name == name)
         c = Case(w, int(si or 0), torch, g, inputs, tile=args.tile)
         _, ev = time_case(c, torch, args.steps, args.warmup)
+        me = c.measured_eta(torch) if args.stamps else None
         print(json.dumps({"workload": c.name(), "us_per_call": round(ev / args.steps * 1e6, 2),
                           "tile": c.plan["tile"], "split": c.plan["split"],
-                          "tail": [c.plan["tail_tiles"], c.plan["tail_split"]]}), flush=True)
+                          "tail": [c.plan["tail_tiles"], c.plan["tail_split"]],
+                          "measured": me}), flush=True)
         return
 
     head_w = inputs.WORKLOADS[1]
@@ -284,8 +299,11 @@ def main():
                     "eta_wave": [p["eta_wave_num"], p["eta_wave_den"]],
                     "eta_pad": [p["eta_pad_num"], p["eta_pad_den"]],
                     "eta_sched": [p["eta_sched_num"], p["eta_sched_den"]],
-                    "eta_measured": (lambda e: None if e is None else round(e, 4))(c.measured_eta(torch)),
                 })
+                me = c.measured_eta(torch)
+                detail[-1]["eta_measured"] = None if me is None else round(me["eta"], 4)
+                detail[-1]["sclk_mhz"] = None if me is None else round(me["sclk_mhz"], 0)
+                detail[-1]["mfma_cycle_eff"] = None if me is None else round(me["mfma_cycle_eff"], 4)
                 if c is not head:
                     del c
                     torch.cuda.empty_cache()

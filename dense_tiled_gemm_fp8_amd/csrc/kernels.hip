@@ -207,8 +207,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     if (p.s.xcd_remap) first = xcd_remap(first, p.s.grid);
 
     for (int32_t u = first; u < p.s.units; u += p.s.grid) {
-        uint64_t stamp0 = 0;
-        if (p.stamps) stamp0 = __builtin_amdgcn_s_memrealtime();
+        uint64_t stamp0 = 0, clk0 = 0;
+        if (p.stamps) {
+            stamp0 = __builtin_amdgcn_s_memrealtime();
+            clk0 = __builtin_amdgcn_s_memtime();
+        }
         const Unit un = decode_unit(p.s, u);
         const int32_t m0 = un.tile_m * TM, n0 = un.tile_n * TN;
         const i32x4 ra = rsrc_words(p.A + (int64_t)un.batch * p.stride_a + (int64_t)m0 * p.lda);
@@ -503,9 +506,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             const uint64_t stamp1 = __builtin_amdgcn_s_memrealtime();
+            const uint64_t clk1 = __builtin_amdgcn_s_memtime();
             if (threadIdx.x == 0) {
-                p.stamps[2 * (int64_t)u] = stamp0;
-                p.stamps[2 * (int64_t)u + 1] = stamp1;
+                uint64_t *st = p.stamps + 4 * (int64_t)u;
+                st[0] = stamp0;
+                st[1] = stamp1;
+                st[2] = clk0;
+                st[3] = clk1;
             }
         }
     }

@@ -98,13 +98,16 @@ typedef struct gemm355_args {
                                  repacked operands, 256-byte aligned
                                  (EALIGN otherwise); NULL: library-owned  */
     size_t workspace_bytes;   /* size of `workspace`                      */
-    uint64_t *unit_stamps;    /* device uint64 [2 * plan.units] or NULL.
+    uint64_t *unit_stamps;    /* device uint64 [4 * plan.units] or NULL.
                                  When set, work unit u records the device
                                  real-time clock (100 MHz) when its
-                                 workgroup starts it at [2u] and after its
-                                 stores have completed at [2u + 1], for
+                                 workgroup starts it at [4u] and after its
+                                 stores have completed at [4u + 1], and the
+                                 shader clock counter (cycles) at the same
+                                 two points at [4u + 2] and [4u + 3], for
                                  measuring how evenly the units fill the
-                                 device.  8-byte aligned (EALIGN).        */
+                                 device and how many cycles a unit takes.
+                                 8-byte aligned (EALIGN).                  */
 } gemm355_args;
 
 /* Everything the planner decided for one call.  Efficiencies are exact

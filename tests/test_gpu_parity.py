@@ -318,14 +318,19 @@ def test_unit_stamps_cover_every_unit():
         p = g.gemm355_plan(args)
         H.say("stamps tile", tile, "split", split, "persistent", pers, "units", p["units"], "grid", p["grid"])
         g.gemm355_gemm_ex(args)
-        stamps = torch.zeros(2 * p["units"], dtype=torch.int64, device="cuda")
+        stamps = torch.zeros(4 * p["units"], dtype=torch.int64, device="cuda")
         args2 = g.make_args(M, N, K, A=A, B=B, C=C1, dtype=g.BF16_F32, tile=tile, split_k=split,
                             persistent=pers, unit_stamps=stamps)
         g.gemm355_gemm_ex(args2)
         torch.cuda.synchronize()
         assert torch.equal(C0, C1)
-        st = stamps.view(-1, 2).cpu().numpy()
+        st = stamps.view(-1, 4).cpu().numpy()
         assert (st[:, 0] > 0).all() and (st[:, 1] >= st[:, 0]).all()
+        assert (st[:, 3] > st[:, 2]).all()
+        # shader cycles per real-time tick (100 MHz): a clock between 0.3 and 3 GHz
+        mhz = 100.0 * float((st[:, 3] - st[:, 2]).sum()) / max(float((st[:, 1] - st[:, 0]).sum()), 1.0)
+        H.say("  shader clock from the stamps (MHz)", mhz)
+        assert 300.0 < mhz < 3000.0
         busy = float((st[:, 1] - st[:, 0]).sum())
         span = float(st[:, 1].max() - st[:, 0].min())
         eta = busy / (p["S"] * p["b"] * span)
