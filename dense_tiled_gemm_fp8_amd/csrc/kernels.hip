@@ -7,9 +7,11 @@
  *                     epilogue to C or to a split-K partial slot
  *   reduce_kernel     the split-K combine: sums a tile's partial slots in
  *                     ascending slice order, scales, converts, stores C
- *   pack_kernel       repacks an operand into the K-contiguous, 16-byte
- *                     aligned layout the main loop reads (other layouts,
- *                     misaligned rows, K not a multiple of 16 bytes)
+ *   pack_rows_kernel, pack_transpose_kernel
+ *                     repack an operand into the K-contiguous, 16-byte
+ *                     aligned layout the main loop reads (misaligned rows
+ *                     or K not a multiple of 16 bytes; the three other
+ *                     operand layouts)
  *   zero_kernel       C = 0 for K == 0
  *
  * Source pages: "10. Tensor Cores, shapes, and tile alignment" (tile grid,
@@ -595,27 +597,112 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
  * Repack one operand to K-contiguous rows of ldd_bytes (a multiple of 16),
  * zero-filled beyond K.  Source element (row, k) of batch entry g is at
  * src[g*stride + (kmajor ? row*ld + k : k*ld + row)] (elements of esize
- * bytes).  One thread per 16-byte output chunk.
+ * bytes).
+ *
+ * pack_rows_kernel (K-contiguous source whose rows are misaligned or whose
+ * K is not a whole number of 16-byte chunks): one wavefront per row.  The
+ * row is read through a buffer resource based at the 16-byte boundary at
+ * or below the row's first byte and ending at the 16-byte boundary at or
+ * above its last byte, so every 16-byte block read lies in a block that
+ * holds a byte of the row (never past the allocation) and blocks beyond
+ * read as zero.  Output chunk c is bytes [sh + 16c, sh + 16c + 16) of that
+ * window (sh = the row's offset from the boundary): two aligned 16-byte
+ * loads and a byte funnel shift.  Bytes at or beyond K are cleared.
  */
-__global__ __launch_bounds__(256) void pack_kernel(PackParams pk)
+__global__ __launch_bounds__(256) void pack_rows_kernel(PackParams pk)
 {
-    const int64_t chunks_per_row = pk.ldd_bytes / 16;
-    const int64_t total = (int64_t)pk.batch * pk.rows * chunks_per_row;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t g = t / ((int64_t)pk.rows * chunks_per_row);
-        const int64_t rem = t - g * pk.rows * chunks_per_row;
-        const int64_t row = rem / chunks_per_row;
-        const int64_t ch = rem - row * chunks_per_row;
-        uint8_t out[16];
-        const int per = 16 / pk.esize;
-        for (int e = 0; e < per; ++e) {
-            const int64_t k = ch * per + e;
-            uint16_t v = 0;
-            if (k < pk.K) {
-                const int64_t idx = g * pk.stride + (pk.kmajor ? row * pk.ld + k : k * pk.ld + row);
-                v = pk.esize == 2 ? ((const uint16_t *)pk.src)[idx] : ((const uint8_t *)pk.src)[idx];
+    const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row_id >= (int64_t)pk.batch * pk.rows) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t g = row_id / pk.rows, r = row_id - g * pk.rows;
+    const uint8_t *row = (const uint8_t *)pk.src + (g * pk.stride + r * pk.ld) * pk.esize;
+    const uint32_t kbytes = (uint32_t)pk.K * (uint32_t)pk.esize;
+    const uintptr_t ra = (uintptr_t)row;
+    const uint32_t sh = (uint32_t)(ra & 15u);
+    const uint8_t *base = (const uint8_t *)(ra - sh);
+    const uint32_t nrec = (sh + kbytes + 15u) & ~15u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)nrec, 0x00020000);
+    uint8_t *drow = pk.dst + g * pk.dst_stride_bytes + r * pk.ldd_bytes;
+    const uint32_t q = sh >> 2, rb = sh & 3u;
+    const int32_t chunks = (int32_t)(pk.ldd_bytes / 16);
+    for (int32_t c = lane; c < chunks; c += 64) {
+        const uint32_t off = (uint32_t)c * 16u;
+        i32x4 out{0, 0, 0, 0};
+        if (off < kbytes) {
+            const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+            const int w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            int o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                /* dword j of the chunk: bytes sh + 4j .. sh + 4j + 3 of the
+                 * window, i.e. (w[q + j + 1] : w[q + j]) >> (8 rb) */
+                int d0 = w[j], d1 = w[j + 1];
+                if (q == 1) { d0 = w[j + 1]; d1 = w[j + 2]; }
+                if (q == 2) { d0 = w[j + 2]; d1 = w[j + 3]; }
+                if (q == 3) { d0 = w[j + 3]; d1 = w[j + 4]; }
+                o[j] = (int)__builtin_amdgcn_alignbyte((uint32_t)d1, (uint32_t)d0, rb);
             }
+            /* clear bytes at or beyond K */
+            const uint32_t valid = kbytes - off;
+            if (valid < 16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int32_t vb = (int32_t)valid - 4 * j;
+                    const uint32_t keep = vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+                    o[j] = (int)((uint32_t)o[j] & keep);
+                }
+            }
+            out = i32x4{o[0], o[1], o[2], o[3]};
+        }
+        *(i32x4 *)(drow + off) = out;
+    }
+}
+
+/*
+ * pack_transpose_kernel (source with rows contiguous along the operand's
+ * M or N index, i.e. element (row, k) at k*ld + row): a workgroup moves a
+ * 64-row x 64-k block through LDS: reads along rows (consecutive lanes,
+ * consecutive rows), writes 16-byte chunks of the K-contiguous output.
+ * Blocks along k cover the whole padded row; k >= K reads as zero.
+ */
+__global__ __launch_bounds__(256) void pack_transpose_kernel(PackParams pk)
+{
+    __shared__ uint16_t tile[64][65];
+    const int32_t kblocks = (int32_t)((pk.ldd_bytes / pk.esize + 63) / 64);
+    const int32_t rblocks = (pk.rows + 63) / 64;
+    const int64_t bid = blockIdx.x;
+    const int32_t kb = (int32_t)(bid % kblocks);
+    const int64_t t2 = bid / kblocks;
+    const int32_t rbk = (int32_t)(t2 % rblocks);
+    const int64_t g = t2 / rblocks;
+    const int32_t r0 = rbk * 64, k0 = kb * 64;
+    const int t = threadIdx.x;
+    const int rr = t & 63;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int kk = (t >> 6) + 4 * i;
+        const int32_t row = r0 + rr, k = k0 + kk;
+        uint16_t v = 0;
+        if (row < pk.rows && k < pk.K) {
+            const int64_t idx = g * pk.stride + (int64_t)k * pk.ld + row;
+            v = pk.esize == 2 ? ((const uint16_t *)pk.src)[idx] : ((const uint8_t *)pk.src)[idx];
+        }
+        tile[kk][rr] = v;
+    }
+    __syncthreads();
+    /* output: 64 rows x (64 esize) bytes = 64 x (8 or 4) chunks of 16 bytes */
+    const int cpr = pk.esize == 2 ? 8 : 4;
+    const int per = 16 / pk.esize;
+    for (int idx = t; idx < 64 * cpr; idx += 256) {
+        const int r = idx / cpr, qc = idx % cpr;
+        const int32_t row = r0 + r;
+        const int64_t boff = (int64_t)k0 * pk.esize + qc * 16;
+        if (row >= pk.rows || boff >= pk.ldd_bytes) continue;
+        uint8_t out[16];
+        for (int e = 0; e < per; ++e) {
+            const uint16_t v = tile[qc * per + e][r];
             if (pk.esize == 2) {
                 out[2 * e] = (uint8_t)(v & 0xFF);
                 out[2 * e + 1] = (uint8_t)(v >> 8);
@@ -625,7 +712,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams pk)
         }
         i32x4 w;
         __builtin_memcpy(&w, out, 16);
-        *(i32x4 *)(pk.dst + g * pk.dst_stride_bytes + row * pk.ldd_bytes + ch * 16) = w;
+        *(i32x4 *)(pk.dst + g * pk.dst_stride_bytes + (int64_t)row * pk.ldd_bytes + boff) = w;
     }
 }
 
@@ -755,11 +842,15 @@ hipError_t launch_reduce(const ReduceParams &r0, int32_t tiles, hipStream_t stre
 
 hipError_t launch_pack(const PackParams &pk, hipStream_t stream)
 {
-    const int64_t total = (int64_t)pk.batch * pk.rows * (pk.ldd_bytes / 16);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, pk);
+    if (pk.kmajor) {
+        const int64_t rows = (int64_t)pk.batch * pk.rows;
+        hipLaunchKernelGGL(pack_rows_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream, pk);
+    } else {
+        const int64_t kblocks = (pk.ldd_bytes / pk.esize + 63) / 64;
+        const int64_t rblocks = (pk.rows + 63) / 64;
+        hipLaunchKernelGGL(pack_transpose_kernel, dim3((uint32_t)((int64_t)pk.batch * rblocks * kblocks)), dim3(256), 0,
+                           stream, pk);
+    }
     return hipGetLastError();
 }
 
