@@ -1,11 +1,14 @@
 """Benchmark of libgemm355 on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-detail] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S]
+                    [--no-cpu-baseline] [--no-detail] [--workload NAME]
 
 A step is one call of the library on the headline workload (bf16
 4096 x 4096 x 4096, A row-major, B column-major, bf16 C, fp32 accumulate)
-with inputs already resident in HBM.  Prints ONE JSON line: throughput in
+with inputs already resident in HBM.  Before the W untimed warm-up steps the
+device runs the same call untimed for S seconds (default 0.5): from idle the
+shader clock takes some tens of milliseconds of load to reach its
+(power-limited) operating point.  Prints ONE JSON line: throughput in
 TFLOP/s of useful work 2MNK per step (section "Shape the operation" of page
 "10. Tensor Cores, shapes, and tile alignment"), the roofline of the main
 kernel (achieved vs the dense bf16 MFMA peak, timed with HIP events on the
@@ -50,8 +53,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=float, default=None, metavar="SECONDS",
+                    help="untimed calls for this long before the warm-up of each workload "
+                         "(the clock ramps up from idle); default 0.5 s, 0 with --profile")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--workload", default=None, help="time only this workload name (detail)")
@@ -63,6 +69,13 @@ def parse():
     ap.add_argument("--stamps", action="store_true",
                     help="with --profile: one more call with the per-unit clock hook; prints the "
                          "measured eta, shader clock and MFMA cycle efficiency")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="with --profile: after the timed calls, keep calling for this long and "
+                         "print the sustained time per call; the device's socket power and "
+                         "graphics clocks are sampled (amd-smi) half way through")
+    ap.add_argument("--vendor", action="store_true",
+                    help="with --profile and a bf16 workload: time the vendor library "
+                         "(torch.matmul on the same operands) instead of this library, as context")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -169,13 +182,28 @@ class Case:
         return "%s %s" % (self.w.name, shp)
 
 
-def time_case(case, torch, steps, warmup):
-    """Warm up, then time `steps` back-to-back calls: wall clock around the
-    whole region (synchronised on both sides) and one HIP event pair on the
-    launch stream around the same calls.  Returns (wall seconds, event
-    seconds), both for all `steps` calls."""
+def settle(case, torch, seconds):
+    """Untimed calls for `seconds` of wall time before the warm-up: the shader
+    clock rises from idle over some tens of milliseconds of load, so a short
+    region right after idle measures the ramp, not the kernel."""
+    if seconds <= 0:
+        return
+    sp = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            case.step(sp)
+        torch.cuda.synchronize()
+
+
+def time_case(case, torch, steps, warmup, settle_s=0.0):
+    """Settle and warm up, then time `steps` back-to-back calls: wall clock
+    around the whole region (synchronised on both sides) and one HIP event
+    pair on the launch stream around the same calls.  Returns (wall seconds,
+    event seconds), both for all `steps` calls."""
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    settle(case, torch, settle_s)
     for _ in range(warmup):
         case.step(sp)
     torch.cuda.synchronize()
@@ -189,6 +217,53 @@ def time_case(case, torch, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, e0.elapsed_time(e1) * 1e-3
+
+
+def sample_smi():
+    """Socket power (W) and graphics clocks (MHz) from amd-smi, or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock"], capture_output=True, text=True,
+                           timeout=20)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    txt = r.stdout
+    pw = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    gfx = []
+    for block in re.split(r"\n\s*GFX_\d+:", txt)[1:]:
+        m = re.search(r"^\s*CLK:\s*([0-9.]+)\s*MHz", block, re.M)
+        if m:
+            gfx.append(float(m.group(1)))
+    return {"socket_power_w": float(pw[0]) if pw else None, "gfx_clk_mhz": gfx}
+
+
+def sustain(case, torch, seconds):
+    """Call the case back to back for `seconds` (synchronising every 50
+    calls), sample power and clocks half way, and return the sustained time
+    per call."""
+    import threading
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    smi = {}
+    t = threading.Timer(seconds / 2, lambda: smi.update(sample_smi() or {}))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = 0
+    t0 = time.perf_counter()
+    e0.record(stream)
+    t.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            case.step(sp)
+        n += 50
+        torch.cuda.synchronize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t.join()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    return {"sustained_us_per_call": round(us, 2), "sustained_calls": n,
+            "sustained_tflops": round(case.flops / us / 1e6, 1), "smi": smi or None}
 
 
 def cpu_baseline(torch, budget_s=15.0):
@@ -241,12 +316,20 @@ def main():
         name, _, si = args.profile.partition(":")
         w = next(x for x in inputs.WORKLOADS if x.name == name)
         c = Case(w, int(si or 0), torch, g, inputs, tile=args.tile)
-        _, ev = time_case(c, torch, args.steps, args.warmup)
-        me = c.measured_eta(torch) if args.stamps else None
-        print(json.dumps({"workload": c.name(), "us_per_call": round(ev / args.steps * 1e6, 2),
-                          "tile": c.plan["tile"], "split": c.plan["split"],
-                          "tail": [c.plan["tail_tiles"], c.plan["tail_split"]],
-                          "measured": me}), flush=True)
+        if args.vendor:
+            if w.fmt != "bf16" or c.batch != 1:
+                sys.exit("--vendor: bf16 single products only")
+            Av, Bv = c.As[0].view(torch.bfloat16), c.Bs[0].view(torch.bfloat16)
+            c.step = lambda stream: torch.matmul(Av, Bv.t(), out=c.C)
+        _, ev = time_case(c, torch, args.steps, args.warmup, args.settle or 0.0)
+        me = c.measured_eta(torch) if args.stamps and not args.vendor else None
+        out = {"workload": c.name(), "us_per_call": round(ev / args.steps * 1e6, 2),
+               "tile": c.plan["tile"], "split": c.plan["split"],
+               "tail": [c.plan["tail_tiles"], c.plan["tail_split"]], "measured": me,
+               "vendor": bool(args.vendor)}
+        if args.sustain > 0:
+            out.update(sustain(c, torch, args.sustain))
+        print(json.dumps(out), flush=True)
         return
 
     head_w = inputs.WORKLOADS[1]
@@ -255,7 +338,9 @@ def main():
     log("bench: plan", {k: head.plan[k] for k in ("tile", "T_M", "T_N", "T_K", "G", "grid", "split")})
     torch.cuda.synchronize()
     # timed region: barrier (single rank) + synchronize on both sides
-    wall, ev = time_case(head, torch, args.steps, args.warmup)
+    if args.settle is None:
+        args.settle = 0.5
+    wall, ev = time_case(head, torch, args.steps, args.warmup, args.settle)
     ms_per_step = wall / args.steps * 1e3
     value = head.flops * args.steps / wall / 1e12
     kern_avg = ev / args.steps
@@ -278,6 +363,7 @@ def main():
                 log("bench: detail", w.name, w.shapes[si])
                 c = head if (w is head_w and si == 0) else Case(w, si, torch, g, inputs)
                 # three timed repetitions; the median of their per-call averages
+                settle(c, torch, args.settle / 2)
                 reps = []
                 for _ in range(3):
                     n = max(10, args.steps // 2)
@@ -317,7 +403,7 @@ def main():
     line = {
         "metric": "GEMM TFLOP/s and % of MFMA peak (bf16 4096^3; skinny split-K shapes)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "warmup": args.warmup, "settle_s": args.settle, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "bf16 GEMM 4096x4096x4096, A row-major, B column-major, C bf16, "
                                "fp32 accumulate, entries N(0,1) rounded to bf16",
