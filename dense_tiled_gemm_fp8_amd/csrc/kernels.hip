@@ -437,20 +437,25 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         /* row of accumulator register e relative to the lane's first row */
         auto erow = [](int e) __attribute__((always_inline)) { return MI == 32 ? (e >> 2) * 8 + (e & 3) : e; };
         if (un.slot >= 0) {
+            /* partial slot: the tile's positions inside M x N only (the
+             * combine pass reads no others) */
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (int64_t)un.slot * (TM * TN));
+            const int32_t mrem = p.M - m0, nrem = p.N - n0;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const uint32_t voff =
-                        (uint32_t)(((wm * WTM + i * MI + ehi * 4) * TN + wn * WTN + j * MI + ecol) * 4);
+                    const int col = wn * WTN + j * MI + ecol;
+                    const int row0 = wm * WTM + i * MI + ehi * 4;
+                    const uint32_t voff = (uint32_t)((row0 * TN + col) * 4);
 #pragma unroll
                     for (int e = 0; e < ACC_N; ++e) {
                         /* copy the element out first: a bit_cast applied to
                          * a vector subscript directly was lowered to element
                          * 0 for every e */
                         const float v = acc[i][j][e];
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, voff,
+                        const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, ok ? voff : kOOB,
                                                               erow(e) * TN * 4, 0);
                     }
                     /* one block at a time keeps the epilogue's registers few */
@@ -521,11 +526,6 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
 }
 
 /*
- * Split-K combine.  Block x = one split tile (uniform split: tile x; tail:
- * tail tile x), 256 threads x 4 consecutive elements per step over the
- * TM x TN partial tile.  Slices are summed in ascending order in fp32.
- */
-/*
  * Split-K combine.  Block x = (reduce tile q, chunk of P float4 positions of
  * the tile); its 256 threads are SG slice groups of P = 256 / SG positions.
  * Group g sums slices [g nsl / SG, (g + 1) nsl / SG) of its position in
@@ -551,7 +551,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
     const int32_t g = (int32_t)threadIdx.x / P, pos = (int32_t)threadIdx.x % P;
     const int64_t tile_f4 = (int64_t)r.TM * r.TN / 4;
     const int64_t e4 = (int64_t)chunk * P + pos;
-    const bool live = e4 < tile_f4;
+    /* positions outside M x N were not written by the main pass and are
+     * not read here */
+    const bool live = e4 < tile_f4 && m0 + (int32_t)(e4 * 4 / r.TN) < r.M && n0 + (int32_t)(e4 * 4 % r.TN) < r.N;
     const int32_t s_lo = (int32_t)((int64_t)g * nsl / SG), s_hi = (int32_t)((int64_t)(g + 1) * nsl / SG);
     f32x4 sum = f32x4{};
     if (live) {

@@ -39,6 +39,7 @@ constexpr int64_t kMaxDim = 0x7FFFFFFF;
 constexpr int64_t kMaxOffset = 0x7FFF0000;   /* largest 32-bit buffer offset used */
 constexpr int32_t kMaxSplit = 256;
 constexpr int32_t kMaxNK = 1 << 23;
+constexpr int32_t kGroupM = 4;                        /* raster band height in tiles */
 constexpr double kPeakBf16PerCu = 2516.6e12 / 256.0;   /* dense MFMA, 2.4 GHz */
 constexpr double kPeakFp8PerCu = 5033.2e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
@@ -163,9 +164,27 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(c.b, cdiv(std::max<int64_t>(c.grid, 1), S)));
     const double eff = cfg.mfma_eff[std::min<int64_t>(per_cu, 4) - 1];
     const double t_mfma = (double)busiest_cu * 2.0 * cfg.TM * cfg.TN * cfg.TK / (cu_peak * eff);
+    /* partial sums are written and read for the split tiles' positions
+     * inside M x N only */
     double partial = 0;
-    if (c.split > 1) partial = (double)c.G * c.split * cfg.TM * cfg.TN * 4.0;
-    if (c.tail_tiles) partial = (double)c.tail_tiles * c.tail_split * cfg.TM * cfg.TN * 4.0;
+    if (c.split > 1 || c.tail_tiles) {
+        Sched sc{};
+        sc.tiles_m = (int32_t)c.tiles_m;
+        sc.tiles_n = (int32_t)c.tiles_n;
+        sc.tiles_per_batch = (int32_t)(c.tiles_m * c.tiles_n);
+        sc.batch = (int32_t)batch;
+        sc.group_m = kGroupM;
+        const int64_t first = c.split > 1 ? 0 : c.units_main;
+        const int64_t count = c.split > 1 ? c.G : c.tail_tiles;
+        const int32_t nsl = c.split > 1 ? c.split : c.tail_split;
+        for (int64_t t = first; t < first + count; ++t) {
+            Unit u;
+            tile_coords(sc, (int32_t)t, u);
+            const int64_t rows = std::min<int64_t>(cfg.TM, M - (int64_t)u.tile_m * cfg.TM);
+            const int64_t cols = std::min<int64_t>(cfg.TN, N - (int64_t)u.tile_n * cfg.TN);
+            partial += (double)rows * cols * 4.0 * nsl;
+        }
+    }
     const double bytes = (double)batch * ((double)(M + N) * K * esize + (double)M * N * out_esize) +
                          2.0 * partial;
     const double spread = busiest_cu ? (double)total / ((double)S * busiest_cu) : 1.0;
@@ -471,7 +490,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     s.tiles_n = (int32_t)best.tiles_n;
     s.tiles_per_batch = (int32_t)(best.tiles_m * best.tiles_n);
     s.batch = (int32_t)batch;
-    s.group_m = 4;
+    s.group_m = kGroupM;
     s.nK = (int32_t)best.nK;
     s.split = best.split;
     s.units_main = (int32_t)best.units_main;
