@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgemm355.so")
-SOURCES = ["kernels.hip", "plan.hip", "api.hip"]
+SOURCES = ["kernels.hip", "quant.hip", "plan.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -12,6 +12,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -248,7 +249,10 @@ gemm355_status run(const gemm355_args &a, void *stream)
     gp.out_bf16 = P.out_esize == 2 ? 1 : 0;
     gp.stamps = a.unit_stamps;
     gp.s = P.s;
-    if (P.s.grid > 0 && launch_gemm(P.pub.tile, gp, hs) != hipSuccess) return GEMM355_EHIP;
+    /* operand-format pair of an 8-bit product: 0 E4M3 x E4M3, 1 E5M2 x E5M2,
+     * 2 E4M3 x E5M2 */
+    const int32_t fmt = !dtype_fp8(a.dtype) ? 0 : dtype_fmt_a(a.dtype) ? 1 : dtype_fmt_b(a.dtype) ? 2 : 0;
+    if (P.s.grid > 0 && launch_gemm(P.pub.tile, fmt, gp, hs) != hipSuccess) return GEMM355_EHIP;
 
     if (P.reduce_tiles > 0) {
         ReduceParams rp;
@@ -415,6 +419,44 @@ gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu)
         return GEMM355_EHIP;
     }
     *blocks_per_cu = n;
+    return GEMM355_OK;
+}
+
+gemm355_status gemm355_quantize(const void *x, int64_t n, int64_t batch, gemm355_src src, gemm355_fp8 fmt,
+                                void *q, float *scale, void *stream)
+{
+    if (n < 0 || batch < 1) return GEMM355_EINVAL;
+    if ((int)src < 0 || (int)src > 1 || (int)fmt < 0 || (int)fmt > 1) return GEMM355_EINVAL;
+    if (!scale || (n > 0 && (!x || !q))) return GEMM355_EINVAL;
+    const int64_t es = src == GEMM355_SRC_F32 ? 4 : 2;
+    if (((uintptr_t)scale & 3u) != 0) return GEMM355_EALIGN;
+    if (n > 0 && ((uintptr_t)x % (uintptr_t)es) != 0) return GEMM355_EALIGN;
+    if (n > 0 && (n >= ((int64_t)1 << 40) || batch >= ((int64_t)1 << 40) / n)) return GEMM355_EUNSUPPORTED;
+    const int64_t total = n * batch;
+    const int32_t parts = (int32_t)std::min<int64_t>(1024, std::max<int64_t>(1, (n + 8191) / 8192));
+    if (batch * parts > ((int64_t)1 << 30)) return GEMM355_EUNSUPPORTED;
+    /* no overlap between the input, the codes and the scales */
+    auto overlap = [](uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; };
+    const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(total * es);
+    const uintptr_t q0 = (uintptr_t)q, q1 = q0 + (uintptr_t)total;
+    const uintptr_t s0 = (uintptr_t)scale, s1 = s0 + (uintptr_t)(batch * 4);
+    if (total > 0 && (overlap(x0, x1, q0, q1) || overlap(x0, x1, s0, s1) || overlap(q0, q1, s0, s1)))
+        return GEMM355_EINVAL;
+    void *scr = nullptr;
+    gemm355_status st = library_scratch((size_t)(batch * parts) * sizeof(float), stream, &scr);
+    if (st != GEMM355_OK) return st;
+    QuantParams qp;
+    qp.x = x;
+    qp.q = (uint8_t *)q;
+    qp.scale = scale;
+    qp.maxima = (float *)scr;
+    qp.n = n;
+    qp.batch = batch;
+    qp.parts = parts;
+    qp.src = src == GEMM355_SRC_F32 ? 0 : 1;
+    qp.fmt = fmt == GEMM355_FP8_E4M3 ? 0 : 1;
+    qp.vec = (x0 % 16 == 0) && (q0 % 8 == 0) && (n % 8 == 0);
+    if (launch_quantize(qp, (hipStream_t)stream) != hipSuccess) return GEMM355_EHIP;
     return GEMM355_OK;
 }
 

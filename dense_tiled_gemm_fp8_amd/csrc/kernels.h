@@ -51,7 +51,25 @@ struct PackParams {
     int32_t kmajor;               /* 1: source K-contiguous                 */
 };
 
-hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream);
+/* Per-tensor quantisation to 8 bits (quant.hip). */
+struct QuantParams {
+    const void *x;                /* batch tensors of n elements            */
+    uint8_t *q;                   /* codes, same layout                     */
+    float *scale;                 /* [batch] dequantisation factors         */
+    float *maxima;                /* scratch [batch * parts]                */
+    int64_t n, batch;
+    int32_t parts;                /* blocks per tensor (1 .. 1024)          */
+    int32_t src;                  /* 0 fp32, 1 bf16                         */
+    int32_t fmt;                  /* 0 E4M3, 1 E5M2                         */
+    int32_t vec;                  /* 1: 8-element vector path (x 16-byte and
+                                     q 8-byte aligned, n % 8 == 0)          */
+};
+
+hipError_t launch_quantize(const QuantParams &qp, hipStream_t stream);
+
+/* fmt: operand formats of an 8-bit tile (0 E4M3 x E4M3, 1 E5M2 x E5M2,
+ * 2 E4M3 x E5M2); 0 for bf16 tiles */
+hipError_t launch_gemm(int32_t tile, int32_t fmt, const GemmParams &p, hipStream_t stream);
 const void *gemm_kernel_symbol(int32_t tile);
 hipError_t launch_reduce(const ReduceParams &r, int32_t tiles, hipStream_t stream);
 hipError_t launch_pack(const PackParams &pk, hipStream_t stream);

@@ -160,9 +160,12 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * issued into the stage just freed, and the last step's MFMAs overlap the
  * reads of the next tile's first fragments.
  */
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
+    /* 8-bit operand formats (instruction format codes: 0 E4M3, 1 E5M2):
+     * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B) */
+    constexpr int FA = FMT == 1 ? 1 : 0, FB = FMT >= 1 ? 1 : 0;
     constexpr int NW = WGM * WGN, WN = WGN;
     constexpr int WTM = TM / WGM, WTN = TN / WGN;
     constexpr int FM = WTM / MI, FN = WTN / MI;
@@ -313,14 +316,14 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
                     else if constexpr (!FP8)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
-                    /* format fields 0/0: both operands E4M3; zero scales
-                     * select the unscaled instruction */
+                    /* format fields FA / FB of the A and B operands; zero
+                     * scales select the unscaled instruction */
                     else if constexpr (MI == 32)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                            fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                            fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, 0, 0, 0);
                 }
                 if constexpr (t < FM)
                     fa[CUR ^ 1][t] = frag(ns + wm * WTM * RB, nks, t);
@@ -736,12 +739,29 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
-static hipError_t launch_tile(const GemmParams &p, hipStream_t stream)
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
+static hipError_t launch_one(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI>), dim3(p.s.grid),
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, FMT>), dim3(p.s.grid),
                        dim3(WGM * WGN * 64), 0, stream, p);
     return hipGetLastError();
+}
+
+/* bf16 tiles have one instantiation; 8-bit tiles one per operand-format pair */
+template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
+static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stream)
+{
+    if constexpr (FP8) {
+        switch (fmt) {
+        case 0: return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+        case 1: return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 1>(p, stream);
+        case 2: return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 2>(p, stream);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        if (fmt != 0) return hipErrorInvalidValue;
+        return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+    }
 }
 
 /* Instantiations, in tile-table order (csrc/tiles.h):
@@ -805,11 +825,11 @@ GEMM355_TILES(X)
 static_assert(0 GEMM355_TILES(X) == kNumTiles, "one instantiation per tile-table entry");
 #undef X
 
-hipError_t launch_gemm(int32_t tile, const GemmParams &p, hipStream_t stream)
+hipError_t launch_gemm(int32_t tile, int32_t fmt, const GemmParams &p, hipStream_t stream)
 {
     switch (tile) {
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) \
-    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp, mi>(p, stream);
+    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp, mi>(fmt, p, stream);
         GEMM355_TILES(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -820,7 +840,7 @@ const void *gemm_kernel_symbol(int32_t tile)
 {
     switch (tile) {
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) \
-    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp, mi>;
+    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp, mi, 0>;
         GEMM355_TILES(X)
 #undef X
     default: return nullptr;

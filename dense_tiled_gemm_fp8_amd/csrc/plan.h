@@ -15,7 +15,7 @@ namespace g355 {
 struct Plan {
     gemm355_plan_t pub;
     Sched s;
-    int32_t esize;              /* input element bytes (2 bf16, 1 E4M3)     */
+    int32_t esize;              /* input element bytes (2 bf16, 1 8-bit)    */
     int32_t out_esize;          /* 4 fp32, 2 bf16                           */
     int32_t Kb;                 /* K bytes seen by the main loop            */
     int32_t pack_a, pack_b;
@@ -28,6 +28,16 @@ struct Plan {
     int32_t reduce_tiles;       /* blocks of the combine kernel (0: none)   */
     int32_t reduce_tail;        /* 1: combine the tail tiles                */
 };
+
+/* Element-type queries. */
+inline bool dtype_fp8(gemm355_dtype d) { return d >= GEMM355_E4M3_F32 && d <= GEMM355_E4M3_E5M2_BF16; }
+inline bool dtype_out_bf16(gemm355_dtype d)
+{
+    return d == GEMM355_BF16_BF16 || d == GEMM355_E4M3_BF16 || d == GEMM355_E5M2_BF16 || d == GEMM355_E4M3_E5M2_BF16;
+}
+/* 8-bit format codes of the MFMA operands: 0 E4M3, 1 E5M2 */
+inline int32_t dtype_fmt_a(gemm355_dtype d) { return (d == GEMM355_E5M2_F32 || d == GEMM355_E5M2_BF16) ? 1 : 0; }
+inline int32_t dtype_fmt_b(gemm355_dtype d) { return (d >= GEMM355_E5M2_F32 && d <= GEMM355_E4M3_E5M2_BF16) ? 1 : 0; }
 
 /* Validate `a` and plan it for S compute units.  Never touches a device. */
 gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &out);

@@ -273,9 +273,9 @@ int32_t resident_workgroups(int32_t tile)
 
 gemm355_status check_pointers(const gemm355_args &a)
 {
-    const bool fp8 = a.dtype == GEMM355_E4M3_F32 || a.dtype == GEMM355_E4M3_BF16;
+    const bool fp8 = dtype_fp8(a.dtype);
     const int32_t esize = fp8 ? 1 : 2;
-    const int32_t out_esize = (a.dtype == GEMM355_BF16_BF16 || a.dtype == GEMM355_E4M3_BF16) ? 2 : 4;
+    const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
     const int64_t M = a.M, N = a.N, K = a.K, batch = a.batch;
@@ -304,7 +304,7 @@ gemm355_status check_pointers(const gemm355_args &a)
 gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
 {
     memset(&P, 0, sizeof P);
-    if ((int)a.dtype < 0 || (int)a.dtype > 3) return GEMM355_EINVAL;
+    if ((int)a.dtype < 0 || (int)a.dtype > 7) return GEMM355_EINVAL;
     if ((int)a.layout < 0 || (int)a.layout > 3) return GEMM355_EINVAL;
     if (a.M < 0 || a.N < 0 || a.K < 0 || a.batch < 1) return GEMM355_EINVAL;
     if (a.split_k < 0 || a.persistent < -1 || a.persistent > 1) return GEMM355_EINVAL;
@@ -312,10 +312,10 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     if (S < 1) return GEMM355_EINVAL;
     if (a.stride_a < 0 || a.stride_b < 0 || a.stride_c < 0) return GEMM355_EINVAL;
 
-    const bool fp8 = a.dtype == GEMM355_E4M3_F32 || a.dtype == GEMM355_E4M3_BF16;
+    const bool fp8 = dtype_fp8(a.dtype);
     const int32_t dclass = fp8 ? 1 : 0;
     const int32_t esize = fp8 ? 1 : 2;
-    const int32_t out_esize = (a.dtype == GEMM355_BF16_BF16 || a.dtype == GEMM355_E4M3_BF16) ? 2 : 4;
+    const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
     if (a.tile >= 0 && kTiles[a.tile].dtype_class != dclass) return GEMM355_EINVAL;

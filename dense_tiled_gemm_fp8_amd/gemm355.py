@@ -24,7 +24,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 # status codes
 OK, EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP = range(6)
 # dtypes (input -> output)
-BF16_F32, BF16_BF16, E4M3_F32, E4M3_BF16 = range(4)
+(BF16_F32, BF16_BF16, E4M3_F32, E4M3_BF16, E5M2_F32, E5M2_BF16, E4M3_E5M2_F32,
+ E4M3_E5M2_BF16) = range(8)
+# 8-bit formats and source types of the quantiser
+FP8_E4M3, FP8_E5M2 = range(2)
+SRC_F32, SRC_BF16 = range(2)
 # layouts
 A_ROW_B_COL, A_ROW_B_ROW, A_COL_B_COL, A_COL_B_ROW = range(4)
 
@@ -84,12 +88,15 @@ _lib.gemm355_tile_info.restype = ctypes.c_int
 _lib.gemm355_tile_info.argtypes = [_i32] + [ctypes.POINTER(_i32)] * 8
 _lib.gemm355_tile_occupancy.restype = ctypes.c_int
 _lib.gemm355_tile_occupancy.argtypes = [_i32, ctypes.POINTER(_i32)]
+_lib.gemm355_quantize.restype = ctypes.c_int
+_lib.gemm355_quantize.argtypes = [_vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]
 _lib.gemm355_status_string.restype = ctypes.c_char_p
 _lib.gemm355_status_string.argtypes = [ctypes.c_int]
 
 EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_plan", "gemm355_eta_wave",
             "gemm355_eta_pad", "gemm355_kslice", "gemm355_unit", "gemm355_num_tiles",
-            "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_status_string")
+            "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_quantize",
+            "gemm355_status_string")
 
 
 class Gemm355Error(RuntimeError):
@@ -196,3 +203,10 @@ def gemm355_tile_occupancy(tile: int) -> int:
     n = _i32()
     _check(_lib.gemm355_tile_occupancy(tile, ctypes.byref(n)), "gemm355_tile_occupancy")
     return n.value
+
+
+def gemm355_quantize(x, n, batch, src, fmt, q, scale, stream=None) -> None:
+    """Per-tensor scaling of `batch` tensors of n elements to 8-bit codes q,
+    dequantisation factors into scale[batch] (device pointers or tensors)."""
+    _check(_lib.gemm355_quantize(_ptr(x), n, batch, src, fmt, _ptr(q), _ptr(scale), _stream(stream)),
+           "gemm355_quantize")

@@ -25,6 +25,8 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+_TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 
 def seed_for(workload: int, shape_index: int, operand: int) -> int:
@@ -55,37 +57,46 @@ def to_bf16_codes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def to_e4m3_codes(x: np.ndarray, scale: Optional[float] = None) -> Tuple[np.ndarray, float]:
-    """Per-tensor quantisation to OCP E4M3FN.  In binary32: s = amax|x|/448
-    (unless given), q = e4m3_rne(clamp(x/s, -448, 448)).  Returns (uint8
-    codes, s); x is approximately s * decode(q)."""
+def to_fp8_codes(x: np.ndarray, fmt: str, scale: Optional[float] = None) -> Tuple[np.ndarray, float]:
+    """Per-tensor quantisation to OCP E4M3FN or E5M2 (the input recipe).  In
+    binary32: s = amax|x|/F (unless given; F = 448 or 57344),
+    q = rne(clamp(x/s, -F, F)) by torch's CPU cast.  Returns (uint8 codes,
+    s); x is approximately s * decode(q)."""
+    F = FP8_MAX[fmt]
     x32 = np.ascontiguousarray(x, dtype=np.float32)
     if scale is None:
         amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
-        scale = float(np.float32(amax) / np.float32(E4M3_MAX)) if amax > 0 else 1.0
+        scale = float(np.float32(amax) / np.float32(F)) if amax > 0 else 1.0
     s32 = np.float32(scale)
-    y = np.clip(x32 / s32, -E4M3_MAX, E4M3_MAX).astype(np.float32)
-    q = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    y = np.clip(x32 / s32, -F, F).astype(np.float32)
+    q = torch.from_numpy(y).to(_TORCH_FP8[fmt]).view(torch.uint8).numpy()
     return q, float(s32)
+
+
+def to_e4m3_codes(x: np.ndarray, scale: Optional[float] = None) -> Tuple[np.ndarray, float]:
+    """to_fp8_codes for E4M3FN."""
+    return to_fp8_codes(x, "e4m3", scale)
 
 
 def small_int_codes(gen: np.random.Generator, shape, fmt: str, lo: int = -4,
                     hi: int = 4) -> np.ndarray:
-    """Integers in [lo, hi], exactly representable in bf16 and E4M3."""
+    """Integers in [lo, hi], exactly representable in bf16, E4M3 and E5M2
+    (fmt "e5m2" gives E5M2 codes, any other 8-bit name E4M3 codes)."""
     v = gen.integers(lo, hi + 1, size=shape).astype(np.float64)
     if fmt == "bf16":
         return to_bf16_codes(v)
-    q, _ = to_e4m3_codes(v, scale=1.0)
+    q, _ = to_fp8_codes(v, "e5m2" if fmt == "e5m2" else "e4m3", scale=1.0)
     return q
 
 
-def codes_to_torch(codes: np.ndarray) -> torch.Tensor:
-    """View raw codes as a torch tensor of the matching element type."""
+def codes_to_torch(codes: np.ndarray, fmt: Optional[str] = None) -> torch.Tensor:
+    """View raw codes as a torch tensor of the matching element type (uint8
+    codes are E4M3 unless fmt is "e5m2")."""
     if codes.dtype == np.uint16:
         return torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16)
     if codes.dtype == np.uint8:
-        return torch.from_numpy(codes).view(torch.float8_e4m3fn)
-    raise TypeError("codes must be uint16 (bf16) or uint8 (E4M3)")
+        return torch.from_numpy(codes).view(_TORCH_FP8["e5m2" if fmt == "e5m2" else "e4m3"])
+    raise TypeError("codes must be uint16 (bf16) or uint8 (E4M3 / E5M2)")
 
 
 def sha256(*arrays: np.ndarray) -> str:
@@ -101,7 +112,7 @@ class Operands:
     M: int
     N: int
     K: int
-    fmt: str                      # "bf16" or "e4m3"
+    fmt: str                      # "bf16", "e4m3", "e5m2" or "e4m3e5m2" (A E4M3, B E5M2)
     A: np.ndarray                 # (batch, M, K) or (M, K)
     B: np.ndarray                 # (batch, N, K) or (N, K)  (column-major B)
     scale_a: List[float] = field(default_factory=list)
@@ -111,6 +122,14 @@ class Operands:
     @property
     def batch(self) -> int:
         return self.A.shape[0] if self.A.ndim == 3 else 1
+
+    @property
+    def fmt_a(self) -> str:
+        return "e4m3" if self.fmt == "e4m3e5m2" else self.fmt
+
+    @property
+    def fmt_b(self) -> str:
+        return "e5m2" if self.fmt == "e4m3e5m2" else self.fmt
 
 
 def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
@@ -128,9 +147,9 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
             Bs.append(to_bf16_codes(xb))
             sa.append(1.0)
             sb.append(1.0)
-        elif fmt == "e4m3":
-            qa, s_a = to_e4m3_codes(xa)
-            qb, s_b = to_e4m3_codes(xb)
+        elif fmt in ("e4m3", "e5m2", "e4m3e5m2"):
+            qa, s_a = to_fp8_codes(xa, "e4m3" if fmt != "e5m2" else "e5m2")
+            qb, s_b = to_fp8_codes(xb, "e5m2" if fmt != "e4m3" else "e4m3")
             As.append(qa)
             Bs.append(qb)
             sa.append(s_a)

@@ -50,14 +50,34 @@ typedef enum gemm355_status {
                                   launch failure) */
 } gemm355_status;
 
-/* Element types, input -> output. */
+/* Element types, input -> output.  The two 8-bit formats are the FP8 pair
+ * of the Hopper row of the input/accumulate table (page "The Tensor Core"):
+ * OCP E4M3FN (bias 7, max 448, no infinities, NaN 0x7F/0xFF) and OCP E5M2
+ * (bias 15, max 57344, infinities 0x7C/0xFC, NaN above them).  Operands
+ * must be finite. */
 typedef enum gemm355_dtype {
     GEMM355_BF16_F32 = 0,   /* bf16 A, B; fp32 C                              */
     GEMM355_BF16_BF16 = 1,  /* bf16 A, B; bf16 C (fp32 result rounded to
                                nearest even)                                  */
-    GEMM355_E4M3_F32 = 2,   /* OCP E4M3FN A, B (max 448, no infinities); fp32 C */
-    GEMM355_E4M3_BF16 = 3   /* OCP E4M3FN A, B; bf16 C                        */
+    GEMM355_E4M3_F32 = 2,   /* E4M3 A, B; fp32 C                              */
+    GEMM355_E4M3_BF16 = 3,  /* E4M3 A, B; bf16 C                              */
+    GEMM355_E5M2_F32 = 4,   /* E5M2 A, B; fp32 C                              */
+    GEMM355_E5M2_BF16 = 5,  /* E5M2 A, B; bf16 C                              */
+    GEMM355_E4M3_E5M2_F32 = 6,  /* E4M3 A, E5M2 B; fp32 C                     */
+    GEMM355_E4M3_E5M2_BF16 = 7  /* E4M3 A, E5M2 B; bf16 C                     */
 } gemm355_dtype;
+
+/* 8-bit formats of the quantiser. */
+typedef enum gemm355_fp8 {
+    GEMM355_FP8_E4M3 = 0,   /* OCP E4M3FN, largest finite 448                 */
+    GEMM355_FP8_E5M2 = 1    /* OCP E5M2, largest finite 57344                 */
+} gemm355_fp8;
+
+/* Source element types of the quantiser. */
+typedef enum gemm355_src {
+    GEMM355_SRC_F32 = 0,
+    GEMM355_SRC_BF16 = 1
+} gemm355_src;
 
 /* Operand storage (the row/column vocabulary of the sweep command in
  * section "Practical shape sweep"):
@@ -210,7 +230,7 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
                             int64_t *kt_begin, int64_t *kt_end);
 
 /* Number of entries in the tile table, and one entry's parameters.
- * dtype_class: 0 = bf16 inputs, 1 = E4M3 inputs. */
+ * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2). */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
                                  int32_t *T_M, int32_t *T_N, int32_t *T_K,
@@ -223,6 +243,33 @@ GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
  * size: 64 threads per wavefront).  Needs a
  * device; EHIP otherwise. */
 GEMM355_API gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu);
+
+/*
+ * gemm355_quantize -- per-tensor scaling of `batch` tensors of n elements each
+ * to an 8-bit format, on the device (page "10. Tensor Cores, ...", section
+ * "Practical shape sweep": a GEMM must be judged with its quantisation
+ * overhead included).  For tensor g (elements x[g*n .. g*n + n - 1]):
+ *     amax  = max_i |x_i|                       (exact)
+ *     s     = amax / F  in fp32, rounded to nearest (s = 1 if amax == 0),
+ *             F = 448 (E4M3) or 57344 (E5M2)
+ *     q_i   = the format's code nearest to min(max(x_i / s, -F), F), the
+ *             quotient x_i / s rounded to nearest in fp32 first; ties go to
+ *             the code with an even mantissa
+ * so that x_i ~ s * dec(q_i): s is the dequantisation factor to pass as
+ * scale_a or scale_b of gemm355_gemm_ex.
+ *   x:     device, batch*n elements of `src` (fp32 or bf16), finite.
+ *   q:     device, batch*n bytes (codes of `fmt`), written.
+ *   scale: device fp32 [batch], written (s of each tensor).
+ *   n >= 0, batch >= 1; n == 0 writes scale[g] = 1 and nothing else.
+ * Two kernels on `stream`: per-block maxima into library-owned scratch, then
+ * each block reduces its tensor's maxima (max is exact in any order), forms
+ * s and quantises its share.  x may not overlap q or scale (EINVAL).
+ * Errors: EINVAL (sizes, enums, null pointers, overlap), EALIGN (x not
+ * aligned to its element size, scale not 4-byte aligned), EUNSUPPORTED
+ * (n * batch >= 2^40), ENOMEM, EHIP.
+ */
+GEMM355_API gemm355_status gemm355_quantize(const void *x, int64_t n, int64_t batch, gemm355_src src,
+                                gemm355_fp8 fmt, void *q, float *scale, void *stream);
 
 /* Static description of a status code. */
 GEMM355_API const char *gemm355_status_string(gemm355_status status);

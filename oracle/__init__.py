@@ -5,11 +5,14 @@ executes anything in this package.  Only the test suite, the smoke check and
 the benchmark's CPU-baseline leg use it.  It shares no code with the GPU path
 and does not import the product package.
 
-Two parts:
+Three parts:
 
 * ``gemm_oracle.c`` (wrapped by :mod:`oracle.reference`): the plain binary64
   triple-loop product C = alpha * A @ B, plus the magnitude W = |alpha| *
-  sum_k |a_ik b_kj|.  It decodes bf16 and E4M3 from their bit definitions.
+  sum_k |a_ik b_kj|.  It decodes bf16, E4M3 and E5M2 from their bit
+  definitions (A and B may use different 8-bit formats).
+* :mod:`oracle.quant`: per-tensor quantisation to E4M3 / E5M2 (amax, scale,
+  nearest code with ties to even) by search over the decoded code table.
 * :mod:`oracle.bookkeeping`: exact-rational tile bookkeeping: the FLOP count,
   the tile grid G, wave efficiency, padding efficiency, K-slices, resident
   workgroups and schedule efficiency.

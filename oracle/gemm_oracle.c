@@ -26,8 +26,13 @@
  *   E4M3  : the OCP 8-bit float "E4M3FN": 1 sign, 4 exponent (bias 7) and
  *           3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6);
  *           S.1111.111 is NaN; there is no infinity; the largest finite
- *           magnitude is 1.75 * 2^8 = 448.  The low-precision input table on
- *           page "The Tensor Core" lists this format as the Hopper-row input.
+ *           magnitude is 1.75 * 2^8 = 448.
+ *   E5M2  : the OCP 8-bit float "E5M2": 1 sign, 5 exponent (bias 15) and
+ *           2 mantissa bits; exponent field 0 is subnormal (m/4 * 2^-14);
+ *           exponent field 31 is infinity (m = 0) or NaN; the largest finite
+ *           magnitude is 1.75 * 2^15 = 57344.
+ *   The low-precision input table on page "The Tensor Core" lists E4M3 and
+ *   E5M2 as the Hopper-row FP8 inputs.  A and B may use different formats.
  *
  * Operand addressing (leading dimensions as in that page's WMMA example):
  *   a_colmajor = 0 : a(i,k) = A[i*lda + k]   (A row-major, M rows of K)
@@ -44,7 +49,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_BF16 = 0, ORACLE_E4M3 = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_E4M3 = 1, ORACLE_E5M2 = 2 };
 
 static double decode_bf16(uint16_t code)
 {
@@ -69,10 +74,27 @@ static double decode_e4m3(uint8_t code)
     return sign ? -mag : mag;
 }
 
+static double decode_e5m2(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 2) & 0x1F;
+    int m = code & 0x3;
+    double mag;
+    if (e == 0x1F)
+        mag = m == 0 ? INFINITY : NAN;
+    else if (e == 0)
+        mag = ldexp((double)m, -16);           /* (m/4) * 2^(1-15) */
+    else
+        mag = ldexp(4.0 + (double)m, e - 17);  /* (1 + m/4) * 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
 static double decode(const void *base, int64_t idx, int fmt)
 {
     if (fmt == ORACLE_BF16)
         return decode_bf16(((const uint16_t *)base)[idx]);
+    if (fmt == ORACLE_E5M2)
+        return decode_e5m2(((const uint8_t *)base)[idx]);
     return decode_e4m3(((const uint8_t *)base)[idx]);
 }
 
@@ -102,7 +124,7 @@ int oracle_threads(void)
 int64_t oracle_gemm(int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, int a_colmajor,
                     const void *B, int64_t ldb, int b_rowmajor,
-                    int fmt, double alpha, double *C, double *W)
+                    int fmt_a, int fmt_b, double alpha, double *C, double *W)
 {
     int64_t i, j, k, macs = 0;
     double *a = NULL, *b = NULL;
@@ -115,10 +137,10 @@ int64_t oracle_gemm(int64_t M, int64_t N, int64_t K,
     /* decode once: a as dense M x K, b as dense K x N (both row-major) */
     for (i = 0; i < M; ++i)
         for (k = 0; k < K; ++k)
-            a[i * K + k] = decode(A, a_index(i, k, lda, a_colmajor), fmt);
+            a[i * K + k] = decode(A, a_index(i, k, lda, a_colmajor), fmt_a);
     for (k = 0; k < K; ++k)
         for (j = 0; j < N; ++j)
-            b[k * N + j] = decode(B, b_index(k, j, ldb, b_rowmajor), fmt);
+            b[k * N + j] = decode(B, b_index(k, j, ldb, b_rowmajor), fmt_b);
 
 #pragma omp parallel for schedule(static) private(j, k) reduction(+ : macs)
     for (i = 0; i < M; ++i) {
@@ -156,7 +178,7 @@ int64_t oracle_gemm(int64_t M, int64_t N, int64_t K,
 int64_t oracle_gemm_entries(int64_t K,
                             const void *A, int64_t lda, int a_colmajor,
                             const void *B, int64_t ldb, int b_rowmajor,
-                            int fmt, double alpha,
+                            int fmt_a, int fmt_b, double alpha,
                             int64_t n, const int64_t *ii, const int64_t *jj,
                             double *c, double *w)
 {
@@ -166,8 +188,8 @@ int64_t oracle_gemm_entries(int64_t K,
         double s = 0.0, sa = 0.0;
         int64_t k;
         for (k = 0; k < K; ++k) {
-            const double p = decode(A, a_index(ii[t], k, lda, a_colmajor), fmt) *
-                             decode(B, b_index(k, jj[t], ldb, b_rowmajor), fmt);
+            const double p = decode(A, a_index(ii[t], k, lda, a_colmajor), fmt_a) *
+                             decode(B, b_index(k, jj[t], ldb, b_rowmajor), fmt_b);
             s += p;
             sa += fabs(p);
         }
@@ -181,3 +203,4 @@ int64_t oracle_gemm_entries(int64_t K,
 /* Element decoders exposed for the codec pins. */
 double oracle_decode_bf16(uint16_t code) { return decode_bf16(code); }
 double oracle_decode_e4m3(uint8_t code) { return decode_e4m3(code); }
+double oracle_decode_e5m2(uint8_t code) { return decode_e5m2(code); }

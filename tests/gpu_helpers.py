@@ -2,8 +2,8 @@
 call libgemm355 through its C ABI, bring C back, compare with the oracle.
 
 Tolerances (per element, W = |alpha| sum_k |a_ik b_kj| from the oracle):
-  bf16 inputs:  |C_gpu - C_ref| <= 1e-3 W + 1e-6
-  E4M3 inputs:  |C_gpu - C_ref| <= 2e-2 W
+  bf16 inputs:             |C_gpu - C_ref| <= 1e-3 W + 1e-6
+  8-bit (E4M3, E5M2) inputs: |C_gpu - C_ref| <= 2e-2 W
 """
 from __future__ import annotations
 
@@ -16,7 +16,7 @@ from dense_tiled_gemm_fp8_amd import gemm355 as g
 from dense_tiled_gemm_fp8_amd import inputs
 from oracle import reference as oracle
 
-TOL = {"bf16": (1e-3, 1e-6), "e4m3": (2e-2, 0.0)}
+TOL = {"bf16": (1e-3, 1e-6), "e4m3": (2e-2, 0.0), "e5m2": (2e-2, 0.0), "e4m3e5m2": (2e-2, 0.0)}
 
 
 def say(*a):
@@ -35,9 +35,9 @@ def dev(codes: np.ndarray) -> torch.Tensor:
 
 
 def out_dtype(fmt: str, out: str) -> int:
-    if fmt == "bf16":
-        return g.BF16_BF16 if out == "bf16" else g.BF16_F32
-    return g.E4M3_BF16 if out == "bf16" else g.E4M3_F32
+    table = {"bf16": (g.BF16_F32, g.BF16_BF16), "e4m3": (g.E4M3_F32, g.E4M3_BF16),
+             "e5m2": (g.E5M2_F32, g.E5M2_BF16), "e4m3e5m2": (g.E4M3_E5M2_F32, g.E4M3_E5M2_BF16)}
+    return table[fmt][1 if out == "bf16" else 0]
 
 
 def empty_c(batch: int, M: int, N: int, out: str, fill: float = float("nan")) -> torch.Tensor:
@@ -57,7 +57,7 @@ def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: in
     if C is None:
         C = empty_c(batch, M, N, out)
     sa = sb = None
-    if scales and ops.fmt == "e4m3":
+    if scales and ops.fmt != "bf16":
         sa = torch.tensor(ops.scale_a, dtype=torch.float32, device="cuda")
         sb = torch.tensor(ops.scale_b, dtype=torch.float32, device="cuda")
     ws = None
@@ -76,7 +76,7 @@ def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: in
 
 
 def alpha_of(ops: inputs.Operands, bi: int = 0) -> float:
-    if ops.fmt == "e4m3":
+    if ops.fmt != "bf16":
         return float(np.float32(ops.scale_a[bi]) * np.float32(ops.scale_b[bi]))
     return 1.0
 
@@ -86,14 +86,22 @@ def oracle_full(ops: inputs.Operands, bi: int = 0, alpha=None):
     B = ops.B[bi] if ops.B.ndim == 3 else ops.B
     if alpha is None:
         alpha = alpha_of(ops, bi)
-    return oracle.gemm(ops.M, ops.N, ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, alpha=alpha)
+    return oracle.gemm(ops.M, ops.N, ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, alpha=alpha,
+                       **fmt_kw(ops))
 
 
 def oracle_entries(ops: inputs.Operands, rows, cols, bi: int = 0):
     A = ops.A[bi] if ops.A.ndim == 3 else ops.A
     B = ops.B[bi] if ops.B.ndim == 3 else ops.B
     return oracle.gemm_entries(ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, rows, cols,
-                               alpha=alpha_of(ops, bi))
+                               alpha=alpha_of(ops, bi), **fmt_kw(ops))
+
+
+def fmt_kw(ops: inputs.Operands):
+    """The oracle's format arguments for the operands' codes."""
+    if ops.fmt == "bf16":
+        return {}
+    return {"fmt_a": ops.fmt_a, "fmt_b": ops.fmt_b}
 
 
 def check(C_gpu: np.ndarray, C_ref: np.ndarray, W: np.ndarray, fmt: str, what: str = ""):

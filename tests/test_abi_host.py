@@ -86,6 +86,7 @@ PLAN_SHAPES = [
     (4097, 4095, 4104, 1, 0), (1000, 3000, 777, 1, 0), (256, 256, 65536, 1, 0),
     (128, 512, 131072, 1, 0), (64, 64, 262144, 1, 0), (8192, 8192, 8192, 1, 2),
     (512, 1024, 4096, 64, 2), (1, 1, 1, 1, 0), (17, 300, 40, 3, 2), (5000, 33, 9000, 1, 0),
+    (1000, 900, 700, 1, 3), (64, 4096, 8192, 2, 4),
 ]
 
 KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1, persistent=1),
@@ -93,7 +94,7 @@ KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1,
 
 
 def _plan_and_check(g, M, N, K, batch, dtype, knobs):
-    if "tile" in knobs and dtype == g.E4M3_F32:
+    if "tile" in knobs and dtype in (g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16):
         knobs = dict(knobs, tile=knobs["tile"] + 3)
     a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, dtype=dtype,
                     batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N, cus=256, **knobs)
@@ -135,14 +136,14 @@ def _plan_and_check(g, M, N, K, batch, dtype, knobs):
 
 @pytest.mark.parametrize("M,N,K,batch,dt", PLAN_SHAPES)
 def test_plan_bookkeeping(g, M, N, K, batch, dt):
-    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32][dt]
+    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16][dt]
     for knobs in KNOBS:
         _plan_and_check(g, M, N, K, batch, dtype, knobs)
 
 
 @pytest.mark.parametrize("M,N,K,batch,dt", [s for s in PLAN_SHAPES if s[0] * s[1] * s[3] <= 5000 * 5000])
 def test_units_cover_every_k_tile_once(g, M, N, K, batch, dt):
-    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32][dt]
+    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16][dt]
     for knobs in KNOBS:
         a, p = _plan_and_check(g, M, N, K, batch, dtype, knobs)
         if p["units"] > 20000:
@@ -225,7 +226,7 @@ def test_argument_errors(g):
     assert status(unit_stamps=0x300000000004) == g.EALIGN  # stamps need 8-byte alignment
     assert status(C=0x200000000002) == g.EALIGN            # fp32 C
     assert status(scale_a=0x3001) == g.EALIGN
-    assert status(dtype=7) == g.EINVAL
+    assert status(dtype=8) == g.EINVAL
     assert status(layout=9) == g.EINVAL
     assert status(tile=99) == g.EINVAL
     assert status(tile=3) == g.EINVAL                      # E4M3 tile for bf16 inputs
@@ -242,6 +243,34 @@ def test_argument_errors(g):
     assert status(M=0) == g.OK
     assert status(N=0, C=None) == g.OK
     assert g.gemm355_status_string(g.ENOMEM).startswith("workspace")
+
+
+def test_quantize_argument_errors(g):
+    """Argument checks of the quantiser run before anything touches a device."""
+    X, Q, S = 0x10000, 0x1000000000, 0x200000000000
+
+    def status(**kw):
+        a = dict(x=X, n=1024, batch=1, src=g.SRC_F32, fmt=g.FP8_E4M3, q=Q, scale=S)
+        a.update(kw)
+        try:
+            g.gemm355_quantize(a["x"], a["n"], a["batch"], a["src"], a["fmt"], a["q"], a["scale"], stream=0)
+            return g.OK
+        except g.Gemm355Error as e:
+            return e.status
+
+    assert status(n=-1) == g.EINVAL
+    assert status(batch=0) == g.EINVAL
+    assert status(src=2) == g.EINVAL
+    assert status(fmt=5) == g.EINVAL
+    assert status(scale=None) == g.EINVAL
+    assert status(x=None) == g.EINVAL
+    assert status(q=None) == g.EINVAL
+    assert status(scale=S + 2) == g.EALIGN
+    assert status(x=X + 2) == g.EALIGN                       # fp32 input
+    assert status(q=X + 100) == g.EINVAL                     # codes overlap the input
+    assert status(scale=X + 64) == g.EINVAL                  # scales overlap the input
+    assert status(n=1 << 40) == g.EUNSUPPORTED
+    assert status(n=1 << 20, batch=1 << 21) == g.EUNSUPPORTED
 
 
 def test_tile_table(g):
@@ -262,20 +291,30 @@ def test_tile_table(g):
 
 def test_main_loop_uses_mfma(g, tmp_path):
     """The compiler emitted the matrix-core instruction family for every
-    main-loop instantiation (bf16 and E4M3), not a scalar fallback."""
+    main-loop instantiation (bf16 and each 8-bit format pair), not a scalar
+    fallback, with the operand-format fields of the pair."""
     from dense_tiled_gemm_fp8_amd import build
     asm = open(build.device_asm("kernels.hip")).read()
     bodies = re.split(r"\n(?=_ZN4g35516gemm_tile_kernel\w+:)", asm)
     kernels = [b for b in bodies if re.match(r"_ZN4g35516gemm_tile_kernel\w+:", b)]
-    assert len(kernels) == g.gemm355_num_tiles()
+    n8 = sum(g.gemm355_tile_info(t)["dtype_class"] for t in range(g.gemm355_num_tiles()))
+    assert len(kernels) == g.gemm355_num_tiles() + 2 * n8      # three format pairs per 8-bit tile
     for body in kernels:
         name = body.split(":")[0]
         fp8 = "Lb1E" in name
-        mi = int(re.findall(r"ELi(\d+)E", name)[-1])      # last template argument: MFMA block edge
+        targs = [int(v) for v in re.findall(r"Li(\d+)E", name)]
+        mi, fmt = targs[-2], targs[-1]                      # MFMA block edge, format pair
         want = {(True, 32): "v_mfma_f32_32x32x64_f8f6f4", (False, 32): "v_mfma_f32_32x32x16_bf16",
                 (True, 16): "v_mfma_f32_16x16x128_f8f6f4", (False, 16): "v_mfma_f32_16x16x32_bf16"}[(fp8, mi)]
-        assert want in body, name
-        assert "v_fma_f32" not in body.split("s_endpgm")[0] or want in body
+        code = body.split("s_endpgm")[0]
+        lines = [l for l in code.splitlines() if want in l]
+        assert lines, name
+        if fp8:
+            # E4M3 is format 0 (no modifier printed), E5M2 format 1
+            assert all(("cbsz:1" in l) == (fmt == 1) for l in lines), name
+            assert all(("blgp:1" in l) == (fmt >= 1) for l in lines), name
+        else:
+            assert fmt == 0
 
 
 def test_struct_layout_matches_header(g, tmp_path):

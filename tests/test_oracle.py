@@ -31,10 +31,11 @@ from dense_tiled_gemm_fp8_amd import inputs
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]  # (a_colmajor, b_rowmajor)
 
 
-def lib_decode(codes):
-    """Decode with torch's CPU casts (independent of the oracle's decoder)."""
+def lib_decode(codes, fmt=None):
+    """Decode with torch's CPU casts (independent of the oracle's decoder);
+    uint8 codes are E4M3 unless fmt is "e5m2"."""
     codes = np.ascontiguousarray(codes)
-    return inputs.codes_to_torch(codes).to(torch.float64).numpy()
+    return inputs.codes_to_torch(codes, fmt).to(torch.float64).numpy()
 
 
 def store(a_log, b_log, a_colmajor, b_rowmajor):
@@ -57,7 +58,7 @@ def rand_codes(gen, shape, fmt):
     x = gen.uniform(-1, 1, size=shape)
     if fmt == "bf16":
         return inputs.to_bf16_codes(x)
-    return inputs.to_e4m3_codes(x)[0]
+    return inputs.to_fp8_codes(x, fmt)[0]
 
 
 # ---------------------------------------------------------------- codecs
@@ -128,6 +129,25 @@ def test_matches_numpy_float64(oracle_lib, fmt, layout, M, N, K):
     assert np.all(np.abs(C - ref) <= 1e-12 * wref + 1e-300)
     assert np.allclose(W, wref, rtol=1e-12, atol=0)
     assert np.all(np.abs(C) <= W * (1 + 1e-15))
+
+
+@pytest.mark.parametrize("fa,fb", [("e5m2", "e5m2"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_matches_numpy_float64_e5m2(oracle_lib, fa, fb, layout):
+    M, N, K = 33, 47, 150
+    g = inputs.rng(hash((fa, fb, layout)) & 0xFFFF)
+    a, b = rand_codes(g, (M, K), fa), rand_codes(g, (K, N), fb)
+    A, lda, B, ldb = store(a, b, *layout)
+    C, W = oracle_lib.gemm(M, N, K, A, lda, B, ldb, a_colmajor=layout[0], b_rowmajor=layout[1],
+                           alpha=-0.75, fmt_a=fa, fmt_b=fb)
+    ad, bd = lib_decode(a, fa), lib_decode(b, fb)
+    ref = -0.75 * (ad @ bd)
+    wref = 0.75 * (np.abs(ad) @ np.abs(bd))
+    assert np.all(np.abs(C - ref) <= 1e-12 * wref + 1e-300)
+    assert np.allclose(W, wref, rtol=1e-12, atol=0)
+    c, w = oracle_lib.gemm_entries(K, A, lda, B, ldb, np.arange(M), np.arange(M) % N, *layout, alpha=-0.75,
+                                   fmt_a=fa, fmt_b=fb)
+    assert np.array_equal(c, C[np.arange(M), np.arange(M) % N])
 
 
 def test_entries_equal_full(oracle_lib):
@@ -312,6 +332,10 @@ MUTANTS = {
     "transposed_b": ("return b_rowmajor ? k * ldb + j : j * ldb + k;", "return b_rowmajor ? j * ldb + k : k * ldb + j;"),
     "e4m3_bias": ("ldexp(8.0 + (double)m, e - 10)", "ldexp(8.0 + (double)m, e - 11)"),
     "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e5m2_bias": ("ldexp(4.0 + (double)m, e - 17)", "ldexp(4.0 + (double)m, e - 16)"),
+    "e5m2_subnormal": ("ldexp((double)m, -16)", "ldexp((double)m, -15)"),
+    "b_format_ignored": ("b[k * N + j] = decode(B, b_index(k, j, ldb, b_rowmajor), fmt_b);",
+                         "b[k * N + j] = decode(B, b_index(k, j, ldb, b_rowmajor), fmt_a);"),
     "no_alpha": ("c[j] *= alpha;", "c[j] *= 1.0;"),
 }
 
@@ -334,14 +358,18 @@ def _pins_pass(lib_path):
         ref8 = lib_decode(codes8)
         got8 = r.decode_e4m3(codes8)
         ok = np.array_equal(np.nan_to_num(got8, nan=7.0), np.nan_to_num(ref8, nan=7.0))
+        ref5 = lib_decode(codes8, "e5m2")
+        got5 = r.decode_e5m2(codes8)
+        ok &= np.array_equal(np.nan_to_num(got5, nan=7.0), np.nan_to_num(ref5, nan=7.0))
         g = inputs.rng(29)
-        for fmt in ("bf16", "e4m3"):
+        for fa, fb in (("bf16", "bf16"), ("e4m3", "e4m3"), ("e4m3", "e5m2")):
             M, N, K = 9, 11, 37
-            a, b = rand_codes(g, (M, K), fmt), rand_codes(g, (K, N), fmt)
-            ad, bd = lib_decode(a), lib_decode(b)
+            a, b = rand_codes(g, (M, K), fa), rand_codes(g, (K, N), fb)
+            ad, bd = lib_decode(a, fa), lib_decode(b, fb)
             for layout in LAYOUTS:
                 A, lda, B, ldb = store(a, b, *layout)
-                C, W = r.gemm(M, N, K, A, lda, B, ldb, *layout, alpha=0.5)
+                C, W = r.gemm(M, N, K, A, lda, B, ldb, *layout, alpha=0.5,
+                              fmt_a=None if fa == "bf16" else fa, fmt_b=None if fb == "bf16" else fb)
                 ref = 0.5 * (ad @ bd)
                 wref = 0.5 * (np.abs(ad) @ np.abs(bd))
                 ok &= bool(np.all(np.abs(C - ref) <= 1e-12 * wref))
