@@ -266,6 +266,77 @@ def sustain(case, torch, seconds):
             "sustained_tflops": round(case.flops / us / 1e6, 1), "smi": smi or None}
 
 
+class _Steps:
+    """A callable sequence of launches timed as one step by time_case."""
+
+    def __init__(self, fn, flops):
+        self.fn, self.flops = fn, flops
+
+    def step(self, stream):
+        self.fn(stream)
+
+
+def fp8_end_to_end(torch, g, inputs, args):
+    """8192^3 products whose operands start as bf16 N(0,1) matrices on the
+    device: per-tensor quantisation of A and B on the device (the library's
+    quantiser) followed by the 8-bit product with the device scales, timed
+    as one step and its parts separately; for E4M3 and for E5M2."""
+    import numpy as np
+    M = N = K = 8192
+    log("bench: detail fp8 end to end", (M, N, K))
+    xs = []
+    for operand in (0, 1):
+        x = inputs.draw(inputs.rng(inputs.seed_for(5, 0, operand)), (M, K), "normal")
+        xs.append(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda())
+        del x
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty(1, dtype=torch.float32, device="cuda")
+    sb = torch.empty(1, dtype=torch.float32, device="cuda")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    flops = 2.0 * M * N * K
+    out = []
+    for fmt, fq, dt in (("e4m3", g.FP8_E4M3, g.E4M3_F32), ("e5m2", g.FP8_E5M2, g.E5M2_F32)):
+        a = g.make_args(M, N, K, A=qa, B=qb, C=C, dtype=dt, scale_a=sa, scale_b=sb)
+        p = g.gemm355_plan(a)
+
+        def quant(sp, fq=fq):
+            g.gemm355_quantize(xs[0], M * K, 1, g.SRC_BF16, fq, qa, sa, sp)
+            g.gemm355_quantize(xs[1], N * K, 1, g.SRC_BF16, fq, qb, sb, sp)
+
+        def gemm(sp, a=a):
+            g.gemm355_gemm_ex(a, sp)
+
+        def both(sp):
+            quant(sp)
+            gemm(sp)
+
+        times = {}
+        for name, fn in (("quantize", quant), ("gemm", gemm), ("step", both)):
+            c = _Steps(fn, flops)
+            n = max(10, args.steps // 10)
+            _, ev = time_case(c, torch, n, max(3, args.warmup // 10), args.settle / 4)
+            times[name] = ev / n
+        out.append({
+            "workload": "%s end to end 8192x8192x8192 (bf16 N(0,1) operands quantised on the device, "
+                        "then the product, fp32 C)" % fmt,
+            "dtype": fmt, "out": "f32",
+            "us_median": round(times["step"] * 1e6, 2),
+            "us_gemm": round(times["gemm"] * 1e6, 2),
+            "us_quantize_a_and_b": round(times["quantize"] * 1e6, 2),
+            "quantize_share": round(times["quantize"] / times["step"], 4),
+            "tflops": round(flops / times["step"] / 1e12, 1),
+            "tflops_gemm_only": round(flops / times["gemm"] / 1e12, 1),
+            "pct_mfma_peak": round(100 * flops / times["step"] / 1e12 / PEAK_TFLOPS["e4m3"], 1),
+            # quantiser bytes: read bf16 A and B twice (amax, then quantise), write the codes
+            "quantize_hbm_gbs": round((2 * 2 * (M + N) * K + (M + N) * K) / times["quantize"] / 1e9, 1),
+            "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"],
+        })
+    del xs
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(torch, budget_s=15.0):
     """The oracle (as it stands) on a bounded sample of the headline product:
     the first R rows of A against all of B, R sized from a short probe to
@@ -393,6 +464,9 @@ def main():
                 if c is not head:
                     del c
                     torch.cuda.empty_cache()
+
+    if not args.no_detail and (args.workload in (None, "fp8-end-to-end")):
+        detail.extend(fp8_end_to_end(torch, g, inputs, args))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -433,7 +433,8 @@ gemm355_status gemm355_quantize(const void *x, int64_t n, int64_t batch, gemm355
     if (n > 0 && ((uintptr_t)x % (uintptr_t)es) != 0) return GEMM355_EALIGN;
     if (n > 0 && (n >= ((int64_t)1 << 40) || batch >= ((int64_t)1 << 40) / n)) return GEMM355_EUNSUPPORTED;
     const int64_t total = n * batch;
-    const int32_t parts = (int32_t)std::min<int64_t>(1024, std::max<int64_t>(1, (n + 8191) / 8192));
+    /* blocks per tensor: one per 16 Ki elements, at most 4096 */
+    const int32_t parts = (int32_t)std::min<int64_t>(4096, std::max<int64_t>(1, (n + 16383) / 16384));
     if (batch * parts > ((int64_t)1 << 30)) return GEMM355_EUNSUPPORTED;
     /* no overlap between the input, the codes and the scales */
     auto overlap = [](uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; };

@@ -58,7 +58,7 @@ struct QuantParams {
     float *scale;                 /* [batch] dequantisation factors         */
     float *maxima;                /* scratch [batch * parts]                */
     int64_t n, batch;
-    int32_t parts;                /* blocks per tensor (1 .. 1024)          */
+    int32_t parts;                /* blocks per tensor (1 .. 4096)          */
     int32_t src;                  /* 0 fp32, 1 bf16                         */
     int32_t fmt;                  /* 0 E4M3, 1 E5M2                         */
     int32_t vec;                  /* 1: 8-element vector path (x 16-byte and

@@ -131,7 +131,16 @@ __global__ __launch_bounds__(256) void amax_kernel(QuantParams qp)
     share(qp.n, qp.parts, part, qp.vec != 0, lo, hi);
     float m = 0.0f;
     if (qp.vec) {
-        for (int64_t i = lo + 8 * (int64_t)threadIdx.x; i < hi; i += 8 * 256) {
+        /* two vectors in flight per thread */
+        int64_t i = lo + 8 * (int64_t)threadIdx.x;
+        for (; i + 8 * 256 < hi; i += 2 * 8 * 256) {
+            float v[8], w[8];
+            load8(xg, i, qp.src, v);
+            load8(xg, i + 8 * 256, qp.src, w);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(v[j]), fabsf(w[j])));
+        }
+        if (i < hi) {
             float v[8];
             load8(xg, i, qp.src, v);
 #pragma unroll
@@ -161,21 +170,45 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams qp)
     uint8_t *qg = qp.q + g * qp.n;
     int64_t lo, hi;
     share(qp.n, qp.parts, part, qp.vec != 0, lo, hi);
+    /* x / s rounded to nearest: with r the reciprocal of s rounded to
+     * nearest, q0 = x r is within an ulp of the quotient and one residual
+     * step q0 + (x - q0 s) r gives the quotient rounded to nearest
+     * (Markstein's theorem; the residual is exact by the fused
+     * multiply-add).  Quotients that would be subnormal in binary32 lie far
+     * below the smallest 8-bit code, where either rounding gives a zero
+     * code of the same sign. */
+    const float r = 1.0f / s;
     auto code = [&](float v) __attribute__((always_inline)) {
-        const float t = fminf(fmaxf(v / s, -F), F);
-        return encode8<FMT>(t);
+        /* on the magnitude; the quotient's sign is v's (s > 0) */
+        const float a = fabsf(v);
+        const float q0 = a * r;
+        const float e = __builtin_fmaf(-q0, s, a);
+        const float t = fminf(__builtin_fmaf(e, r, q0), F);
+        return encode8<FMT>(__builtin_copysignf(t, v));
+    };
+    auto quant8 = [&](int64_t i, const float (&v)[8]) __attribute__((always_inline)) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w0 |= code(v[j]) << (8 * j);
+            w1 |= code(v[j + 4]) << (8 * j);
+        }
+        *(uint2 *)(qg + i) = make_uint2(w0, w1);
     };
     if (qp.vec) {
-        for (int64_t i = lo + 8 * (int64_t)threadIdx.x; i < hi; i += 8 * 256) {
+        /* two vectors in flight per thread */
+        int64_t i = lo + 8 * (int64_t)threadIdx.x;
+        for (; i + 8 * 256 < hi; i += 2 * 8 * 256) {
+            float v[8], w[8];
+            load8(xg, i, qp.src, v);
+            load8(xg, i + 8 * 256, qp.src, w);
+            quant8(i, v);
+            quant8(i + 8 * 256, w);
+        }
+        if (i < hi) {
             float v[8];
             load8(xg, i, qp.src, v);
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                w0 |= code(v[j]) << (8 * j);
-                w1 |= code(v[j + 4]) << (8 * j);
-            }
-            *(uint2 *)(qg + i) = make_uint2(w0, w1);
+            quant8(i, v);
         }
     } else {
         for (int64_t i = lo + threadIdx.x; i < hi; i += 256) qg[i] = (uint8_t)code(load_elem(xg, i, qp.src));
