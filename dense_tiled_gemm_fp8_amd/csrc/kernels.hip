@@ -185,7 +185,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     static_assert(RB % KB_STEP == 0, "K-tile holds whole MFMA steps");
     static_assert(A_LOADS >= 1 && B_LOADS >= 1 && FM >= 1 && FN >= 1 && KSTEPS >= 1, "tile");
     static_assert(STAGES >= 2 && (STAGES - 1) * LOADS < 64, "ring depth");
-    static_assert(!SPREAD || STAGES >= 3, "spread copies need a third stage");
+    static_assert(SPREAD != 1 || STAGES >= 3, "spread copies need a third stage");
+    /* SPREAD 2: fragments read two K-steps ahead, one barrier per K-tile
+     * before its second-to-last step, copies over its last two steps */
+    static_assert(SPREAD != 2 || (KSTEPS == 4 && STAGES == 2 && LOADS % 2 == 0), "two-step prefetch schedule");
+    constexpr int NB = SPREAD == 2 ? 4 : 2;     /* fragment buffers */
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -290,8 +294,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = Acc{};
 
-        /* Fragments double-buffered by K-step parity. */
-        Frag fa[2][FM], fb[2][FN];
+        /* Fragments double-buffered by K-step parity (SPREAD 2: one buffer
+         * per K-step of the tile). */
+        Frag fa[NB][FM], fb[NB][FN];
 
         /* One K-step: the FM x FN MFMAs on buffer CUR, interleaved slot by
          * slot with the fragment reads of step nks of the stage at `ns` into
@@ -302,12 +307,22 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         auto step = [&](auto cur_c, auto d0_c, auto dn_c, const uint8_t *ns, int nks, uint32_t dso,
                         uint32_t kb, const KV &kv) __attribute__((always_inline)) {
             constexpr int CUR = decltype(cur_c)::value;
+            /* buffer the reads of this step fill */
+            constexpr int TGT = SPREAD == 2 ? (CUR + 2) % NB : CUR ^ 1;
             constexpr int D0 = decltype(d0_c)::value, DN = decltype(dn_c)::value;
             constexpr int NM = FM * FN, NR = FM + FN;
-            constexpr int SLOTS = NM > (NR > DN ? NR : DN) ? NM : (NR > DN ? NR : DN);
-            /* this step's fragments (read during the previous step) are in;
-             * nothing else is outstanding on the LDS counter here */
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            /* SPREAD 2 puts the copies after the reads: NR + DN slots at least */
+            constexpr int SLOTS = SPREAD == 2 ? (NM > NR + DN ? NM : NR + DN)
+                                              : NM > (NR > DN ? NR : DN) ? NM : (NR > DN ? NR : DN);
+            if constexpr (SPREAD == 2) {
+                /* this step's fragments (read two steps ago) are in; the NR
+                 * reads of the previous step may still be outstanding */
+                asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NR < 15 ? NR : 15) : "memory");
+            } else {
+                /* this step's fragments (read during the previous step) are
+                 * in; nothing else is outstanding on the LDS counter here */
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
             unroll<SLOTS>([&](auto tc) __attribute__((always_inline)) {
                 constexpr int t = decltype(tc)::value;
                 if constexpr (t < NM) {
@@ -326,10 +341,18 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                             fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, 0, 0, 0);
                 }
                 if constexpr (t < FM)
-                    fa[CUR ^ 1][t] = frag(ns + wm * WTM * RB, nks, t);
+                    fa[TGT][t] = frag(ns + wm * WTM * RB, nks, t);
                 else if constexpr (t < NR)
-                    fb[CUR ^ 1][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
-                if constexpr (DN > 0) {
+                    fb[TGT][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
+                if constexpr (DN > 0 && SPREAD == 2) {
+                    /* copies after the fragment reads, spread over the rest
+                     * of the step */
+                    constexpr int FREE = SLOTS - NR;
+                    unroll<DN>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value;
+                        if constexpr (NR + (j * FREE) / DN == t) dma(std::integral_constant<int, D0 + j>{}, dso, kb, kv);
+                    });
+                } else if constexpr (DN > 0) {
                     constexpr int j = (t * DN + SLOTS - 1) / SLOTS;
                     if constexpr (j < DN && (j * SLOTS) / DN == t)
                         dma(std::integral_constant<int, D0 + j>{}, dso, kb, kv);
@@ -348,29 +371,53 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
          * goes into the stage dso of tile kt-1 (free since the previous
          * barrier), its copies spread evenly over all K-steps, so the copy
          * queue never receives a whole K-tile at once. */
+        /* SPREAD 2, one K-tile of 4 K-steps in stage so (nso: the next
+         * tile's stage).  Step ks runs its MFMAs on buffer ks and reads the
+         * fragments of step ks+2 into buffer (ks+2) % 4: steps 0 and 1 read
+         * steps 2 and 3 of this stage, steps 2 and 3 read steps 0 and 1 of
+         * the next.  Before step 2 every wave has finished reading this stage
+         * and the next stage has landed: one barrier, then the copies of
+         * K-tile kt+2 into this stage over steps 2 and 3. */
+        auto tile2 = [&](uint32_t so, uint32_t nso, int32_t kt) __attribute__((always_inline)) {
+            const uint8_t *cs = smem + so;
+            const KV kv0{{false, false}};
+            step(IC<0>{}, IC<0>{}, IC<0>{}, cs, 2, so, 0u, kv0);
+            step(IC<1>{}, IC<0>{}, IC<0>{}, cs, 3, so, 0u, kv0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            /* tile kt+1 landed (its copies are the only ones outstanding) */
+            wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const KV kv = kvalid(kt + 2);
+            const uint32_t kb = (uint32_t)ktile(kt + 2) * RB;
+            step(IC<2>{}, IC<0>{}, IC<LOADS / 2>{}, smem + nso, 0, so, kb, kv);
+            step(IC<3>{}, IC<LOADS / 2>{}, IC<LOADS / 2>{}, smem + nso, 1, so, kb, kv);
+        };
+
         auto tile = [&](auto pc, uint32_t so, uint32_t nso, uint32_t dso, int32_t kt) __attribute__((always_inline)) {
             /* kt: the iteration index within the unit */
             constexpr int P = decltype(pc)::value;
-            constexpr int LPRE = SPREAD ? (KSTEPS - 1) * LOADS / KSTEPS : 0;
+            constexpr bool SP1 = SPREAD == 1;
+            constexpr int LPRE = SP1 ? (KSTEPS - 1) * LOADS / KSTEPS : 0;
             const uint8_t *cs = smem + so;
             KV kv{{false, false}};
             uint32_t kb = 0;
-            if constexpr (SPREAD) {
+            if constexpr (SP1) {
                 kv = kvalid(kt + STAGES - 1);
                 kb = (uint32_t)ktile(kt + STAGES - 1) * RB;
             }
             unroll<KSTEPS - 1>([&](auto kc) __attribute__((always_inline)) {
                 constexpr int ks = decltype(kc)::value;
-                constexpr int D0 = SPREAD ? ks * LOADS / KSTEPS : 0;
-                constexpr int DN = SPREAD ? (ks + 1) * LOADS / KSTEPS - D0 : 0;
+                constexpr int D0 = SP1 ? ks * LOADS / KSTEPS : 0;
+                constexpr int DN = SP1 ? (ks + 1) * LOADS / KSTEPS - D0 : 0;
                 step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, ks + 1, dso, kb, kv);
             });
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             /* tile kt+1 landed: later copies may still be in flight */
-            wait_vmcnt<SPREAD ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
+            wait_vmcnt<SP1 ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if constexpr (SPREAD) {
+            if constexpr (SP1) {
                 step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, 0, dso, kb, kv);
             } else {
                 kv = kvalid(kt + STAGES);
@@ -387,7 +434,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         if (nkt > 0) {
             int32_t kt = 0;
             /* prologue: the first PRE K-tiles of the unit */
-            constexpr int PRE = SPREAD ? STAGES - 1 : STAGES;
+            constexpr int PRE = SPREAD == 1 ? STAGES - 1 : STAGES;
             unroll<PRE>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int st = decltype(sc)::value;
                 copy_tile(st * STAGE_BYTES, kt + st);
@@ -395,12 +442,22 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
             wait_vmcnt<(PRE - 1) * LOADS>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
+            /* fragments of the first K-step (SPREAD 2: the first two) */
+            unroll<SPREAD == 2 ? 2 : 1>([&](auto pc) __attribute__((always_inline)) {
+                constexpr int b = decltype(pc)::value;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[0][i] = frag(smem + wm * WTM * RB, 0, i);
+                for (int i = 0; i < FM; ++i) fa[b][i] = frag(smem + wm * WTM * RB, b, i);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[0][j] = frag(smem + A_BYTES + wn * WTN * RB, 0, j);
+                for (int j = 0; j < FN; ++j) fb[b][j] = frag(smem + A_BYTES + wn * WTN * RB, b, j);
+            });
             uint32_t so = 0, dso = (STAGES - 1) * STAGE_BYTES;
-            if constexpr (KSTEPS % 2 == 0) {
+            if constexpr (SPREAD == 2) {
+                for (; kt < nkt; ++kt) {
+                    const uint32_t nso = next_stage(so);
+                    tile2(so, nso, kt);
+                    so = nso;
+                }
+            } else if constexpr (KSTEPS % 2 == 0) {
                 /* one loop body; the stage advances around the ring */
                 for (; kt < nkt; ++kt) {
                     const uint32_t nso = next_stage(so);
@@ -808,7 +865,10 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(37, 256, 256, false, 1, 64, 4, 2, 4, 0, 16)                                                   \
     X(38, 256, 256, false, 1, 64, 4, 2, 2, 0, 16)                                                   \
     X(39, 256, 256, false, 1, 64, 4, 2, 2, 1, 16)                                                   \
-    X(40, 256, 256, false, 1, 64, 5, 2, 2, 0, 16)
+    X(40, 256, 256, false, 1, 64, 5, 2, 2, 0, 16)                                                   \
+    X(41, 256, 256, false, 1, 128, 2, 2, 2, 2, 32)                                                  \
+    X(42, 256, 256, false, 1, 128, 2, 2, 4, 2, 32)                                                  \
+    X(43, 128, 128, false, 2, 128, 2, 2, 2, 2, 32)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi)                                                      \

@@ -25,8 +25,12 @@ struct TileCfg {
     int32_t row_bytes;     /* RB: K bytes per tile row per stage             */
     int32_t stages;
     int32_t waves_m, waves_n;
-    int32_t spread;        /* 1: copies of a K-tile spread over the K-steps of
-                              the tile before (ring of >= 3 stages)          */
+    int32_t spread;        /* copy schedule: 0 copies of a K-tile in the last
+                              K-step of the tile STAGES before; 1 spread
+                              over the K-steps of the tile before (ring of
+                              >= 3 stages); 2 fragments read two K-steps
+                              ahead and copies over the last two K-steps of
+                              the tile two before (2 stages, 4 K-steps)     */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
     int32_t lds_bytes;     /* stages * (TM + TN) * RB                        */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
@@ -99,6 +103,11 @@ constexpr TileCfg kTiles[] = {
     {0, 256, 256, 32, 64, 4, 2, 2, 0, 16, 4 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
     {0, 256, 256, 32, 64, 4, 2, 2, 1, 16, 4 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
     {0, 256, 256, 32, 64, 5, 2, 2, 0, 16, 5 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
+    /* 32 x 32 MFMA blocks, fragments read two K-steps ahead, copies over the
+     * last two K-steps of each K-tile */
+    {0, 256, 256, 64, 128, 2, 2, 2, 2, 32, 2 * (256 + 256) * 128, 1, 512, {0.90f, 0.90f, 0.90f, 0.90f}, 0.80f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 2, 32, 2 * (256 + 256) * 128, 1, 256, {0.85f, 0.85f, 0.85f, 0.85f}, 0.80f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 2, 32, 2 * (128 + 128) * 128, 2, 256, {0.50f, 0.65f, 0.65f, 0.65f}, 0.70f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 
