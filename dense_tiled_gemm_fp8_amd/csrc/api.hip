@@ -402,7 +402,7 @@ gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_
     if (T_N) *T_N = c.TN;
     if (T_K) *T_K = c.TK;
     if (stages) *stages = c.stages;
-    if (waves) *waves = c.waves_m * c.waves_n;
+    if (waves) *waves = tile_waves(c);
     if (lds_bytes) *lds_bytes = c.lds_bytes;
     if (b_max) *b_max = resident_workgroups(tile);
     return GEMM355_OK;
@@ -412,7 +412,7 @@ gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu)
 {
     if (tile < 0 || tile >= kNumTiles || !blocks_per_cu) return GEMM355_EINVAL;
     int n = 0;
-    const int threads = kTiles[tile].waves_m * kTiles[tile].waves_n * kWaveSize;
+    const int threads = tile_waves(kTiles[tile]) * kWaveSize;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel_symbol(tile), threads, 0) !=
         hipSuccess) {
         (void)hipGetLastError();

@@ -161,17 +161,21 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * reads of the next tile's first fragments.
  */
 template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
-__global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmParams p)
+__global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
     /* 8-bit operand formats (instruction format codes: 0 E4M3, 1 E5M2):
      * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B) */
     constexpr int FA = FMT == 1 ? 1 : 0, FB = FMT >= 1 ? 1 : 0;
     constexpr int NW = WGM * WGN, WN = WGN;
+    /* SPREAD 3 (warp specialisation): four more wavefronts, one per SIMD,
+     * issue every copy and run no MFMA; the NW MFMA wavefronts only read LDS.
+     * CW wavefronts copy. */
+    constexpr int NP = SPREAD == 3 ? 4 : 0, CW = SPREAD == 3 ? NP : NW;
     constexpr int WTM = TM / WGM, WTN = TN / WGN;
     constexpr int FM = WTM / MI, FN = WTN / MI;
     constexpr int CPR = RB / 16, RPL = 256 / RB, ROWS_PER_DMA = 1024 / RB;
     constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB, STAGE_BYTES = A_BYTES + B_BYTES;
-    constexpr int A_LOADS = TM / ROWS_PER_DMA / NW, B_LOADS = TN / ROWS_PER_DMA / NW;
+    constexpr int A_LOADS = TM / ROWS_PER_DMA / CW, B_LOADS = TN / ROWS_PER_DMA / CW;
     constexpr int LOADS = A_LOADS + B_LOADS;
     /* bytes of K per MFMA step: 32 x 32 blocks take 16 bf16 or 64 E4M3
      * values, 16 x 16 blocks 32 bf16 or 128 E4M3; CPS 16-byte chunks */
@@ -189,6 +193,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     /* SPREAD 2: fragments read two K-steps ahead, one barrier per K-tile
      * before its second-to-last step, copies over its last two steps */
     static_assert(SPREAD != 2 || (KSTEPS == 4 && STAGES == 2 && LOADS % 2 == 0), "two-step prefetch schedule");
+    static_assert(SPREAD != 3 || STAGES >= 3, "producer wavefronts run two K-tiles ahead");
+    static_assert(A_LOADS * CW * ROWS_PER_DMA == TM && B_LOADS * CW * ROWS_PER_DMA == TN, "whole copies");
     constexpr int NB = SPREAD == 2 ? 4 : 2;     /* fragment buffers */
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
@@ -196,17 +202,21 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
+    /* this wavefront's index among the CW copying ones (SPREAD 3: the
+     * producers NW .. NW+3) */
+    const bool producer = SPREAD == 3 && wave >= NW;
+    const int cw = SPREAD == 3 ? wave - NW : wave;
     const int drow = lane / CPR;
-    /* Copy d of a stage part is copy group d * NW + wave; the lane's row is
-     * r = (d * NW + wave) * ROWS_PER_DMA + drow, and ROWS_PER_DMA = 4 RPL,
-     * so (r / RPL) % CPR = (4 (d NW + wave) + drow / RPL) % CPR: with
-     * 4 NW a multiple of CPR it is the same for every d, otherwise (CPR = 8,
-     * NW odd) it alternates with the parity of d.  lchunk[d & 1] is the
+    /* Copy d of a stage part is copy group d * CW + cw; the lane's row is
+     * r = (d * CW + cw) * ROWS_PER_DMA + drow, and ROWS_PER_DMA = 4 RPL,
+     * so (r / RPL) % CPR = (4 (d CW + cw) + drow / RPL) % CPR: with
+     * 4 CW a multiple of CPR it is the same for every d, otherwise (CPR = 8,
+     * CW odd) it alternates with the parity of d.  lchunk[d & 1] is the
      * logical chunk the lane fetches. */
-    constexpr bool TWO = (4 * NW) % CPR != 0;
+    constexpr bool TWO = (4 * CW) % CPR != 0;
     int lchunk[2];
-    lchunk[0] = (lane % CPR) ^ ((4 * wave + drow / RPL) % CPR);
-    lchunk[1] = (lane % CPR) ^ ((4 * (NW + wave) + drow / RPL) % CPR);
+    lchunk[0] = (lane % CPR) ^ ((4 * cw + drow / RPL) % CPR);
+    lchunk[1] = (lane % CPR) ^ ((4 * (CW + cw) + drow / RPL) % CPR);
     /* fragment lanes: lane l reads row l % MI of the block and K-chunk
      * group l / MI of the step */
     const int frow = lane % MI, hi = lane / MI, sw = (frow / RPL) % CPR;
@@ -229,12 +239,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         uint32_t aoff[A_LOADS], boff[B_LOADS];
 #pragma unroll
         for (int i = 0; i < A_LOADS; ++i) {
-            const int r = (i * NW + wave) * ROWS_PER_DMA + drow;
+            const int r = (i * CW + cw) * ROWS_PER_DMA + drow;
             aoff[i] = (m0 + r < p.M) ? (uint32_t)(r * p.lda + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
         }
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
-            const int r = (i * NW + wave) * ROWS_PER_DMA + drow;
+            const int r = (i * CW + cw) * ROWS_PER_DMA + drow;
             boff[i] = (n0 + r < p.N) ? (uint32_t)(r * p.ldb + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
         }
 
@@ -262,11 +272,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
             constexpr int d = decltype(dc)::value;
             constexpr int di = d < A_LOADS ? d : d - A_LOADS;
             const bool ok = kv.v[TWO ? di & 1 : 0];
-            const uint32_t dst = smem_base + so + wave * 1024;
+            const uint32_t dst = smem_base + so + cw * 1024;
             if constexpr (d < A_LOADS)
-                dma16<d * NW * 1024>(ra, dst, ok ? aoff[d] + kb : kOOB);
+                dma16<d * CW * 1024>(ra, dst, ok ? aoff[d] + kb : kOOB);
             else
-                dma16<A_BYTES + (d - A_LOADS) * NW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
+                dma16<A_BYTES + (d - A_LOADS) * CW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
         };
         auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
             const KV kv = kvalid(i);
@@ -413,12 +423,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
                 step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, ks + 1, dso, kb, kv);
             });
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            /* tile kt+1 landed: later copies may still be in flight */
-            wait_vmcnt<SP1 ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
+            /* tile kt+1 landed: later copies may still be in flight (SPREAD
+             * 3: the producers have waited for it before this barrier) */
+            if constexpr (SPREAD != 3)
+                wait_vmcnt<SP1 ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             if constexpr (SP1) {
                 step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, 0, dso, kb, kv);
+            } else if constexpr (SPREAD == 3) {
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<0>{}, smem + nso, 0, so, 0u, kv);
             } else {
                 kv = kvalid(kt + STAGES);
                 kb = (uint32_t)ktile(kt + STAGES) * RB;
@@ -431,15 +445,37 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
 
-        if (nkt > 0) {
-            int32_t kt = 0;
-            /* prologue: the first PRE K-tiles of the unit */
-            constexpr int PRE = SPREAD == 1 ? STAGES - 1 : STAGES;
-            unroll<PRE>([&](auto sc) __attribute__((always_inline)) {
+        if (producer && nkt > 0) {
+            /* SPREAD 3 producer: K-tiles 0 .. STAGES-2 first; then, between
+             * the MFMA wavefronts' barriers kt-1 and kt, K-tile kt+STAGES-1
+             * into the stage of K-tile kt-1 (read by every wavefront before
+             * barrier kt-1), and barrier kt only once K-tile kt+1 has
+             * landed.  Same barrier count as the MFMA wavefronts. */
+            unroll<STAGES - 1>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int st = decltype(sc)::value;
-                copy_tile(st * STAGE_BYTES, kt + st);
+                copy_tile(st * STAGE_BYTES, st);
             });
-            wait_vmcnt<(PRE - 1) * LOADS>();
+            wait_vmcnt<(STAGES - 2) * LOADS>();
+            __builtin_amdgcn_s_barrier();
+            uint32_t dso = (STAGES - 1) * STAGE_BYTES;
+            for (int32_t kt = 0; kt < nkt; ++kt) {
+                copy_tile(dso, kt + STAGES - 1);
+                wait_vmcnt<(STAGES - 2) * LOADS>();
+                __builtin_amdgcn_s_barrier();
+                dso = next_stage(dso);
+            }
+        } else if (nkt > 0) {
+            int32_t kt = 0;
+            /* prologue: the first PRE K-tiles of the unit (SPREAD 3: issued
+             * by the producers) */
+            if constexpr (SPREAD != 3) {
+                constexpr int PRE = SPREAD == 1 ? STAGES - 1 : STAGES;
+                unroll<PRE>([&](auto sc) __attribute__((always_inline)) {
+                    constexpr int st = decltype(sc)::value;
+                    copy_tile(st * STAGE_BYTES, kt + st);
+                });
+                wait_vmcnt<(PRE - 1) * LOADS>();
+            }
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             /* fragments of the first K-step (SPREAD 2: the first two) */
@@ -493,79 +529,81 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void gemm_tile_kernel(GemmPar
          * and hold them in registers across it. */
         int lv = threadIdx.x;
         asm volatile("" : "+v"(lv));
-        const int el = lv & 63, ecol = el % MI, ehi = el / MI;
-        /* row of accumulator register e relative to the lane's first row */
-        auto erow = [](int e) __attribute__((always_inline)) { return MI == 32 ? (e >> 2) * 8 + (e & 3) : e; };
-        if (un.slot >= 0) {
-            /* partial slot: the tile's positions inside M x N only (the
-             * combine pass reads no others) */
-            const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (int64_t)un.slot * (TM * TN));
-            const int32_t mrem = p.M - m0, nrem = p.N - n0;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = wn * WTN + j * MI + ecol;
-                    const int row0 = wm * WTM + i * MI + ehi * 4;
-                    const uint32_t voff = (uint32_t)((row0 * TN + col) * 4);
-#pragma unroll
-                    for (int e = 0; e < ACC_N; ++e) {
-                        /* copy the element out first: a bit_cast applied to
-                         * a vector subscript directly was lowered to element
-                         * 0 for every e */
-                        const float v = acc[i][j][e];
-                        const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, ok ? voff : kOOB,
-                                                              erow(e) * TN * 4, 0);
-                    }
-                    /* one block at a time keeps the epilogue's registers few */
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-        } else {
-            const float alpha = unit_alpha(p, un.batch);
-            const int32_t mrem = p.M - m0, nrem = p.N - n0;
-            if (p.out_bf16) {
-                const __amdgpu_buffer_rsrc_t rc = make_rsrc(
-                    (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 2);
-                const int32_t ldcb = (int32_t)p.ldc * 2;
+        if (!producer) {
+            const int el = lv & 63, ecol = el % MI, ehi = el / MI;
+            /* row of accumulator register e relative to the lane's first row */
+            auto erow = [](int e) __attribute__((always_inline)) { return MI == 32 ? (e >> 2) * 8 + (e & 3) : e; };
+            if (un.slot >= 0) {
+                /* partial slot: the tile's positions inside M x N only (the
+                 * combine pass reads no others) */
+                const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (int64_t)un.slot * (TM * TN));
+                const int32_t mrem = p.M - m0, nrem = p.N - n0;
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         const int col = wn * WTN + j * MI + ecol;
                         const int row0 = wm * WTM + i * MI + ehi * 4;
-                        const uint32_t voff = (uint32_t)(row0 * ldcb + col * 2);
+                        const uint32_t voff = (uint32_t)((row0 * TN + col) * 4);
 #pragma unroll
                         for (int e = 0; e < ACC_N; ++e) {
-                            const int dr = erow(e);
-                            const bool ok = (row0 + dr < mrem) && (col < nrem);
-                            const float v = alpha * acc[i][j][e];
-                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc,
-                                                                  ok ? voff : kOOB, dr * ldcb, 0);
+                            /* copy the element out first: a bit_cast applied to
+                             * a vector subscript directly was lowered to element
+                             * 0 for every e */
+                            const float v = acc[i][j][e];
+                            const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, ok ? voff : kOOB,
+                                                                  erow(e) * TN * 4, 0);
                         }
+                        /* one block at a time keeps the epilogue's registers few */
                         __builtin_amdgcn_sched_barrier(0);
                     }
             } else {
-                const __amdgpu_buffer_rsrc_t rc = make_rsrc(
-                    (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
-                const int32_t ldcb = (int32_t)p.ldc * 4;
+                const float alpha = unit_alpha(p, un.batch);
+                const int32_t mrem = p.M - m0, nrem = p.N - n0;
+                if (p.out_bf16) {
+                    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+                        (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 2);
+                    const int32_t ldcb = (int32_t)p.ldc * 2;
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+                    for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const int col = wn * WTN + j * MI + ecol;
-                        const int row0 = wm * WTM + i * MI + ehi * 4;
-                        const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
+                        for (int j = 0; j < FN; ++j) {
+                            const int col = wn * WTN + j * MI + ecol;
+                            const int row0 = wm * WTM + i * MI + ehi * 4;
+                            const uint32_t voff = (uint32_t)(row0 * ldcb + col * 2);
 #pragma unroll
-                        for (int e = 0; e < ACC_N; ++e) {
-                            const int dr = erow(e);
-                            const bool ok = (row0 + dr < mrem) && (col < nrem);
-                            const float v = alpha * acc[i][j][e];
-                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc,
-                                                                  ok ? voff : kOOB, dr * ldcb, 0);
+                            for (int e = 0; e < ACC_N; ++e) {
+                                const int dr = erow(e);
+                                const bool ok = (row0 + dr < mrem) && (col < nrem);
+                                const float v = alpha * acc[i][j][e];
+                                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc,
+                                                                      ok ? voff : kOOB, dr * ldcb, 0);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                } else {
+                    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+                        (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
+                    const int32_t ldcb = (int32_t)p.ldc * 4;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            const int col = wn * WTN + j * MI + ecol;
+                            const int row0 = wm * WTM + i * MI + ehi * 4;
+                            const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
+#pragma unroll
+                            for (int e = 0; e < ACC_N; ++e) {
+                                const int dr = erow(e);
+                                const bool ok = (row0 + dr < mrem) && (col < nrem);
+                                const float v = alpha * acc[i][j][e];
+                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc,
+                                                                      ok ? voff : kOOB, dr * ldcb, 0);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                }
             }
         }
         if (p.stamps) {
@@ -800,7 +838,7 @@ template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int W
 static hipError_t launch_one(const GemmParams &p, hipStream_t stream)
 {
     hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, FMT>), dim3(p.s.grid),
-                       dim3(WGM * WGN * 64), 0, stream, p);
+                       dim3((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -868,7 +906,11 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(40, 256, 256, false, 1, 64, 5, 2, 2, 0, 16)                                                   \
     X(41, 256, 256, false, 1, 128, 2, 2, 2, 2, 32)                                                  \
     X(42, 256, 256, false, 1, 128, 2, 2, 4, 2, 32)                                                  \
-    X(43, 128, 128, false, 2, 128, 2, 2, 2, 2, 32)
+    X(43, 128, 128, false, 2, 128, 2, 2, 2, 2, 32)                                                  \
+    X(44, 256, 128, false, 1, 128, 3, 2, 2, 3, 32)                                                  \
+    X(45, 256, 128, false, 1, 128, 3, 2, 2, 3, 16)                                                  \
+    X(46, 256, 128, true, 1, 128, 3, 2, 2, 3, 32)                                                   \
+    X(47, 256, 128, false, 1, 128, 3, 2, 2, 0, 32)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi)                                                      \

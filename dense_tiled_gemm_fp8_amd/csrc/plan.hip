@@ -261,7 +261,7 @@ double rational_to_double(uint64_t num, uint64_t den)
 int32_t resident_workgroups(int32_t tile)
 {
     const TileCfg &c = kTiles[tile];
-    const int32_t waves = c.waves_m * c.waves_n;
+    const int32_t waves = tile_waves(c);
     const int32_t threads = waves * kWaveSize;
     const int32_t by_lds = kLdsPerCu / c.lds_bytes;
     const int32_t regs = (c.vgpr_budget + kRegGranule - 1) / kRegGranule * kRegGranule;
@@ -452,7 +452,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     o.T_N = cfg.TN;
     o.T_K = cfg.TK;
     o.stages = cfg.stages;
-    o.waves = cfg.waves_m * cfg.waves_n;
+    o.waves = tile_waves(cfg);
     o.lds_bytes = cfg.lds_bytes;
     o.vgpr_budget = cfg.vgpr_budget;
     o.b = best.b;

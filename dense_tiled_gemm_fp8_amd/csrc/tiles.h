@@ -30,12 +30,16 @@ struct TileCfg {
                               over the K-steps of the tile before (ring of
                               >= 3 stages); 2 fragments read two K-steps
                               ahead and copies over the last two K-steps of
-                              the tile two before (2 stages, 4 K-steps)     */
+                              the tile two before (2 stages, 4 K-steps);
+                              3 warp specialisation: four more wavefronts
+                              (one per SIMD) issue every copy, STAGES-1
+                              K-tiles ahead, and the waves_m x waves_n MFMA
+                              wavefronts only read LDS (3 stages or more)  */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
     int32_t lds_bytes;     /* stages * (TM + TN) * RB                        */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
-    int32_t vgpr_budget;   /* 512 / (min_blocks * waves / 4): registers per
-                              lane one wave may hold                        */
+    int32_t vgpr_budget;   /* 512 / (min_blocks * tile_waves / 4): registers
+                              per lane one wave may hold                    */
     /* planning prior: fraction of a compute unit's dense MFMA peak the tile
      * sustains with 1, 2, 3, 4 of its workgroups resident on the unit */
     float mfma_eff[4];
@@ -98,7 +102,7 @@ constexpr TileCfg kTiles[] = {
     {0, 256, 256, 32, 64, 4, 4, 4, 1, 32, 4 * (256 + 256) * 64, 1, 128, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
     /* 256 x 256 with 16 x 16 MFMA blocks */
     {0, 256, 256, 64, 128, 2, 2, 2, 0, 16, 2 * (256 + 256) * 128, 1, 512, {0.86f, 0.86f, 0.86f, 0.86f}, 0.80f},
-    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.85f, 0.85f, 0.85f, 0.85f}, 0.80f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.92f, 0.92f, 0.92f, 0.92f}, 0.80f},
     {0, 256, 256, 32, 64, 4, 2, 4, 0, 16, 4 * (256 + 256) * 64, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
     {0, 256, 256, 32, 64, 4, 2, 2, 0, 16, 4 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
     {0, 256, 256, 32, 64, 4, 2, 2, 1, 16, 4 * (256 + 256) * 64, 1, 512, {0.78f, 0.78f, 0.78f, 0.78f}, 0.80f},
@@ -108,8 +112,22 @@ constexpr TileCfg kTiles[] = {
     {0, 256, 256, 64, 128, 2, 2, 2, 2, 32, 2 * (256 + 256) * 128, 1, 512, {0.90f, 0.90f, 0.90f, 0.90f}, 0.80f},
     {0, 256, 256, 64, 128, 2, 2, 4, 2, 32, 2 * (256 + 256) * 128, 1, 256, {0.85f, 0.85f, 0.85f, 0.85f}, 0.80f},
     {0, 128, 128, 64, 128, 2, 2, 2, 2, 32, 2 * (128 + 128) * 128, 2, 256, {0.50f, 0.65f, 0.65f, 0.65f}, 0.70f},
+    /* 256 x 128, 3 stages: producer wavefronts (warp specialisation) with
+     * 32 x 32 and 16 x 16 blocks and for E4M3, and the same tile with
+     * uniform wavefronts for comparison */
+    {0, 256, 128, 64, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 128, 64, 128, 3, 2, 2, 3, 16, 3 * (256 + 128) * 128, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {1, 256, 128, 128, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    {0, 256, 128, 64, 128, 3, 2, 2, 0, 32, 3 * (256 + 128) * 128, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
+
+/* wavefronts of one workgroup: the MFMA grid plus, with copy schedule 3,
+ * one producer per SIMD */
+constexpr int32_t tile_waves(const TileCfg &c)
+{
+    return c.waves_m * c.waves_n + (c.spread == 3 ? kSimdsPerCu : 0);
+}
 
 } /* namespace g355 */
 
