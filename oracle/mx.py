@@ -1,0 +1,95 @@
+"""Block-scaled ("microscaled") 8-bit products: the CPU oracle.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product library.
+
+Page "The Tensor Core", the low-precision input table, lists microscaled
+formats as the row after the Hopper FP8 pair. The pages stop at the name.
+The reading taken here is the OCP Microscaling Formats (MX) specification,
+version 1.0:
+
+* a block is 32 consecutive elements along the contraction dimension K,
+  all sharing one scale;
+* the scale is an E8M0 code e, whose value is 2^(e - 127); e = 255 is NaN;
+* the elements are E4M3 or E5M2 codes, decoded as in ``gemm_oracle.c``;
+* an element's value is scale * element.
+
+For A (M x K) each row has ceil(K/32) scales. For B (K x N) each column has
+ceil(K/32) scales. The product is written out directly:
+
+    C[i][j] = alpha * sum_k (2^(sa[i][k/32] - 127) a(i,k)) (2^(sb[j][k/32] - 127) b(k,j))
+    W[i][j] = |alpha| * sum_k |same term|
+
+Element values come from the C oracle's decoders, which are pinned
+exhaustively against torch's casts. Each scaled element is then exact in
+binary64: a power of two times a short significand, far inside binary64's
+range. The K-term sum is a binary64 matrix product (a library primitive), so
+the only rounding is binary64 summation.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import reference
+
+BLOCK = 32
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale codes -> binary64: 2^(e - 127), NaN for e = 255."""
+    e = np.asarray(codes, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def _element_table(fmt: str) -> np.ndarray:
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    if fmt == "e4m3":
+        return reference.decode_e4m3(codes)
+    if fmt == "e5m2":
+        return reference.decode_e5m2(codes)
+    raise ValueError("block-scaled element format must be e4m3 or e5m2, not %r" % (fmt,))
+
+
+def scaled_operand(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
+    """Rows x K element codes and rows x ceil(K/32) E8M0 scales -> the
+    binary64 values 2^(s - 127) * element, rows x K."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, K = codes.shape
+    nb = -(-K // BLOCK)
+    scales = np.asarray(scales, dtype=np.uint8)
+    if scales.shape != (rows, nb):
+        raise ValueError("scales must be rows x ceil(K/32) = %s, got %s" % ((rows, nb), scales.shape))
+    vals = _element_table(fmt)[codes]
+    per_k = np.repeat(decode_e8m0(scales), BLOCK, axis=1)[:, :K]
+    return vals * per_k
+
+
+def gemm(A: np.ndarray, sa: np.ndarray, B: np.ndarray, sb: np.ndarray, fmt_a: str = "e4m3",
+         fmt_b: Optional[str] = None, alpha: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """A: M x K codes (row-major), sa: M x ceil(K/32); B: N x K codes (column
+    j of B is row j), sb: N x ceil(K/32). Returns (C, W), both binary64
+    M x N."""
+    fmt_b = fmt_a if fmt_b is None else fmt_b
+    a = scaled_operand(A, sa, fmt_a)
+    b = scaled_operand(B, sb, fmt_b)
+    C = alpha * (a @ b.T)
+    W = abs(alpha) * (np.abs(a) @ np.abs(b).T)
+    return C, W
+
+
+def gemm_entries(A: np.ndarray, sa: np.ndarray, B: np.ndarray, sb: np.ndarray, rows: np.ndarray,
+                 cols: np.ndarray, fmt_a: str = "e4m3", fmt_b: Optional[str] = None,
+                 alpha: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected entries (rows[t], cols[t]) of the same product, each its own
+    K-term dot product."""
+    fmt_b = fmt_a if fmt_b is None else fmt_b
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    a = scaled_operand(np.asarray(A)[rows], np.asarray(sa)[rows], fmt_a)
+    b = scaled_operand(np.asarray(B)[cols], np.asarray(sb)[cols], fmt_b)
+    c = alpha * np.einsum("tk,tk->t", a, b)
+    w = abs(alpha) * np.einsum("tk,tk->t", np.abs(a), np.abs(b))
+    return c, w
