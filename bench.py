@@ -337,6 +337,47 @@ def fp8_end_to_end(torch, g, inputs, args):
     return out
 
 
+def mx_products(torch, g, inputs, args):
+    """8192^3 block-scaled products (E8M0 scale per 32 K-values of each row
+    of A and column of B), E4M3 and E5M2 elements, fp32 C, timed like the
+    per-tensor E4M3 product beside them (same shape, same box)."""
+    import numpy as np
+    M = N = K = 8192
+    flops = 2.0 * M * N * K
+    out = []
+    for fmt, dt in (("mxe4m3", g.MXE4M3_F32), ("mxe5m2", g.MXE5M2_F32)):
+        log("bench: detail block-scaled", fmt, (M, N, K))
+        ops = inputs.make_operands(M, N, K, fmt, "normal", inputs.seed_for(6, 0, 0), inputs.seed_for(6, 0, 1))
+        A = torch.from_numpy(ops.A).cuda()
+        B = torch.from_numpy(ops.B).cuda()
+        sa = torch.from_numpy(ops.bsa).cuda()
+        sb = torch.from_numpy(ops.bsb).cuda()
+        del ops
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        a = g.make_args(M, N, K, A=A, B=B, C=C, dtype=dt, block_scale_a=sa, block_scale_b=sb)
+        p = g.gemm355_plan(a)
+        c = _Steps(lambda sp, a=a: g.gemm355_gemm_ex(a, sp), flops)
+        settle(c, torch, args.settle / 2)
+        reps = []
+        for _ in range(3):
+            n = max(10, args.steps // 10)
+            _, ev = time_case(c, torch, n, max(3, args.warmup // 10))
+            reps.append(ev / n)
+        reps.sort()
+        med = reps[1]
+        out.append({
+            "workload": "%s 8192x8192x8192 (block-scaled: E8M0 scale per 32 K-values, entries N(0,1) "
+                        "quantised per block, fp32 C)" % fmt,
+            "dtype": fmt, "out": "f32", "us_median": round(med * 1e6, 2), "us_min": round(reps[0] * 1e6, 2),
+            "tflops": round(flops / med / 1e12, 1),
+            "pct_mfma_peak": round(100 * flops / med / 1e12 / PEAK_TFLOPS["e4m3"], 1),
+            "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"], "grid": p["grid"],
+        })
+        del A, B, sa, sb, C
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(torch, budget_s=15.0):
     """The oracle (as it stands) on a bounded sample of the headline product:
     the first R rows of A against all of B, R sized from a short probe to
@@ -467,6 +508,8 @@ def main():
 
     if not args.no_detail and (args.workload in (None, "fp8-end-to-end")):
         detail.extend(fp8_end_to_end(torch, g, inputs, args))
+    if not args.no_detail and (args.workload in (None, "block-scaled")):
+        detail.extend(mx_products(torch, g, inputs, args))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -97,7 +97,8 @@ PlanKey key_of(const gemm355_args &a, int32_t S)
                         (((uintptr_t)a.C & 15u) << 8) | (((uintptr_t)a.scale_a & 3u) << 12) |
                         (((uintptr_t)a.scale_b & 3u) << 14));
     /* null-ness matters for validation */
-    k.v[14] = (a.A ? 1 : 0) | (a.B ? 2 : 0) | (a.C ? 4 : 0);
+    k.v[14] = (a.A ? 1 : 0) | (a.B ? 2 : 0) | (a.C ? 4 : 0) | (a.block_scale_a ? 8 : 0) |
+              (a.block_scale_b ? 16 : 0);
     return k;
 }
 
@@ -248,6 +249,28 @@ gemm355_status run(const gemm355_args &a, void *stream)
     gp.Kb = P.Kb;
     gp.out_bf16 = P.out_esize == 2 ? 1 : 0;
     gp.stamps = a.unit_stamps;
+    gp.bsa = gp.bsb = nullptr;
+    gp.ktp_a = a.M * 4;
+    gp.ktp_b = a.N * 4;
+    gp.stride_bsa = a.M * (a.K / 32);
+    gp.stride_bsb = a.N * (a.K / 32);
+    if (P.ws_scale_a_bytes) {
+        /* regroup the block scales K-tile-major so that one direct-to-LDS
+         * dword copy of 64 rows reads 256 contiguous bytes */
+        ScalePackParams sp;
+        sp.src = a.block_scale_a;
+        sp.dst = (uint32_t *)(ws + P.ws_scale_a_off);
+        sp.rows = (int32_t)a.M;
+        sp.nK = (int32_t)(a.K / 128);
+        sp.batch = (int32_t)a.batch;
+        if (launch_pack_scales(sp, hs) != hipSuccess) return GEMM355_EHIP;
+        gp.bsa = (const uint8_t *)sp.dst;
+        sp.src = a.block_scale_b;
+        sp.dst = (uint32_t *)(ws + P.ws_scale_b_off);
+        sp.rows = (int32_t)a.N;
+        if (launch_pack_scales(sp, hs) != hipSuccess) return GEMM355_EHIP;
+        gp.bsb = (const uint8_t *)sp.dst;
+    }
     gp.s = P.s;
     /* operand-format pair of an 8-bit product: 0 E4M3 x E4M3, 1 E5M2 x E5M2,
      * 2 E4M3 x E5M2 */

@@ -26,6 +26,11 @@ struct GemmParams {
     int32_t M, N, Kb;             /* Kb: K in bytes (multiple of 16)        */
     int32_t out_bf16;
     uint64_t *stamps;             /* per-unit start/end clock or null       */
+    /* block scales (MX tiles), regrouped: dword [batch][K-tile][row] holds
+     * a row's four E8M0 scales of one K-tile of 128 values */
+    const uint8_t *bsa, *bsb;
+    int64_t ktp_a, ktp_b;         /* bytes between K-tiles: 4 M, 4 N        */
+    int64_t stride_bsa, stride_bsb;   /* bytes between batch entries        */
     Sched s;
 };
 
@@ -51,6 +56,13 @@ struct PackParams {
     int32_t kmajor;               /* 1: source K-contiguous                 */
 };
 
+/* Block scales [batch][rows][nK * 4] bytes -> [batch][nK][rows] dwords. */
+struct ScalePackParams {
+    const uint8_t *src;
+    uint32_t *dst;
+    int32_t rows, nK, batch;
+};
+
 /* Per-tensor quantisation to 8 bits (quant.hip). */
 struct QuantParams {
     const void *x;                /* batch tensors of n elements            */
@@ -68,11 +80,12 @@ struct QuantParams {
 hipError_t launch_quantize(const QuantParams &qp, hipStream_t stream);
 
 /* fmt: operand formats of an 8-bit tile (0 E4M3 x E4M3, 1 E5M2 x E5M2,
- * 2 E4M3 x E5M2); 0 for bf16 tiles */
+ * 2 E4M3 x E5M2), with or without block scales; 0 for bf16 tiles */
 hipError_t launch_gemm(int32_t tile, int32_t fmt, const GemmParams &p, hipStream_t stream);
 const void *gemm_kernel_symbol(int32_t tile);
 hipError_t launch_reduce(const ReduceParams &r, int32_t tiles, hipStream_t stream);
 hipError_t launch_pack(const PackParams &pk, hipStream_t stream);
+hipError_t launch_pack_scales(const ScalePackParams &sp, hipStream_t stream);
 hipError_t launch_zero(void *C, int32_t M, int32_t N, int64_t ldc, int64_t stride_c,
                        int32_t batch, int32_t esize, hipStream_t stream);
 

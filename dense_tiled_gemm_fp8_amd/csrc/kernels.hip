@@ -12,6 +12,8 @@
  *                     aligned layout the main loop reads (misaligned rows
  *                     or K not a multiple of 16 bytes; the three other
  *                     operand layouts)
+ *   pack_scales_kernel
+ *                     regroup block scales (MX) K-tile-major
  *   zero_kernel       C = 0 for K == 0
  *
  * Source pages: "10. Tensor Cores, shapes, and tile alignment" (tile grid,
@@ -98,6 +100,18 @@ __device__ __forceinline__ void dma16(const i32x4 &rsrc, uint32_t lds_base, uint
     (void)m0_out;
 }
 
+/* One direct-to-LDS dword copy: lane l fetches 4 bytes at voffset and the
+ * wavefront writes them to LDS at lds_addr + 4 l (256 bytes). */
+__device__ __forceinline__ void dma4(const i32x4 &rsrc, uint32_t lds_addr_, uint32_t voffset)
+{
+    int m0_out;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %1, %3, 0 offen lds"
+                 : "={m0}"(m0_out)
+                 : "v"(voffset), "s"(lds_addr_), "s"(rsrc)
+                 : "memory");
+    (void)m0_out;
+}
+
 /* All of this wave's direct-to-LDS copies have landed, then the workgroup
  * meets; the asm statements keep the compiler from moving LDS accesses
  * across. */
@@ -160,9 +174,11 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * issued into the stage just freed, and the last step's MFMAs overlap the
  * reads of the next tile's first fragments.
  */
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
+template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
 __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
+    /* element class: 0 bf16, 1 8-bit, 2 8-bit with E8M0 block scales */
+    constexpr bool FP8 = EL != 0, MX = EL == 2;
     /* 8-bit operand formats (instruction format codes: 0 E4M3, 1 E5M2):
      * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B) */
     constexpr int FA = FMT == 1 ? 1 : 0, FB = FMT >= 1 ? 1 : 0;
@@ -174,9 +190,16 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     constexpr int WTM = TM / WGM, WTN = TN / WGN;
     constexpr int FM = WTM / MI, FN = WTN / MI;
     constexpr int CPR = RB / 16, RPL = 256 / RB, ROWS_PER_DMA = 1024 / RB;
-    constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB, STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB;
+    /* MX: a K-tile of 128 values holds four 32-value blocks per row, so one
+     * dword of E8M0 scales per row of A and B; a stage keeps TM + TN such
+     * dwords after the operand rows (A's, then B's), copied 64 rows per
+     * direct-to-LDS dword load, SC loads per wavefront */
+    constexpr int SCA_OFF = A_BYTES + B_BYTES, SCB_OFF = SCA_OFF + TM * 4;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES + (MX ? (TM + TN) * 4 : 0);
+    constexpr int SC = MX ? (TM + TN) / 64 / NW : 0;
     constexpr int A_LOADS = TM / ROWS_PER_DMA / CW, B_LOADS = TN / ROWS_PER_DMA / CW;
-    constexpr int LOADS = A_LOADS + B_LOADS;
+    constexpr int LOADS = A_LOADS + B_LOADS + SC;
     /* bytes of K per MFMA step: 32 x 32 blocks take 16 bf16 or 64 E4M3
      * values, 16 x 16 blocks 32 bf16 or 128 E4M3; CPS 16-byte chunks */
     constexpr int KB_STEP = (FP8 ? 64 : 32) * (MI == 32 ? 1 : 2);
@@ -195,6 +218,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     static_assert(SPREAD != 2 || (KSTEPS == 4 && STAGES == 2 && LOADS % 2 == 0), "two-step prefetch schedule");
     static_assert(SPREAD != 3 || STAGES >= 3, "producer wavefronts run two K-tiles ahead");
     static_assert(A_LOADS * CW * ROWS_PER_DMA == TM && B_LOADS * CW * ROWS_PER_DMA == TN, "whole copies");
+    static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == TM + TN),
+                  "block scales: one dword per row and K-tile, whole 64-row copies per wavefront");
     constexpr int NB = SPREAD == 2 ? 4 : 2;     /* fragment buffers */
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
@@ -247,6 +272,28 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             const int r = (i * CW + cw) * ROWS_PER_DMA + drow;
             boff[i] = (n0 + r < p.N) ? (uint32_t)(r * p.ldb + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
         }
+        /* MX: scale copy q of this wavefront moves the dwords of 64 rows,
+         * group g = q NW + wave: rows 64 g .. 64 g + 63 of A if g < TM / 64,
+         * else rows 64 (g - TM / 64) .. of B; lane l takes the group's row l
+         * (the scales are regrouped K-tile-major, so the 64 dwords are
+         * contiguous).  Rows past M or N read zero (scale 2^-127 on zero
+         * operands). */
+        i32x4 srs[SC > 0 ? SC : 1];
+        uint32_t soff[SC > 0 ? SC : 1], sdst[SC > 0 ? SC : 1], stp[SC > 0 ? SC : 1];
+        if constexpr (MX) {
+            const uint8_t *sa0 = p.bsa + (int64_t)un.batch * p.stride_bsa + (int64_t)m0 * 4;
+            const uint8_t *sb0 = p.bsb + (int64_t)un.batch * p.stride_bsb + (int64_t)n0 * 4;
+            unroll<SC>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                const int g = q * NW + wave;
+                const bool in_a = g < TM / 64;
+                const int r = (in_a ? g : g - TM / 64) * 64 + lane;
+                srs[q] = rsrc_words(in_a ? sa0 : sb0);
+                soff[q] = (in_a ? m0 + r < p.M : n0 + r < p.N) ? (uint32_t)(r * 4) : kOOB;
+                sdst[q] = (uint32_t)(SCA_OFF + g * 256);
+                stp[q] = (uint32_t)(in_a ? p.ktp_a : p.ktp_b);
+            });
+        }
 
         /* Copy of K-tile kt into the stage at LDS byte offset so: chunks past
          * K, and every chunk of a K-tile past the unit's range, read zero, so
@@ -273,10 +320,15 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             constexpr int di = d < A_LOADS ? d : d - A_LOADS;
             const bool ok = kv.v[TWO ? di & 1 : 0];
             const uint32_t dst = smem_base + so + cw * 1024;
-            if constexpr (d < A_LOADS)
+            if constexpr (d < A_LOADS) {
                 dma16<d * CW * 1024>(ra, dst, ok ? aoff[d] + kb : kOOB);
-            else
+            } else if constexpr (d < A_LOADS + B_LOADS) {
                 dma16<A_BYTES + (d - A_LOADS) * CW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
+            } else {
+                /* K-tile kb / RB of the regrouped scales */
+                constexpr int q = d - A_LOADS - B_LOADS;
+                dma4(srs[q], smem_base + so + sdst[q], kv.v[0] ? soff[q] + (kb / RB) * stp[q] : kOOB);
+            }
         };
         auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
             const KV kv = kvalid(i);
@@ -291,9 +343,44 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             if constexpr (!FP8) {
                 return *(const bf16x8 *)(row + (((CPS * ks + hi) ^ sw) * 16));
             } else {
-                const i32x4 lo = *(const i32x4 *)(row + (((CPS * ks + 2 * hi) ^ sw) * 16));
-                const i32x4 up = *(const i32x4 *)(row + (((CPS * ks + 2 * hi + 1) ^ sw) * 16));
+                /* the instruction takes K in 16-byte quarters: lane group
+                 * hi's first and second halves are quarters hi and 2 + hi of
+                 * the step, and the block scale of lane group hi covers
+                 * quarters 2 hi and 2 hi + 1 (the first halves of both
+                 * groups, or the second halves).  Without block scales any
+                 * consistent order of A's and B's chunks gives the same
+                 * products; with them, reading chunks hi and 2 + hi puts
+                 * the step's 32-value block hi under scale byte hi. */
+                const int c0 = MX ? CPS * ks + hi : CPS * ks + 2 * hi;
+                const int c1 = MX ? CPS * ks + 2 + hi : CPS * ks + 2 * hi + 1;
+                const i32x4 lo = *(const i32x4 *)(row + ((c0 ^ sw) * 16));
+                const i32x4 up = *(const i32x4 *)(row + ((c1 ^ sw) * 16));
                 return i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+            }
+        };
+
+        /* MX: the scale dwords of this wavefront's MFMA rows for the next
+         * K-tile (read from LDS in the last K-step, after the next tile's
+         * first fragments) and for the current one, shifted so that byte 0
+         * holds the lane's first block (the instruction takes its scale
+         * from byte 0) */
+        uint32_t nsa[MX ? FM : 1], nsb[MX ? FN : 1], csa[MX ? FM : 1], csb[MX ? FN : 1];
+        auto read_scales = [&](const uint8_t *st) __attribute__((always_inline)) {
+            if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    nsa[i] = *(const uint32_t *)(st + SCA_OFF + (wm * WTM + i * MI + frow) * 4);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    nsb[j] = *(const uint32_t *)(st + SCB_OFF + (wn * WTN + j * MI + frow) * 4);
+            }
+        };
+        auto take_scales = [&]() __attribute__((always_inline)) {
+            if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) csa[i] = nsa[i] >> (8 * hi);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) csb[j] = nsb[j] >> (8 * hi);
             }
         };
 
@@ -315,15 +402,22 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * j * SLOTS / DN.  The scheduling barriers keep this interleave as
          * written. */
         auto step = [&](auto cur_c, auto d0_c, auto dn_c, const uint8_t *ns, int nks, uint32_t dso,
-                        uint32_t kb, const KV &kv) __attribute__((always_inline)) {
+                        uint32_t kb, const KV &kv, auto ks_c) __attribute__((always_inline)) {
             constexpr int CUR = decltype(cur_c)::value;
+            /* K-step of the tile the MFMAs work on (MX: its blocks are bytes
+             * 8 KS KB_STEP / 32 + 8 hi of the scale dwords) */
+            constexpr int KS = decltype(ks_c)::value;
             /* buffer the reads of this step fill */
             constexpr int TGT = SPREAD == 2 ? (CUR + 2) % NB : CUR ^ 1;
             constexpr int D0 = decltype(d0_c)::value, DN = decltype(dn_c)::value;
             constexpr int NM = FM * FN, NR = FM + FN;
+            /* MX: the last K-step, which reads the next tile's first
+             * fragments, also reads its FM + FN scale dwords, after them */
+            constexpr bool SCALES = MX && KS == KSTEPS - 1;
             /* SPREAD 2 puts the copies after the reads: NR + DN slots at least */
-            constexpr int SLOTS = SPREAD == 2 ? (NM > NR + DN ? NM : NR + DN)
-                                              : NM > (NR > DN ? NR : DN) ? NM : (NR > DN ? NR : DN);
+            constexpr int SLOTS0 = SPREAD == 2 ? (NM > NR + DN ? NM : NR + DN)
+                                               : NM > (NR > DN ? NR : DN) ? NM : (NR > DN ? NR : DN);
+            constexpr int SLOTS = SCALES && SLOTS0 < 2 * NR ? 2 * NR : SLOTS0;
             if constexpr (SPREAD == 2) {
                 /* this step's fragments (read two steps ago) are in; the NR
                  * reads of the previous step may still be outstanding */
@@ -341,6 +435,12 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
                     else if constexpr (!FP8)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                    else if constexpr (MX) {
+                        constexpr int SH = 8 * KS * (KB_STEP / 32);
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, (int)(csa[i] >> SH), 0,
+                            (int)(csb[j] >> SH));
+                    }
                     /* format fields FA / FB of the A and B operands; zero
                      * scales select the unscaled instruction */
                     else if constexpr (MI == 32)
@@ -354,6 +454,10 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     fa[TGT][t] = frag(ns + wm * WTM * RB, nks, t);
                 else if constexpr (t < NR)
                     fb[TGT][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
+                else if constexpr (SCALES && t < NR + FM)
+                    nsa[t - NR] = *(const uint32_t *)(ns + SCA_OFF + (wm * WTM + (t - NR) * MI + frow) * 4);
+                else if constexpr (SCALES && t < 2 * NR)
+                    nsb[t - NR - FM] = *(const uint32_t *)(ns + SCB_OFF + (wn * WTN + (t - NR - FM) * MI + frow) * 4);
                 if constexpr (DN > 0 && SPREAD == 2) {
                     /* copies after the fragment reads, spread over the rest
                      * of the step */
@@ -391,8 +495,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         auto tile2 = [&](uint32_t so, uint32_t nso, int32_t kt) __attribute__((always_inline)) {
             const uint8_t *cs = smem + so;
             const KV kv0{{false, false}};
-            step(IC<0>{}, IC<0>{}, IC<0>{}, cs, 2, so, 0u, kv0);
-            step(IC<1>{}, IC<0>{}, IC<0>{}, cs, 3, so, 0u, kv0);
+            step(IC<0>{}, IC<0>{}, IC<0>{}, cs, 2, so, 0u, kv0, IC<0>{});
+            step(IC<1>{}, IC<0>{}, IC<0>{}, cs, 3, so, 0u, kv0, IC<1>{});
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             /* tile kt+1 landed (its copies are the only ones outstanding) */
             wait_vmcnt<0>();
@@ -400,8 +504,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             asm volatile("" ::: "memory");
             const KV kv = kvalid(kt + 2);
             const uint32_t kb = (uint32_t)ktile(kt + 2) * RB;
-            step(IC<2>{}, IC<0>{}, IC<LOADS / 2>{}, smem + nso, 0, so, kb, kv);
-            step(IC<3>{}, IC<LOADS / 2>{}, IC<LOADS / 2>{}, smem + nso, 1, so, kb, kv);
+            step(IC<2>{}, IC<0>{}, IC<LOADS / 2>{}, smem + nso, 0, so, kb, kv, IC<2>{});
+            step(IC<3>{}, IC<LOADS / 2>{}, IC<LOADS / 2>{}, smem + nso, 1, so, kb, kv, IC<3>{});
         };
 
         auto tile = [&](auto pc, uint32_t so, uint32_t nso, uint32_t dso, int32_t kt) __attribute__((always_inline)) {
@@ -412,6 +516,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             const uint8_t *cs = smem + so;
             KV kv{{false, false}};
             uint32_t kb = 0;
+            take_scales();
             if constexpr (SP1) {
                 kv = kvalid(kt + STAGES - 1);
                 kb = (uint32_t)ktile(kt + STAGES - 1) * RB;
@@ -420,7 +525,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 constexpr int ks = decltype(kc)::value;
                 constexpr int D0 = SP1 ? ks * LOADS / KSTEPS : 0;
                 constexpr int DN = SP1 ? (ks + 1) * LOADS / KSTEPS - D0 : 0;
-                step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, ks + 1, dso, kb, kv);
+                step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, ks + 1, dso, kb, kv, IC<ks>{});
             });
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             /* tile kt+1 landed: later copies may still be in flight (SPREAD
@@ -430,13 +535,14 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             if constexpr (SP1) {
-                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, 0, dso, kb, kv);
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, 0, dso, kb, kv,
+                     IC<KSTEPS - 1>{});
             } else if constexpr (SPREAD == 3) {
-                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<0>{}, smem + nso, 0, so, 0u, kv);
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<0>{}, smem + nso, 0, so, 0u, kv, IC<KSTEPS - 1>{});
             } else {
                 kv = kvalid(kt + STAGES);
                 kb = (uint32_t)ktile(kt + STAGES) * RB;
-                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, 0, so, kb, kv);
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, 0, so, kb, kv, IC<KSTEPS - 1>{});
             }
         };
         auto next_stage = [](uint32_t so) __attribute__((always_inline)) {
@@ -486,6 +592,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
 #pragma unroll
                 for (int j = 0; j < FN; ++j) fb[b][j] = frag(smem + A_BYTES + wn * WTN * RB, b, j);
             });
+            read_scales(smem);
             uint32_t so = 0, dso = (STAGES - 1) * STAGE_BYTES;
             if constexpr (SPREAD == 2) {
                 for (; kt < nkt; ++kt) {
@@ -816,6 +923,36 @@ __global__ __launch_bounds__(256) void pack_transpose_kernel(PackParams pk)
     }
 }
 
+/*
+ * Block-scale regrouping for the MX tiles: src holds batch x rows x (4 nK)
+ * E8M0 bytes (a row's four scales of K-tile kt are bytes 4 kt .. 4 kt + 3,
+ * one dword); dst[b][kt][row] receives that dword.  Block (b, row block of
+ * 64, K-tile block of 32) moves a 64 x 32 dword tile through LDS: reads of
+ * 128 contiguous bytes per row, writes of 256 contiguous bytes per K-tile.
+ */
+__global__ __launch_bounds__(256) void pack_scales_kernel(ScalePackParams sp)
+{
+    __shared__ uint32_t t[64][33];
+    const int32_t rblocks = (sp.rows + 63) / 64, kblocks = (sp.nK + 31) / 32;
+    int32_t bid = blockIdx.x;
+    const int32_t kb = bid % kblocks;
+    bid /= kblocks;
+    const int32_t rb = bid % rblocks;
+    const int32_t b = bid / rblocks;
+    const int32_t r0 = rb * 64, k0 = kb * 32;
+    const uint32_t *src = (const uint32_t *)sp.src + (int64_t)b * sp.rows * sp.nK;
+    uint32_t *dst = sp.dst + (int64_t)b * sp.rows * sp.nK;
+    for (int32_t i = threadIdx.x; i < 64 * 32; i += 256) {
+        const int32_t r = i / 32, k = i % 32;
+        if (r0 + r < sp.rows && k0 + k < sp.nK) t[r][k] = src[(int64_t)(r0 + r) * sp.nK + k0 + k];
+    }
+    __syncthreads();
+    for (int32_t i = threadIdx.x; i < 64 * 32; i += 256) {
+        const int32_t k = i / 64, r = i % 64;
+        if (r0 + r < sp.rows && k0 + k < sp.nK) dst[(int64_t)(k0 + k) * sp.rows + r0 + r] = t[r][k];
+    }
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N, int64_t ldc,
                                                     int64_t stride_c, int32_t batch, int32_t esize)
 {
@@ -834,34 +971,35 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
+template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
 static hipError_t launch_one(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, FMT>), dim3(p.s.grid),
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, FMT>), dim3(p.s.grid),
                        dim3((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 /* bf16 tiles have one instantiation; 8-bit tiles one per operand-format pair */
-template <int TM, int TN, bool FP8, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
+template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
 static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stream)
 {
-    if constexpr (FP8) {
+    if constexpr (EL != 0) {
         switch (fmt) {
-        case 0: return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
-        case 1: return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 1>(p, stream);
-        case 2: return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 2>(p, stream);
+        case 0: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+        case 1: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 1>(p, stream);
+        case 2: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 2>(p, stream);
         default: return hipErrorInvalidValue;
         }
     } else {
         if (fmt != 0) return hipErrorInvalidValue;
-        return launch_one<TM, TN, FP8, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+        return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
     }
 }
 
 /* Instantiations, in tile-table order (csrc/tiles.h):
- * id, TM, TN, E4M3, groups per CU, K-tile bytes, stages, waves along M, N,
- * copies spread over the K-steps, MFMA block edge */
+ * id, TM, TN, element class (false bf16, true 8-bit, 2 block-scaled 8-bit),
+ * groups per CU, K-tile bytes, stages, waves along M, N, copy schedule,
+ * MFMA block edge */
 #define GEMM355_TILES(X)                                                                          \
     X(0, 256, 256, false, 1, 128, 2, 2, 2, 0, 32)                                                       \
     X(1, 128, 128, false, 2, 128, 2, 2, 2, 0, 32)                                                       \
@@ -910,11 +1048,14 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(44, 256, 128, false, 1, 128, 3, 2, 2, 3, 32)                                                  \
     X(45, 256, 128, false, 1, 128, 3, 2, 2, 3, 16)                                                  \
     X(46, 256, 128, true, 1, 128, 3, 2, 2, 3, 32)                                                   \
-    X(47, 256, 128, false, 1, 128, 3, 2, 2, 0, 32)
+    X(47, 256, 128, false, 1, 128, 3, 2, 2, 0, 32)                                                  \
+    X(48, 256, 256, 2, 1, 128, 2, 2, 2, 0, 32)                                                      \
+    X(49, 128, 128, 2, 2, 128, 2, 2, 2, 0, 32)                                                      \
+    X(50, 128, 128, 2, 1, 128, 4, 2, 2, 0, 32)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi)                                                      \
-    static_assert(kTiles[id].dtype_class == (f8 ? 1 : 0) && kTiles[id].TM == tm &&               \
+    static_assert(kTiles[id].dtype_class == (int)(f8) && kTiles[id].TM == tm &&                  \
                       kTiles[id].TN == tn && kTiles[id].min_blocks == mb &&                      \
                       kTiles[id].row_bytes == rb && kTiles[id].stages == st &&                   \
                       kTiles[id].waves_m == wm && kTiles[id].waves_n == wn &&                    \
@@ -975,6 +1116,13 @@ hipError_t launch_pack(const PackParams &pk, hipStream_t stream)
         hipLaunchKernelGGL(pack_transpose_kernel, dim3((uint32_t)((int64_t)pk.batch * rblocks * kblocks)), dim3(256), 0,
                            stream, pk);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_scales(const ScalePackParams &sp, hipStream_t stream)
+{
+    const int64_t blocks = (int64_t)sp.batch * ((sp.rows + 63) / 64) * ((sp.nK + 31) / 32);
+    hipLaunchKernelGGL(pack_scales_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
 

@@ -25,19 +25,33 @@ struct Plan {
     size_t ws_partial_off, ws_partial_bytes;
     size_t ws_pack_a_off, ws_pack_a_bytes;
     size_t ws_pack_b_off, ws_pack_b_bytes;
+    /* MX: block scales regrouped K-tile-major, [batch][nK][rows] dwords */
+    size_t ws_scale_a_off, ws_scale_a_bytes;
+    size_t ws_scale_b_off, ws_scale_b_bytes;
     int32_t reduce_tiles;       /* blocks of the combine kernel (0: none)   */
     int32_t reduce_tail;        /* 1: combine the tail tiles                */
 };
 
-/* Element-type queries. */
-inline bool dtype_fp8(gemm355_dtype d) { return d >= GEMM355_E4M3_F32 && d <= GEMM355_E4M3_E5M2_BF16; }
-inline bool dtype_out_bf16(gemm355_dtype d)
-{
-    return d == GEMM355_BF16_BF16 || d == GEMM355_E4M3_BF16 || d == GEMM355_E5M2_BF16 || d == GEMM355_E4M3_E5M2_BF16;
-}
+/* Element-type queries.  Dtypes come in pairs (fp32 C, bf16 C). */
+constexpr int kNumDtypes = 14;
+/* 8-bit inputs, with or without block scales */
+inline bool dtype_fp8(gemm355_dtype d) { return d >= GEMM355_E4M3_F32 && d <= GEMM355_MXE4M3_E5M2_BF16; }
+/* block-scaled 8-bit inputs */
+inline bool dtype_mx(gemm355_dtype d) { return d >= GEMM355_MXE4M3_F32 && d <= GEMM355_MXE4M3_E5M2_BF16; }
+inline bool dtype_out_bf16(gemm355_dtype d) { return ((int)d & 1) != 0; }
+/* tile-table class: 0 bf16, 1 8-bit, 2 block-scaled 8-bit */
+inline int32_t dtype_class_of(gemm355_dtype d) { return dtype_mx(d) ? 2 : dtype_fp8(d) ? 1 : 0; }
 /* 8-bit format codes of the MFMA operands: 0 E4M3, 1 E5M2 */
-inline int32_t dtype_fmt_a(gemm355_dtype d) { return (d == GEMM355_E5M2_F32 || d == GEMM355_E5M2_BF16) ? 1 : 0; }
-inline int32_t dtype_fmt_b(gemm355_dtype d) { return (d >= GEMM355_E5M2_F32 && d <= GEMM355_E4M3_E5M2_BF16) ? 1 : 0; }
+inline int32_t dtype_fmt_a(gemm355_dtype d)
+{
+    return (d == GEMM355_E5M2_F32 || d == GEMM355_E5M2_BF16 || d == GEMM355_MXE5M2_F32 ||
+            d == GEMM355_MXE5M2_BF16) ? 1 : 0;
+}
+inline int32_t dtype_fmt_b(gemm355_dtype d)
+{
+    return ((d >= GEMM355_E5M2_F32 && d <= GEMM355_E4M3_E5M2_BF16) ||
+            (d >= GEMM355_MXE5M2_F32 && d <= GEMM355_MXE4M3_E5M2_BF16)) ? 1 : 0;
+}
 
 /* Validate `a` and plan it for S compute units.  Never touches a device. */
 gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &out);

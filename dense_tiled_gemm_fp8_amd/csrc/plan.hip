@@ -287,7 +287,13 @@ gemm355_status check_pointers(const gemm355_args &a)
         return GEMM355_EALIGN;
     if (((uintptr_t)a.scale_a & 3u) != 0 || ((uintptr_t)a.scale_b & 3u) != 0) return GEMM355_EALIGN;
     if (((uintptr_t)a.unit_stamps & 7u) != 0) return GEMM355_EALIGN;
+    if (!dtype_mx(a.dtype) && (a.block_scale_a || a.block_scale_b)) return GEMM355_EINVAL;
     if (K == 0) return GEMM355_OK;
+    if (dtype_mx(a.dtype)) {
+        if (!a.block_scale_a || !a.block_scale_b) return GEMM355_EINVAL;
+        if (((uintptr_t)a.block_scale_a & 3u) != 0 || ((uintptr_t)a.block_scale_b & 3u) != 0)
+            return GEMM355_EALIGN;
+    }
     /* C must not overlap A or B (byte ranges spanned by all batch entries) */
     const uintptr_t c_lo = (uintptr_t)a.C;
     const uintptr_t c_hi = c_lo + (uintptr_t)(((batch - 1) * a.stride_c + (M - 1) * a.ldc + N) * out_esize);
@@ -298,13 +304,21 @@ gemm355_status check_pointers(const gemm355_args &a)
     const uintptr_t b_lo = (uintptr_t)a.B;
     const uintptr_t b_hi = b_lo + (uintptr_t)(((batch - 1) * a.stride_b + (b_rows - 1) * a.ldb + b_cols) * esize);
     if ((c_lo < a_hi && a_lo < c_hi) || (c_lo < b_hi && b_lo < c_hi)) return GEMM355_EINVAL;
+    if (dtype_mx(a.dtype)) {
+        /* block-scale arrays: batch * rows * ceil(K / 32) bytes */
+        const uintptr_t sa_lo = (uintptr_t)a.block_scale_a;
+        const uintptr_t sa_hi = sa_lo + (uintptr_t)(batch * M * ((K + 31) / 32));
+        const uintptr_t sb_lo = (uintptr_t)a.block_scale_b;
+        const uintptr_t sb_hi = sb_lo + (uintptr_t)(batch * N * ((K + 31) / 32));
+        if ((c_lo < sa_hi && sa_lo < c_hi) || (c_lo < sb_hi && sb_lo < c_hi)) return GEMM355_EINVAL;
+    }
     return GEMM355_OK;
 }
 
 gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
 {
     memset(&P, 0, sizeof P);
-    if ((int)a.dtype < 0 || (int)a.dtype > 7) return GEMM355_EINVAL;
+    if ((int)a.dtype < 0 || (int)a.dtype >= kNumDtypes) return GEMM355_EINVAL;
     if ((int)a.layout < 0 || (int)a.layout > 3) return GEMM355_EINVAL;
     if (a.M < 0 || a.N < 0 || a.K < 0 || a.batch < 1) return GEMM355_EINVAL;
     if (a.split_k < 0 || a.persistent < -1 || a.persistent > 1) return GEMM355_EINVAL;
@@ -313,7 +327,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     if (a.stride_a < 0 || a.stride_b < 0 || a.stride_c < 0) return GEMM355_EINVAL;
 
     const bool fp8 = dtype_fp8(a.dtype);
-    const int32_t dclass = fp8 ? 1 : 0;
+    const int32_t dclass = dtype_class_of(a.dtype);
     const int32_t esize = fp8 ? 1 : 2;
     const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
@@ -325,6 +339,12 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     if (a.ldb < std::max<int64_t>(1, b_col ? K : N)) return GEMM355_EINVAL;
     if (a.ldc < std::max<int64_t>(1, N)) return GEMM355_EINVAL;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim) return GEMM355_EUNSUPPORTED;
+    /* block scales are read one dword (four 32-value blocks) per row and
+     * K-tile of 128 values */
+    if (dtype_mx(a.dtype) && K % 128 != 0) return GEMM355_EUNSUPPORTED;
+    /* the regrouped scales of one batch entry are addressed with 32-bit
+     * offsets */
+    if (dtype_mx(a.dtype) && std::max(M, N) * (K / 32) > kMaxOffset) return GEMM355_EUNSUPPORTED;
 
     P.esize = esize;
     P.out_esize = out_esize;
@@ -528,6 +548,12 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     carve(P.ws_pack_a_bytes, P.ws_pack_a_off);
     P.ws_pack_b_bytes = P.pack_b ? (size_t)(batch * N * P.ldb_b) : 0;
     carve(P.ws_pack_b_bytes, P.ws_pack_b_off);
+    /* block scales: one dword (four 32-value blocks) per row and K-tile */
+    const bool mx = dtype_mx(a.dtype) && work && K > 0;
+    P.ws_scale_a_bytes = mx ? (size_t)(batch * M * (K / 32)) : 0;
+    carve(P.ws_scale_a_bytes, P.ws_scale_a_off);
+    P.ws_scale_b_bytes = mx ? (size_t)(batch * N * (K / 32)) : 0;
+    carve(P.ws_scale_b_bytes, P.ws_scale_b_off);
     o.workspace_bytes = off;
     if (!work) {
         o.units = 0;

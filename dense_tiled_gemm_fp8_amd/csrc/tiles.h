@@ -20,7 +20,8 @@
 namespace g355 {
 
 struct TileCfg {
-    int32_t dtype_class;   /* 0 bf16 inputs, 1 E4M3 inputs                  */
+    int32_t dtype_class;   /* 0 bf16 inputs, 1 8-bit inputs, 2 8-bit inputs
+                              with E8M0 block scales (MX)                   */
     int32_t TM, TN, TK;
     int32_t row_bytes;     /* RB: K bytes per tile row per stage             */
     int32_t stages;
@@ -36,7 +37,8 @@ struct TileCfg {
                               K-tiles ahead, and the waves_m x waves_n MFMA
                               wavefronts only read LDS (3 stages or more)  */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
-    int32_t lds_bytes;     /* stages * (TM + TN) * RB                        */
+    int32_t lds_bytes;     /* stages * (TM + TN) * RB, plus 4 bytes of block
+                              scales per row and stage for MX               */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
     int32_t vgpr_budget;   /* 512 / (min_blocks * tile_waves / 4): registers
                               per lane one wave may hold                    */
@@ -119,6 +121,11 @@ constexpr TileCfg kTiles[] = {
     {0, 256, 128, 64, 128, 3, 2, 2, 3, 16, 3 * (256 + 128) * 128, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
     {1, 256, 128, 128, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
     {0, 256, 128, 64, 128, 3, 2, 2, 0, 32, 3 * (256 + 128) * 128, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
+    /* block-scaled 8-bit (MX): the 8-bit tiles with the scale dwords of
+     * each K-tile in the stage */
+    {2, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 132, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
+    {2, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 132, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {2, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 132, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

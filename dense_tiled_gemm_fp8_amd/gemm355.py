@@ -25,7 +25,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP = range(6)
 # dtypes (input -> output)
 (BF16_F32, BF16_BF16, E4M3_F32, E4M3_BF16, E5M2_F32, E5M2_BF16, E4M3_E5M2_F32,
- E4M3_E5M2_BF16) = range(8)
+ E4M3_E5M2_BF16, MXE4M3_F32, MXE4M3_BF16, MXE5M2_F32, MXE5M2_BF16, MXE4M3_E5M2_F32,
+ MXE4M3_E5M2_BF16) = range(14)
 # 8-bit formats and source types of the quantiser
 FP8_E4M3, FP8_E5M2 = range(2)
 SRC_F32, SRC_BF16 = range(2)
@@ -47,6 +48,7 @@ class gemm355_args(ctypes.Structure):
         ("split_k", _i32), ("persistent", _i32), ("tile", _i32), ("cus", _i32),
         ("workspace", _vp), ("workspace_bytes", _sz),
         ("unit_stamps", _vp),
+        ("block_scale_a", _vp), ("block_scale_b", _vp),
     ]
 
 
@@ -142,7 +144,8 @@ def gemm355_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, layout=A_ROW_B_COL, spl
 def make_args(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, dtype=BF16_F32,
               layout=A_ROW_B_COL, batch=1, stride_a=0, stride_b=0, stride_c=0, scale_a=None,
               scale_b=None, split_k=0, persistent=-1, tile=-1, cus=0, workspace=None,
-              workspace_bytes=0, unit_stamps=None) -> gemm355_args:
+              workspace_bytes=0, unit_stamps=None, block_scale_a=None,
+              block_scale_b=None) -> gemm355_args:
     """Fill a gemm355_args; leading dimensions default to the packed ones."""
     a_row = layout in (A_ROW_B_COL, A_ROW_B_ROW)
     b_col = layout in (A_ROW_B_COL, A_COL_B_COL)
@@ -154,7 +157,8 @@ def make_args(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, dty
         ldc = max(1, N)
     return gemm355_args(M, N, K, _ptr(A), lda, stride_a, _ptr(B), ldb, stride_b, _ptr(C), ldc,
                         stride_c, batch, _ptr(scale_a), _ptr(scale_b), dtype, layout, split_k,
-                        persistent, tile, cus, _ptr(workspace), workspace_bytes, _ptr(unit_stamps))
+                        persistent, tile, cus, _ptr(workspace), workspace_bytes, _ptr(unit_stamps),
+                        _ptr(block_scale_a), _ptr(block_scale_b))
 
 
 def gemm355_gemm_ex(args: gemm355_args, stream=None) -> None:

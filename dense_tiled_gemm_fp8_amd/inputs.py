@@ -78,6 +78,35 @@ def to_e4m3_codes(x: np.ndarray, scale: Optional[float] = None) -> Tuple[np.ndar
     return to_fp8_codes(x, "e4m3", scale)
 
 
+FP8_EMAX = {"e4m3": 8, "e5m2": 15}     # exponent of the largest finite value
+
+
+def to_mx_codes(x: np.ndarray, fmt: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Block-scaled quantisation of a rows x K array (the input recipe of
+    the block-scaled dtypes; OCP MX v1.0 conversion): for each block of 32
+    values along K, the E8M0 scale is 2^(floor(log2 amax) - emax) with emax
+    the element format's largest exponent (8 for E4M3, 15 for E5M2), code
+    floor(log2 amax) - emax + 127 clamped to [0, 254] (127 for an all-zero
+    block); the elements are x / scale clamped to the format's largest
+    magnitude and rounded to nearest even by torch's CPU cast.  K must be a
+    multiple of 32.  Returns (uint8 element codes rows x K, uint8 scale
+    codes rows x K / 32)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    rows, K = x64.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x64.reshape(rows, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    _, e = np.frexp(amax)                 # amax = m 2^e, 0.5 <= m < 1
+    code = np.where(amax > 0, e - 1 - FP8_EMAX[fmt] + 127, 127)
+    code = np.clip(code, 0, 254).astype(np.uint8)
+    scale = np.ldexp(1.0, code.astype(np.int64) - 127)
+    F = FP8_MAX[fmt]
+    y = np.clip(blocks / scale[:, :, None], -F, F).reshape(rows, K).astype(np.float32)
+    q = torch.from_numpy(np.ascontiguousarray(y)).to(_TORCH_FP8[fmt]).view(torch.uint8).numpy()
+    return q, code
+
+
 def small_int_codes(gen: np.random.Generator, shape, fmt: str, lo: int = -4,
                     hi: int = 4) -> np.ndarray:
     """Integers in [lo, hi], exactly representable in bf16, E4M3 and E5M2
@@ -112,24 +141,37 @@ class Operands:
     M: int
     N: int
     K: int
-    fmt: str                      # "bf16", "e4m3", "e5m2" or "e4m3e5m2" (A E4M3, B E5M2)
+    fmt: str                      # "bf16", "e4m3", "e5m2" or "e4m3e5m2" (A E4M3, B E5M2);
+                                  # "mx" + one of the 8-bit names: block-scaled
     A: np.ndarray                 # (batch, M, K) or (M, K)
     B: np.ndarray                 # (batch, N, K) or (N, K)  (column-major B)
     scale_a: List[float] = field(default_factory=list)
     scale_b: List[float] = field(default_factory=list)
     seeds: Tuple[int, int] = (0, 0)
+    # block-scaled formats: E8M0 scale codes, (batch,) M x K/32 and N x K/32
+    bsa: Optional[np.ndarray] = None
+    bsb: Optional[np.ndarray] = None
 
     @property
     def batch(self) -> int:
         return self.A.shape[0] if self.A.ndim == 3 else 1
 
     @property
+    def mx(self) -> bool:
+        return self.fmt.startswith("mx")
+
+    @property
+    def elem(self) -> str:
+        """The element format name without the block-scaling prefix."""
+        return self.fmt[2:] if self.mx else self.fmt
+
+    @property
     def fmt_a(self) -> str:
-        return "e4m3" if self.fmt == "e4m3e5m2" else self.fmt
+        return "e4m3" if self.elem == "e4m3e5m2" else self.elem
 
     @property
     def fmt_b(self) -> str:
-        return "e5m2" if self.fmt == "e4m3e5m2" else self.fmt
+        return "e5m2" if self.elem == "e4m3e5m2" else self.elem
 
 
 def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
@@ -139,6 +181,7 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
     ga, gb = rng(seed_a), rng(seed_b)
     nb = max(batch, 1)
     As, Bs, sa, sb = [], [], [], []
+    bsa_l, bsb_l = [], []
     for _ in range(nb):
         xa = draw(ga, (M, K), dist, K)
         xb = draw(gb, (N, K), dist, K)
@@ -147,6 +190,17 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
             Bs.append(to_bf16_codes(xb))
             sa.append(1.0)
             sb.append(1.0)
+        elif fmt.startswith("mx"):
+            fa = "e5m2" if fmt == "mxe5m2" else "e4m3"
+            fb = "e4m3" if fmt == "mxe4m3" else "e5m2"
+            qa, ca = to_mx_codes(xa, fa)
+            qb, cb = to_mx_codes(xb, fb)
+            As.append(qa)
+            Bs.append(qb)
+            sa.append(1.0)
+            sb.append(1.0)
+            bsa_l.append(ca)
+            bsb_l.append(cb)
         elif fmt in ("e4m3", "e5m2", "e4m3e5m2"):
             qa, s_a = to_fp8_codes(xa, "e4m3" if fmt != "e5m2" else "e5m2")
             qb, s_b = to_fp8_codes(xb, "e5m2" if fmt != "e4m3" else "e4m3")
@@ -158,9 +212,13 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
             raise ValueError(fmt)
     if batch:
         A, B = np.stack(As), np.stack(Bs)
+        bsa = np.stack(bsa_l) if bsa_l else None
+        bsb = np.stack(bsb_l) if bsb_l else None
     else:
         A, B = As[0], Bs[0]
-    return Operands(M, N, K, fmt, A, B, sa, sb, (seed_a, seed_b))
+        bsa = bsa_l[0] if bsa_l else None
+        bsb = bsb_l[0] if bsb_l else None
+    return Operands(M, N, K, fmt, A, B, sa, sb, (seed_a, seed_b), bsa, bsb)
 
 
 @dataclass(frozen=True)

@@ -43,7 +43,8 @@ typedef enum gemm355_status {
                                   split factor, or C overlapping A/B */
     GEMM355_EALIGN = 2,        /* pointer not aligned to its element size */
     GEMM355_EUNSUPPORTED = 3,  /* extents beyond the 32-bit offsets the
-                                  kernels use, or an unknown tile id */
+                                  kernels use, an unknown tile id, or an MX
+                                  dtype with K not a multiple of 128 */
     GEMM355_ENOMEM = 4,        /* caller workspace smaller than the plan's
                                   workspace_bytes, or allocation failed */
     GEMM355_EHIP = 5           /* a HIP runtime call failed (no device,
@@ -64,7 +65,18 @@ typedef enum gemm355_dtype {
     GEMM355_E5M2_F32 = 4,   /* E5M2 A, B; fp32 C                              */
     GEMM355_E5M2_BF16 = 5,  /* E5M2 A, B; bf16 C                              */
     GEMM355_E4M3_E5M2_F32 = 6,  /* E4M3 A, E5M2 B; fp32 C                     */
-    GEMM355_E4M3_E5M2_BF16 = 7  /* E4M3 A, E5M2 B; bf16 C                     */
+    GEMM355_E4M3_E5M2_BF16 = 7, /* E4M3 A, E5M2 B; bf16 C                     */
+    /* Block-scaled ("microscaled", the precision-table row after the FP8
+     * pair on page "The Tensor Core"; format as in the OCP Microscaling
+     * specification v1.0): every 32 consecutive K-values of a row of A and
+     * of a column of B share one E8M0 scale 2^(e - 127), given in
+     * block_scale_a / block_scale_b.  K must be a multiple of 128. */
+    GEMM355_MXE4M3_F32 = 8,     /* MX E4M3 A, B; fp32 C                       */
+    GEMM355_MXE4M3_BF16 = 9,    /* MX E4M3 A, B; bf16 C                       */
+    GEMM355_MXE5M2_F32 = 10,    /* MX E5M2 A, B; fp32 C                       */
+    GEMM355_MXE5M2_BF16 = 11,   /* MX E5M2 A, B; bf16 C                       */
+    GEMM355_MXE4M3_E5M2_F32 = 12,  /* MX E4M3 A, MX E5M2 B; fp32 C            */
+    GEMM355_MXE4M3_E5M2_BF16 = 13  /* MX E4M3 A, MX E5M2 B; bf16 C            */
 } gemm355_dtype;
 
 /* 8-bit formats of the quantiser. */
@@ -128,6 +140,16 @@ typedef struct gemm355_args {
                                  measuring how evenly the units fill the
                                  device and how many cycles a unit takes.
                                  8-byte aligned (EALIGN).                  */
+    /* Block scales of the MX dtypes (NULL otherwise, else EINVAL): E8M0
+     * bytes, dense, block_scale_a[g][i][k / 32] for row i of A and
+     * block_scale_b[g][j][k / 32] for column j of B (rows of K / 32 bytes,
+     * batch entries M * K / 32 and N * K / 32 bytes apart), whatever the
+     * element layout.  Device memory, 4-byte aligned (EALIGN); NULL with
+     * M, N, K > 0 is EINVAL; overlapping C is EINVAL.  Scale 255 (NaN)
+     * makes the affected outputs NaN.  The per-tensor scale_a / scale_b
+     * still multiply the result when given. */
+    const uint8_t *block_scale_a;
+    const uint8_t *block_scale_b;
 } gemm355_args;
 
 /* Everything the planner decided for one call.  Efficiencies are exact
@@ -170,7 +192,9 @@ typedef struct gemm355_plan_t {
  * in a second kernel, summing slices in ascending order.  The persistent
  * mode (same section) launches S*b workgroups that loop over the work units.
  * Scratch is library-owned here (allocated on first use per device, grown
- * when needed, freed at unload).
+ * when needed, freed at unload).  The MX dtypes need block scales, which
+ * only gemm355_gemm_ex takes: here they fail with EINVAL (unless M, N or K
+ * is 0).
  * Errors: EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP as listed above.
  */
 GEMM355_API gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K,
@@ -186,6 +210,10 @@ GEMM355_API gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K,
  * (alpha_g = scale_a[g] * scale_b[g]), a forced tile, and caller-provided
  * scratch (needs at least plan.workspace_bytes; ENOMEM otherwise).
  * The batch strides must keep entries from overlapping C with A or B.
+ * MX dtypes: the block scales are first regrouped on the device into the
+ * scratch (one dword per row and K-tile of 128 values, K-tile-major), then
+ * the main loop stages them through LDS beside the operand tiles and feeds
+ * them to the scaled matrix instruction.
  */
 GEMM355_API gemm355_status gemm355_gemm_ex(const gemm355_args *args, void *stream);
 
@@ -230,7 +258,8 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
                             int64_t *kt_begin, int64_t *kt_end);
 
 /* Number of entries in the tile table, and one entry's parameters.
- * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2). */
+ * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2), 2 = block-scaled
+ * 8-bit inputs (the MX dtypes). */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
                                  int32_t *T_M, int32_t *T_N, int32_t *T_K,

@@ -3,7 +3,8 @@ call libgemm355 through its C ABI, bring C back, compare with the oracle.
 
 Tolerances (per element, W = |alpha| sum_k |a_ik b_kj| from the oracle):
   bf16 inputs:             |C_gpu - C_ref| <= 1e-3 W + 1e-6
-  8-bit (E4M3, E5M2) inputs: |C_gpu - C_ref| <= 2e-2 W
+  8-bit (E4M3, E5M2) inputs, with or without block scales:
+                           |C_gpu - C_ref| <= 2e-2 W
 """
 from __future__ import annotations
 
@@ -14,9 +15,11 @@ import torch
 
 from dense_tiled_gemm_fp8_amd import gemm355 as g
 from dense_tiled_gemm_fp8_amd import inputs
+from oracle import mx as mx_oracle
 from oracle import reference as oracle
 
-TOL = {"bf16": (1e-3, 1e-6), "e4m3": (2e-2, 0.0), "e5m2": (2e-2, 0.0), "e4m3e5m2": (2e-2, 0.0)}
+TOL = {"bf16": (1e-3, 1e-6), "e4m3": (2e-2, 0.0), "e5m2": (2e-2, 0.0), "e4m3e5m2": (2e-2, 0.0),
+       "mxe4m3": (2e-2, 0.0), "mxe5m2": (2e-2, 0.0), "mxe4m3e5m2": (2e-2, 0.0)}
 
 
 def say(*a):
@@ -36,7 +39,9 @@ def dev(codes: np.ndarray) -> torch.Tensor:
 
 def out_dtype(fmt: str, out: str) -> int:
     table = {"bf16": (g.BF16_F32, g.BF16_BF16), "e4m3": (g.E4M3_F32, g.E4M3_BF16),
-             "e5m2": (g.E5M2_F32, g.E5M2_BF16), "e4m3e5m2": (g.E4M3_E5M2_F32, g.E4M3_E5M2_BF16)}
+             "e5m2": (g.E5M2_F32, g.E5M2_BF16), "e4m3e5m2": (g.E4M3_E5M2_F32, g.E4M3_E5M2_BF16),
+             "mxe4m3": (g.MXE4M3_F32, g.MXE4M3_BF16), "mxe5m2": (g.MXE5M2_F32, g.MXE5M2_BF16),
+             "mxe4m3e5m2": (g.MXE4M3_E5M2_F32, g.MXE4M3_E5M2_BF16)}
     return table[fmt][1 if out == "bf16" else 0]
 
 
@@ -57,13 +62,17 @@ def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: in
     if C is None:
         C = empty_c(batch, M, N, out)
     sa = sb = None
-    if scales and ops.fmt != "bf16":
+    if scales and ops.fmt != "bf16" and not ops.mx:
         sa = torch.tensor(ops.scale_a, dtype=torch.float32, device="cuda")
         sb = torch.tensor(ops.scale_b, dtype=torch.float32, device="cuda")
+    bsa = bsb = None
+    if ops.mx:
+        bsa, bsb = dev(ops.bsa), dev(ops.bsb)
     ws = None
     args = g.make_args(M, N, K, A=A_dev, lda=lda, B=B_dev, ldb=ldb, C=C, dtype=out_dtype(ops.fmt, out),
                        layout=layout, batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N,
-                       scale_a=sa, scale_b=sb, split_k=split_k, persistent=persistent, tile=tile)
+                       scale_a=sa, scale_b=sb, split_k=split_k, persistent=persistent, tile=tile,
+                       block_scale_a=bsa, block_scale_b=bsb)
     if workspace == "caller":
         p = g.gemm355_plan(args)
         if p["workspace_bytes"]:
@@ -76,7 +85,7 @@ def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: in
 
 
 def alpha_of(ops: inputs.Operands, bi: int = 0) -> float:
-    if ops.fmt != "bf16":
+    if ops.fmt != "bf16" and not ops.mx:
         return float(np.float32(ops.scale_a[bi]) * np.float32(ops.scale_b[bi]))
     return 1.0
 
@@ -86,6 +95,10 @@ def oracle_full(ops: inputs.Operands, bi: int = 0, alpha=None):
     B = ops.B[bi] if ops.B.ndim == 3 else ops.B
     if alpha is None:
         alpha = alpha_of(ops, bi)
+    if ops.mx:
+        bsa = ops.bsa[bi] if ops.bsa.ndim == 3 else ops.bsa
+        bsb = ops.bsb[bi] if ops.bsb.ndim == 3 else ops.bsb
+        return mx_oracle.gemm(A, bsa, B, bsb, ops.fmt_a, ops.fmt_b, alpha=alpha)
     return oracle.gemm(ops.M, ops.N, ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, alpha=alpha,
                        **fmt_kw(ops))
 
@@ -93,6 +106,10 @@ def oracle_full(ops: inputs.Operands, bi: int = 0, alpha=None):
 def oracle_entries(ops: inputs.Operands, rows, cols, bi: int = 0):
     A = ops.A[bi] if ops.A.ndim == 3 else ops.A
     B = ops.B[bi] if ops.B.ndim == 3 else ops.B
+    if ops.mx:
+        bsa = ops.bsa[bi] if ops.bsa.ndim == 3 else ops.bsa
+        bsb = ops.bsb[bi] if ops.bsb.ndim == 3 else ops.bsb
+        return mx_oracle.gemm_entries(A, bsa, B, bsb, rows, cols, ops.fmt_a, ops.fmt_b, alpha=alpha_of(ops, bi))
     return oracle.gemm_entries(ops.K, A.reshape(-1), ops.K, B.reshape(-1), ops.K, rows, cols,
                                alpha=alpha_of(ops, bi), **fmt_kw(ops))
 

@@ -86,8 +86,10 @@ PLAN_SHAPES = [
     (4097, 4095, 4104, 1, 0), (1000, 3000, 777, 1, 0), (256, 256, 65536, 1, 0),
     (128, 512, 131072, 1, 0), (64, 64, 262144, 1, 0), (8192, 8192, 8192, 1, 2),
     (512, 1024, 4096, 64, 2), (1, 1, 1, 1, 0), (17, 300, 40, 3, 2), (5000, 33, 9000, 1, 0),
-    (1000, 900, 700, 1, 3), (64, 4096, 8192, 2, 4),
+    (1000, 900, 700, 1, 3), (64, 4096, 8192, 2, 4), (8192, 8192, 8192, 1, 5),
+    (512, 1024, 4096, 64, 5), (1000, 900, 768, 1, 5), (100, 70, 131072, 1, 5),
 ]
+PLAN_DTYPES = ["BF16_F32", "BF16_BF16", "E4M3_F32", "E5M2_F32", "E4M3_E5M2_BF16", "MXE4M3_F32"]
 
 KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1, persistent=1),
          dict(split_k=5, persistent=1), dict(tile=1), dict(tile=2, persistent=1, split_k=1)]
@@ -96,6 +98,10 @@ KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1,
 def _plan_and_check(g, M, N, K, batch, dtype, knobs):
     if "tile" in knobs and dtype in (g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16):
         knobs = dict(knobs, tile=knobs["tile"] + 3)
+    elif "tile" in knobs and dtype == g.MXE4M3_F32:
+        knobs = dict(knobs, tile=knobs["tile"] + 48)           # the block-scaled 128x128 tiles
+    if dtype == g.MXE4M3_F32:
+        knobs = dict(knobs, block_scale_a=0x300000000000, block_scale_b=0x380000000000)
     a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, dtype=dtype,
                     batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N, cus=256, **knobs)
     p = g.gemm355_plan(a)
@@ -136,14 +142,14 @@ def _plan_and_check(g, M, N, K, batch, dtype, knobs):
 
 @pytest.mark.parametrize("M,N,K,batch,dt", PLAN_SHAPES)
 def test_plan_bookkeeping(g, M, N, K, batch, dt):
-    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16][dt]
+    dtype = getattr(g, PLAN_DTYPES[dt])
     for knobs in KNOBS:
         _plan_and_check(g, M, N, K, batch, dtype, knobs)
 
 
 @pytest.mark.parametrize("M,N,K,batch,dt", [s for s in PLAN_SHAPES if s[0] * s[1] * s[3] <= 5000 * 5000])
 def test_units_cover_every_k_tile_once(g, M, N, K, batch, dt):
-    dtype = [g.BF16_F32, g.BF16_BF16, g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16][dt]
+    dtype = getattr(g, PLAN_DTYPES[dt])
     for knobs in KNOBS:
         a, p = _plan_and_check(g, M, N, K, batch, dtype, knobs)
         if p["units"] > 20000:
@@ -226,7 +232,20 @@ def test_argument_errors(g):
     assert status(unit_stamps=0x300000000004) == g.EALIGN  # stamps need 8-byte alignment
     assert status(C=0x200000000002) == g.EALIGN            # fp32 C
     assert status(scale_a=0x3001) == g.EALIGN
-    assert status(dtype=8) == g.EINVAL
+    assert status(dtype=14) == g.EINVAL
+    # block-scaled dtypes: scales required (and only there), K a multiple of 128
+    BS = dict(block_scale_a=0x300000000000, block_scale_b=0x380000000000)
+    g.gemm355_plan(g.make_args(64, 64, 128, dtype=g.MXE4M3_F32, **P, **BS))   # valid
+    assert status(dtype=g.MXE4M3_F32, K=128) == g.EINVAL
+    assert status(dtype=g.MXE4M3_F32, K=128, block_scale_a=BS["block_scale_a"]) == g.EINVAL
+    assert status(dtype=g.MXE4M3_F32, K=64, **BS) == g.EUNSUPPORTED
+    assert status(dtype=g.MXE4M3_F32, K=128, block_scale_a=0x300000000002,
+                  block_scale_b=BS["block_scale_b"]) == g.EALIGN
+    assert status(dtype=g.MXE4M3_F32, K=128, block_scale_a=0x200000000000 + 256,
+                  block_scale_b=BS["block_scale_b"]) == g.EINVAL   # scales overlap C
+    g.gemm355_plan(g.make_args(64, 64, 0, dtype=g.MXE5M2_BF16, **P))  # K = 0: C = 0, no scales read
+    assert status(dtype=g.E4M3_F32, **BS) == g.EINVAL        # block scales for a per-tensor dtype
+    assert status(dtype=g.MXE4M3_F32, K=128, tile=3, **BS) == g.EINVAL   # tile of another class
     assert status(layout=9) == g.EINVAL
     assert status(tile=99) == g.EINVAL
     assert status(tile=3) == g.EINVAL                      # E4M3 tile for bf16 inputs
@@ -281,10 +300,12 @@ def test_tile_table(g):
         info = g.gemm355_tile_info(t)
         row_bytes = info["T_K"] * (1 if info["dtype_class"] else 2)
         assert row_bytes in (64, 128)
-        assert info["lds_bytes"] == info["stages"] * (info["T_M"] + info["T_N"]) * row_bytes
+        # block-scaled tiles keep one dword of E8M0 scales per row and stage
+        scale_bytes = 4 if info["dtype_class"] == 2 else 0
+        assert info["lds_bytes"] == info["stages"] * (info["T_M"] + info["T_N"]) * (row_bytes + scale_bytes)
         assert info["lds_bytes"] <= 160 * 1024
         seen.add((info["dtype_class"], info["T_M"], info["T_N"]))
-    assert (0, 256, 256) in seen and (1, 256, 256) in seen
+    assert (0, 256, 256) in seen and (1, 256, 256) in seen and (2, 256, 256) in seen
     with pytest.raises(g.Gemm355Error):
         g.gemm355_tile_info(n)
 
@@ -297,15 +318,16 @@ def test_main_loop_uses_mfma(g, tmp_path):
     asm = open(build.device_asm("kernels.hip")).read()
     bodies = re.split(r"\n(?=_ZN4g35516gemm_tile_kernel\w+:)", asm)
     kernels = [b for b in bodies if re.match(r"_ZN4g35516gemm_tile_kernel\w+:", b)]
-    n8 = sum(g.gemm355_tile_info(t)["dtype_class"] for t in range(g.gemm355_num_tiles()))
+    n8 = sum(g.gemm355_tile_info(t)["dtype_class"] != 0 for t in range(g.gemm355_num_tiles()))
     assert len(kernels) == g.gemm355_num_tiles() + 2 * n8      # three format pairs per 8-bit tile
     for body in kernels:
         name = body.split(":")[0]
-        fp8 = "Lb1E" in name
         targs = [int(v) for v in re.findall(r"Li(\d+)E", name)]
-        mi, fmt = targs[-2], targs[-1]                      # MFMA block edge, format pair
-        want = {(True, 32): "v_mfma_f32_32x32x64_f8f6f4", (False, 32): "v_mfma_f32_32x32x16_bf16",
-                (True, 16): "v_mfma_f32_16x16x128_f8f6f4", (False, 16): "v_mfma_f32_16x16x32_bf16"}[(fp8, mi)]
+        el, mi, fmt = targs[2], targs[-2], targs[-1]        # element class, MFMA block edge, format pair
+        fp8 = el != 0
+        want = {(1, 32): "v_mfma_f32_32x32x64_f8f6f4", (0, 32): "v_mfma_f32_32x32x16_bf16",
+                (1, 16): "v_mfma_f32_16x16x128_f8f6f4", (0, 16): "v_mfma_f32_16x16x32_bf16",
+                (2, 32): "v_mfma_scale_f32_32x32x64_f8f6f4"}[(el, mi)]
         code = body.split("s_endpgm")[0]
         lines = [l for l in code.splitlines() if want in l]
         assert lines, name
