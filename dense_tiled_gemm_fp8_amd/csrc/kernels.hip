@@ -177,11 +177,13 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
 template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
 __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
-    /* element class: 0 bf16, 1 8-bit, 2 8-bit with E8M0 block scales */
-    constexpr bool FP8 = EL != 0, MX = EL == 2;
-    /* 8-bit operand formats (instruction format codes: 0 E4M3, 1 E5M2):
-     * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B) */
-    constexpr int FA = FMT == 1 ? 1 : 0, FB = FMT >= 1 ? 1 : 0;
+    /* element class: 0 bf16, 1 8-bit, 2 8-bit with E8M0 block scales, 3 FP4
+     * (E2M1, two per byte) with E8M0 block scales.  FP8 marks the f8f6f4
+     * matrix instructions (classes 1-3). */
+    constexpr bool FP8 = EL != 0, MX = EL >= 2, FP4 = EL == 3;
+    /* operand formats (instruction format codes: 0 E4M3, 1 E5M2, 4 E2M1):
+     * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B); FP4 both 4 */
+    constexpr int FA = FP4 ? 4 : FMT == 1 ? 1 : 0, FB = FP4 ? 4 : FMT >= 1 ? 1 : 0;
     constexpr int NW = WGM * WGN, WN = WGN;
     /* SPREAD 3 (warp specialisation): four more wavefronts, one per SIMD,
      * issue every copy and run no MFMA; the NW MFMA wavefronts only read LDS.
@@ -191,18 +193,21 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     constexpr int FM = WTM / MI, FN = WTN / MI;
     constexpr int CPR = RB / 16, RPL = 256 / RB, ROWS_PER_DMA = 1024 / RB;
     constexpr int A_BYTES = TM * RB, B_BYTES = TN * RB;
-    /* MX: a K-tile of 128 values holds four 32-value blocks per row, so one
-     * dword of E8M0 scales per row of A and B; a stage keeps TM + TN such
-     * dwords after the operand rows (A's, then B's), copied 64 rows per
-     * direct-to-LDS dword load, SC loads per wavefront */
-    constexpr int SCA_OFF = A_BYTES + B_BYTES, SCB_OFF = SCA_OFF + TM * 4;
-    constexpr int STAGE_BYTES = A_BYTES + B_BYTES + (MX ? (TM + TN) * 4 : 0);
-    constexpr int SC = MX ? (TM + TN) / 64 / NW : 0;
+    /* MX: a K-tile of RB bytes holds RB * VPB values per row, i.e. SW
+     * dwords of four E8M0 scales (one per 32-value block) per row of A and
+     * B (SW = 1 for 8-bit, 2 for FP4).  A stage keeps them after the operand
+     * rows as SW planes of TM + TN dwords (plane w: A's rows, then B's),
+     * copied 64 rows per direct-to-LDS dword load, SC loads per wavefront. */
+    constexpr int VPB = FP4 ? 2 : 1;
+    constexpr int SW = MX ? RB * VPB / 128 : 0;
+    constexpr int SCA_OFF = A_BYTES + B_BYTES, SCB_OFF = SCA_OFF + TM * 4, SPLANE = (TM + TN) * 4;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SW * SPLANE;
+    constexpr int SC = SW * (TM + TN) / 64 / NW;
     constexpr int A_LOADS = TM / ROWS_PER_DMA / CW, B_LOADS = TN / ROWS_PER_DMA / CW;
     constexpr int LOADS = A_LOADS + B_LOADS + SC;
-    /* bytes of K per MFMA step: 32 x 32 blocks take 16 bf16 or 64 E4M3
-     * values, 16 x 16 blocks 32 bf16 or 128 E4M3; CPS 16-byte chunks */
-    constexpr int KB_STEP = (FP8 ? 64 : 32) * (MI == 32 ? 1 : 2);
+    /* bytes of K per MFMA step: 32 x 32 blocks take 16 bf16, 64 E4M3 or 64
+     * FP4 values, 16 x 16 blocks twice that; CPS 16-byte chunks */
+    constexpr int KB_STEP = (FP8 && !FP4 ? 64 : 32) * (MI == 32 ? 1 : 2);
     constexpr int CPS = KB_STEP / 16;
     constexpr int KSTEPS = RB / KB_STEP;
     constexpr int ACC_N = MI * MI / 64;
@@ -218,8 +223,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     static_assert(SPREAD != 2 || (KSTEPS == 4 && STAGES == 2 && LOADS % 2 == 0), "two-step prefetch schedule");
     static_assert(SPREAD != 3 || STAGES >= 3, "producer wavefronts run two K-tiles ahead");
     static_assert(A_LOADS * CW * ROWS_PER_DMA == TM && B_LOADS * CW * ROWS_PER_DMA == TN, "whole copies");
-    static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == TM + TN),
-                  "block scales: one dword per row and K-tile, whole 64-row copies per wavefront");
+    static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == SW * (TM + TN)),
+                  "block scales: whole dwords per row and K-tile, whole 64-row copies per wavefront");
     constexpr int NB = SPREAD == 2 ? 4 : 2;     /* fragment buffers */
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
@@ -285,13 +290,17 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             const uint8_t *sb0 = p.bsb + (int64_t)un.batch * p.stride_bsb + (int64_t)n0 * 4;
             unroll<SC>([&](auto qc) __attribute__((always_inline)) {
                 constexpr int q = decltype(qc)::value;
+                /* group g: plane w = g / G1, then A's or B's 64-row group */
+                constexpr int G1 = (TM + TN) / 64;
                 const int g = q * NW + wave;
-                const bool in_a = g < TM / 64;
-                const int r = (in_a ? g : g - TM / 64) * 64 + lane;
+                const int w = g / G1, g1 = g % G1;
+                const bool in_a = g1 < TM / 64;
+                const int r = (in_a ? g1 : g1 - TM / 64) * 64 + lane;
+                const uint32_t plane = (uint32_t)(in_a ? p.ktp_a : p.ktp_b);
                 srs[q] = rsrc_words(in_a ? sa0 : sb0);
-                soff[q] = (in_a ? m0 + r < p.M : n0 + r < p.N) ? (uint32_t)(r * 4) : kOOB;
+                soff[q] = (in_a ? m0 + r < p.M : n0 + r < p.N) ? (uint32_t)(r * 4) + w * plane : kOOB;
                 sdst[q] = (uint32_t)(SCA_OFF + g * 256);
-                stp[q] = (uint32_t)(in_a ? p.ktp_a : p.ktp_b);
+                stp[q] = SW * plane;
             });
         }
 
@@ -342,6 +351,10 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             const uint8_t *row = rows + (blk * MI + frow) * RB;
             if constexpr (!FP8) {
                 return *(const bf16x8 *)(row + (((CPS * ks + hi) ^ sw) * 16));
+            } else if constexpr (FP4) {
+                /* 32 values (one block) per lane in the low four dwords */
+                const i32x4 v = *(const i32x4 *)(row + (((CPS * ks + hi) ^ sw) * 16));
+                return i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
             } else {
                 /* the instruction takes K in 16-byte quarters: lane group
                  * hi's first and second halves are quarters hi and 2 + hi of
@@ -364,23 +377,30 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * first fragments) and for the current one, shifted so that byte 0
          * holds the lane's first block (the instruction takes its scale
          * from byte 0) */
-        uint32_t nsa[MX ? FM : 1], nsb[MX ? FN : 1], csa[MX ? FM : 1], csb[MX ? FN : 1];
+        constexpr int NSW = MX ? SW : 1;
+        uint32_t nsa[NSW][MX ? FM : 1], nsb[NSW][MX ? FN : 1], csa[NSW][MX ? FM : 1], csb[NSW][MX ? FN : 1];
         auto read_scales = [&](const uint8_t *st) __attribute__((always_inline)) {
             if constexpr (MX) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    nsa[i] = *(const uint32_t *)(st + SCA_OFF + (wm * WTM + i * MI + frow) * 4);
+                for (int w = 0; w < SW; ++w) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    nsb[j] = *(const uint32_t *)(st + SCB_OFF + (wn * WTN + j * MI + frow) * 4);
+                    for (int i = 0; i < FM; ++i)
+                        nsa[w][i] = *(const uint32_t *)(st + w * SPLANE + SCA_OFF + (wm * WTM + i * MI + frow) * 4);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        nsb[w][j] = *(const uint32_t *)(st + w * SPLANE + SCB_OFF + (wn * WTN + j * MI + frow) * 4);
+                }
             }
         };
         auto take_scales = [&]() __attribute__((always_inline)) {
             if constexpr (MX) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i) csa[i] = nsa[i] >> (8 * hi);
+                for (int w = 0; w < SW; ++w) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) csb[j] = nsb[j] >> (8 * hi);
+                    for (int i = 0; i < FM; ++i) csa[w][i] = nsa[w][i] >> (8 * hi);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) csb[w][j] = nsb[w][j] >> (8 * hi);
+                }
             }
         };
 
@@ -414,10 +434,11 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             /* MX: the last K-step, which reads the next tile's first
              * fragments, also reads its FM + FN scale dwords, after them */
             constexpr bool SCALES = MX && KS == KSTEPS - 1;
+            constexpr int NS = SW * (FM + FN);        /* scale dwords read in that step */
             /* SPREAD 2 puts the copies after the reads: NR + DN slots at least */
             constexpr int SLOTS0 = SPREAD == 2 ? (NM > NR + DN ? NM : NR + DN)
                                                : NM > (NR > DN ? NR : DN) ? NM : (NR > DN ? NR : DN);
-            constexpr int SLOTS = SCALES && SLOTS0 < 2 * NR ? 2 * NR : SLOTS0;
+            constexpr int SLOTS = SCALES && SLOTS0 < NR + NS ? NR + NS : SLOTS0;
             if constexpr (SPREAD == 2) {
                 /* this step's fragments (read two steps ago) are in; the NR
                  * reads of the previous step may still be outstanding */
@@ -436,10 +457,11 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     else if constexpr (!FP8)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
                     else if constexpr (MX) {
-                        constexpr int SH = 8 * KS * (KB_STEP / 32);
+                        /* the step's first block: its plane and byte */
+                        constexpr int B0 = KS * (KB_STEP * VPB / 32), DW = B0 / 4, SH = 8 * (B0 % 4);
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, (int)(csa[i] >> SH), 0,
-                            (int)(csb[j] >> SH));
+                            fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, (int)(csa[DW][i] >> SH), 0,
+                            (int)(csb[DW][j] >> SH));
                     }
                     /* format fields FA / FB of the A and B operands; zero
                      * scales select the unscaled instruction */
@@ -454,10 +476,15 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     fa[TGT][t] = frag(ns + wm * WTM * RB, nks, t);
                 else if constexpr (t < NR)
                     fb[TGT][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
-                else if constexpr (SCALES && t < NR + FM)
-                    nsa[t - NR] = *(const uint32_t *)(ns + SCA_OFF + (wm * WTM + (t - NR) * MI + frow) * 4);
-                else if constexpr (SCALES && t < 2 * NR)
-                    nsb[t - NR - FM] = *(const uint32_t *)(ns + SCB_OFF + (wn * WTN + (t - NR - FM) * MI + frow) * 4);
+                else if constexpr (SCALES && t < NR + NS) {
+                    /* dword u of the step's scale reads: plane u / (FM + FN) */
+                    constexpr int u = t - NR, w = u / (FM + FN), v = u % (FM + FN);
+                    if constexpr (v < FM)
+                        nsa[w][v] = *(const uint32_t *)(ns + w * SPLANE + SCA_OFF + (wm * WTM + v * MI + frow) * 4);
+                    else
+                        nsb[w][v - FM] =
+                            *(const uint32_t *)(ns + w * SPLANE + SCB_OFF + (wn * WTN + (v - FM) * MI + frow) * 4);
+                }
                 if constexpr (DN > 0 && SPREAD == 2) {
                     /* copies after the fragment reads, spread over the rest
                      * of the step */
@@ -983,7 +1010,10 @@ static hipError_t launch_one(const GemmParams &p, hipStream_t stream)
 template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
 static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stream)
 {
-    if constexpr (EL != 0) {
+    if constexpr (EL == 3) {
+        if (fmt != 0) return hipErrorInvalidValue;
+        return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+    } else if constexpr (EL != 0) {
         switch (fmt) {
         case 0: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
         case 1: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 1>(p, stream);
@@ -997,7 +1027,8 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
 }
 
 /* Instantiations, in tile-table order (csrc/tiles.h):
- * id, TM, TN, element class (false bf16, true 8-bit, 2 block-scaled 8-bit),
+ * id, TM, TN, element class (false bf16, true 8-bit, 2 block-scaled 8-bit,
+ * 3 block-scaled FP4),
  * groups per CU, K-tile bytes, stages, waves along M, N, copy schedule,
  * MFMA block edge */
 #define GEMM355_TILES(X)                                                                          \
@@ -1051,7 +1082,10 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(47, 256, 128, false, 1, 128, 3, 2, 2, 0, 32)                                                  \
     X(48, 256, 256, 2, 1, 128, 2, 2, 2, 0, 32)                                                      \
     X(49, 128, 128, 2, 2, 128, 2, 2, 2, 0, 32)                                                      \
-    X(50, 128, 128, 2, 1, 128, 4, 2, 2, 0, 32)
+    X(50, 128, 128, 2, 1, 128, 4, 2, 2, 0, 32)                                                      \
+    X(51, 256, 256, 3, 1, 128, 2, 2, 2, 0, 32)                                                      \
+    X(52, 128, 128, 3, 2, 128, 2, 2, 2, 0, 32)                                                      \
+    X(53, 128, 128, 3, 1, 128, 4, 2, 2, 0, 32)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi)                                                      \
@@ -1059,7 +1093,8 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
                       kTiles[id].TN == tn && kTiles[id].min_blocks == mb &&                      \
                       kTiles[id].row_bytes == rb && kTiles[id].stages == st &&                   \
                       kTiles[id].waves_m == wm && kTiles[id].waves_n == wn &&                    \
-                      kTiles[id].TK == (f8 ? rb : rb / 2) && kTiles[id].spread == sp &&          \
+                      kTiles[id].TK == ((f8) == 3 ? 2 * rb : (f8) ? rb : rb / 2) &&             \
+                      kTiles[id].spread == sp &&                                                 \
                       kTiles[id].mfma == mi,                                                     \
                   "tile table entry " #id);
 GEMM355_TILES(X)

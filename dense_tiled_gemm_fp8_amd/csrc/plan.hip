@@ -42,6 +42,7 @@ constexpr int32_t kMaxNK = 1 << 23;
 constexpr int32_t kGroupM = 4;                        /* raster band height in tiles */
 constexpr double kPeakBf16PerCu = 2516.6e12 / 256.0;   /* dense MFMA, 2.4 GHz */
 constexpr double kPeakFp8PerCu = 5033.2e12 / 256.0;
+constexpr double kPeakFp4PerCu = 10066.3e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
 constexpr double kExtraPassSec = 4.0e-6;              /* one launch: main, combine or repack */
 constexpr double kCopyBytesPerSecPerCu = 100.0e9;     /* L2 -> LDS copies per compute unit */
@@ -144,7 +145,7 @@ void schedule_loads(const Cand &c, int64_t slots, int32_t S, uint64_t &total, ui
 }
 
 void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t N, int64_t K,
-                      int64_t batch, int32_t esize, int32_t out_esize, int pack_passes)
+                      int64_t batch, int64_t kbytes, int32_t out_esize, int pack_passes)
 {
     const int64_t slots = (int64_t)S * c.b;
     uint64_t total = 0, busiest = 0, busiest_cu = 0;
@@ -159,7 +160,7 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
      * workgroups.  Memory side: algorithmic bytes plus split-K partial
      * traffic (written, then read), at a sustained HBM rate scaled by how
      * evenly the work is spread over the compute units. */
-    const double cu_peak = cfg.dtype_class ? kPeakFp8PerCu : kPeakBf16PerCu;
+    const double cu_peak = cfg.dtype_class == 3 ? kPeakFp4PerCu : cfg.dtype_class ? kPeakFp8PerCu : kPeakBf16PerCu;
     /* workgroups actually sharing a compute unit */
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(c.b, cdiv(std::max<int64_t>(c.grid, 1), S)));
     const double eff = cfg.mfma_eff[std::min<int64_t>(per_cu, 4) - 1];
@@ -185,7 +186,7 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
             partial += (double)rows * cols * 4.0 * nsl;
         }
     }
-    const double bytes = (double)batch * ((double)(M + N) * K * esize + (double)M * N * out_esize) +
+    const double bytes = (double)batch * ((double)(M + N) * kbytes + (double)M * N * out_esize) +
                          2.0 * partial;
     const double spread = busiest_cu ? (double)total / ((double)S * busiest_cu) : 1.0;
     const double t_mem = bytes / (kHbmBytesPerSec * cfg.stream_eff * spread);
@@ -273,8 +274,8 @@ int32_t resident_workgroups(int32_t tile)
 
 gemm355_status check_pointers(const gemm355_args &a)
 {
-    const bool fp8 = dtype_fp8(a.dtype);
-    const int32_t esize = fp8 ? 1 : 2;
+    const int32_t ebits = dtype_ebits(a.dtype);
+    const int32_t esize = ebits >= 8 ? ebits / 8 : 1;   /* alignment */
     const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
@@ -300,9 +301,11 @@ gemm355_status check_pointers(const gemm355_args &a)
     const int64_t a_rows = a_row ? M : K, a_cols = a_row ? K : M;
     const int64_t b_rows = b_col ? N : K, b_cols = b_col ? K : N;
     const uintptr_t a_lo = (uintptr_t)a.A;
-    const uintptr_t a_hi = a_lo + (uintptr_t)(((batch - 1) * a.stride_a + (a_rows - 1) * a.lda + a_cols) * esize);
+    /* element counts to bytes, rounded up (4-bit elements pack two a byte) */
+    auto span = [ebits](int64_t elems) { return (uintptr_t)((elems * ebits + 7) / 8); };
+    const uintptr_t a_hi = a_lo + span((batch - 1) * a.stride_a + (a_rows - 1) * a.lda + a_cols);
     const uintptr_t b_lo = (uintptr_t)a.B;
-    const uintptr_t b_hi = b_lo + (uintptr_t)(((batch - 1) * a.stride_b + (b_rows - 1) * a.ldb + b_cols) * esize);
+    const uintptr_t b_hi = b_lo + span((batch - 1) * a.stride_b + (b_rows - 1) * a.ldb + b_cols);
     if ((c_lo < a_hi && a_lo < c_hi) || (c_lo < b_hi && b_lo < c_hi)) return GEMM355_EINVAL;
     if (dtype_mx(a.dtype)) {
         /* block-scale arrays: batch * rows * ceil(K / 32) bytes */
@@ -326,9 +329,10 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     if (S < 1) return GEMM355_EINVAL;
     if (a.stride_a < 0 || a.stride_b < 0 || a.stride_c < 0) return GEMM355_EINVAL;
 
-    const bool fp8 = dtype_fp8(a.dtype);
+    const bool fp8 = dtype_fp8(a.dtype), fp4 = dtype_fp4(a.dtype);
     const int32_t dclass = dtype_class_of(a.dtype);
-    const int32_t esize = fp8 ? 1 : 2;
+    const int32_t ebits = dtype_ebits(a.dtype);
+    const int32_t esize = fp8 || fp4 ? 1 : 2;    /* bytes per element of the repack passes */
     const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
@@ -342,6 +346,11 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     /* block scales are read one dword (four 32-value blocks) per row and
      * K-tile of 128 values */
     if (dtype_mx(a.dtype) && K % 128 != 0) return GEMM355_EUNSUPPORTED;
+    /* FP4: native layout, whole bytes per row and batch entry, whole
+     * K-tiles of 256 values (two scale dwords per row) */
+    if (fp4 && (a.layout != GEMM355_A_ROW_B_COL || K % 256 != 0 || a.lda % 2 || a.ldb % 2 ||
+                (batch > 1 && (a.stride_a % 2 || a.stride_b % 2))))
+        return GEMM355_EUNSUPPORTED;
     /* the regrouped scales of one batch entry are addressed with 32-bit
      * offsets */
     if (dtype_mx(a.dtype) && std::max(M, N) * (K / 32) > kMaxOffset) return GEMM355_EUNSUPPORTED;
@@ -360,25 +369,28 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     /* Operand views of the main loop: K-contiguous rows, 16-byte aligned
      * rows and starts, K a whole number of 16-byte chunks; otherwise the
      * operand is repacked (zero-filled to a whole number of K-tiles). */
-    const int64_t kbytes = K * esize;
+    auto bytes_of = [ebits](int64_t elems) { return elems * ebits / 8; };
+    const int64_t kbytes = bytes_of(K);
     const int64_t packed_ld = cdiv(std::max<int64_t>(kbytes, 1), 128) * 128;
-    P.pack_a = !a_row || misaligned16(a.A) || (a.lda * esize) % 16 || kbytes % 16 ||
-               (batch > 1 && (a.stride_a * esize) % 16);
-    P.pack_b = !b_col || misaligned16(a.B) || (a.ldb * esize) % 16 || kbytes % 16 ||
-               (batch > 1 && (a.stride_b * esize) % 16);
+    P.pack_a = !a_row || misaligned16(a.A) || bytes_of(a.lda) % 16 || kbytes % 16 ||
+               (batch > 1 && bytes_of(a.stride_a) % 16);
+    P.pack_b = !b_col || misaligned16(a.B) || bytes_of(a.ldb) % 16 || kbytes % 16 ||
+               (batch > 1 && bytes_of(a.stride_b) % 16);
+    /* the repack passes move whole bytes per element */
+    if (fp4 && (P.pack_a || P.pack_b)) return GEMM355_EUNSUPPORTED;
     if (P.pack_a) {
         P.lda_b = packed_ld;
         P.stride_a_b = M * packed_ld;
     } else {
-        P.lda_b = a.lda * esize;
-        P.stride_a_b = a.stride_a * esize;
+        P.lda_b = bytes_of(a.lda);
+        P.stride_a_b = bytes_of(a.stride_a);
     }
     if (P.pack_b) {
         P.ldb_b = packed_ld;
         P.stride_b_b = N * packed_ld;
     } else {
-        P.ldb_b = a.ldb * esize;
-        P.stride_b_b = a.stride_b * esize;
+        P.ldb_b = bytes_of(a.ldb);
+        P.stride_b_b = bytes_of(a.stride_b);
     }
     P.Kb = (int32_t)std::min<int64_t>(cdiv(kbytes, 16) * 16, kMaxDim);
     P.pub.repack = (P.pack_a ? 1 : 0) | (P.pack_b ? 2 : 0);
@@ -456,7 +468,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
                         bu == b_max)
                         continue;
                     if (K > 0)
-                        finish_candidate(c, cfg, S, M, N, K, batch, esize, out_esize, pack_passes);
+                        finish_candidate(c, cfg, S, M, N, K, batch, kbytes, out_esize, pack_passes);
                     if (better(c, best)) best = c;
                 }
             }

@@ -21,8 +21,9 @@ namespace g355 {
 
 struct TileCfg {
     int32_t dtype_class;   /* 0 bf16 inputs, 1 8-bit inputs, 2 8-bit inputs
-                              with E8M0 block scales (MX)                   */
-    int32_t TM, TN, TK;
+                              with E8M0 block scales (MX), 3 FP4 inputs
+                              with E8M0 block scales                        */
+    int32_t TM, TN, TK;    /* TK in elements                                 */
     int32_t row_bytes;     /* RB: K bytes per tile row per stage             */
     int32_t stages;
     int32_t waves_m, waves_n;
@@ -37,8 +38,9 @@ struct TileCfg {
                               K-tiles ahead, and the waves_m x waves_n MFMA
                               wavefronts only read LDS (3 stages or more)  */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
-    int32_t lds_bytes;     /* stages * (TM + TN) * RB, plus 4 bytes of block
-                              scales per row and stage for MX               */
+    int32_t lds_bytes;     /* stages * (TM + TN) * RB, plus 4 (8 for FP4)
+                              bytes of block scales per row and stage for
+                              MX                                            */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
     int32_t vgpr_budget;   /* 512 / (min_blocks * tile_waves / 4): registers
                               per lane one wave may hold                    */
@@ -126,6 +128,11 @@ constexpr TileCfg kTiles[] = {
     {2, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 132, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
     {2, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 132, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
     {2, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 132, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
+    /* block-scaled FP4: 128-byte K-tiles of 256 values, two scale dwords per
+     * row and stage */
+    {3, 256, 256, 256, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 136, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
+    {3, 128, 128, 256, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 136, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {3, 128, 128, 256, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 136, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

@@ -78,7 +78,47 @@ def to_e4m3_codes(x: np.ndarray, scale: Optional[float] = None) -> Tuple[np.ndar
     return to_fp8_codes(x, "e4m3", scale)
 
 
-FP8_EMAX = {"e4m3": 8, "e5m2": 15}     # exponent of the largest finite value
+FP8_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}     # exponent of the largest finite value
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # codes 0..7 (OCP FP4)
+
+
+def to_e2m1_codes(y: np.ndarray) -> np.ndarray:
+    """Round to the nearest E2M1 value, ties to the even code, saturating
+    at 6; returns 4-bit codes (sign in bit 3) as uint8.  The value steps are
+    0.5 below 2, 1 in [2, 4) and 2 in [4, 6], and an even code is an even
+    multiple of the step, so rint (ties to even) on the scaled magnitude
+    picks it."""
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.minimum(np.abs(y), 6.0)
+    q = np.where(mag < 2.0, np.rint(mag * 2.0) / 2.0,
+                 np.where(mag < 4.0, np.rint(mag), np.minimum(2.0 * np.rint(mag / 2.0), 6.0)))
+    code = np.searchsorted(E2M1_VALUES, q).astype(np.uint8)
+    return code | (np.signbit(y).astype(np.uint8) << 3)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """rows x K 4-bit codes -> rows x K/2 bytes, element 2i in the low
+    nibble of byte i."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def to_mx_fp4_codes(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Block-scaled FP4 quantisation (OCP MX v1.0 conversion, as
+    to_mx_codes with emax 2): returns (rows x K/2 packed bytes, rows x K/32
+    scale codes)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    rows, K = x64.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x64.reshape(rows, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    _, e = np.frexp(amax)
+    code = np.where(amax > 0, e - 1 - FP8_EMAX["e2m1"] + 127, 127)
+    code = np.clip(code, 0, 254).astype(np.uint8)
+    scale = np.ldexp(1.0, code.astype(np.int64) - 127)
+    q = to_e2m1_codes((blocks / scale[:, :, None]).reshape(rows, K))
+    return pack_nibbles(q), code
 
 
 def to_mx_codes(x: np.ndarray, fmt: str) -> Tuple[np.ndarray, np.ndarray]:
@@ -114,6 +154,10 @@ def small_int_codes(gen: np.random.Generator, shape, fmt: str, lo: int = -4,
     v = gen.integers(lo, hi + 1, size=shape).astype(np.float64)
     if fmt == "bf16":
         return to_bf16_codes(v)
+    if fmt == "e2m1":
+        # integers of E2M1: 0, 1, 2, 3, 4, 6 (packed two per byte)
+        v = np.where(np.abs(v) == 5, np.sign(v) * 4, v)
+        return pack_nibbles(to_e2m1_codes(v))
     q, _ = to_fp8_codes(v, "e5m2" if fmt == "e5m2" else "e4m3", scale=1.0)
     return q
 
@@ -142,7 +186,8 @@ class Operands:
     N: int
     K: int
     fmt: str                      # "bf16", "e4m3", "e5m2" or "e4m3e5m2" (A E4M3, B E5M2);
-                                  # "mx" + one of the 8-bit names: block-scaled
+                                  # "mx" + one of the 8-bit names, or "mxfp4":
+                                  # block-scaled (FP4 A and B hold K/2 bytes a row)
     A: np.ndarray                 # (batch, M, K) or (M, K)
     B: np.ndarray                 # (batch, N, K) or (N, K)  (column-major B)
     scale_a: List[float] = field(default_factory=list)
@@ -167,10 +212,14 @@ class Operands:
 
     @property
     def fmt_a(self) -> str:
+        if self.elem == "fp4":
+            return "e2m1"
         return "e4m3" if self.elem == "e4m3e5m2" else self.elem
 
     @property
     def fmt_b(self) -> str:
+        if self.elem == "fp4":
+            return "e2m1"
         return "e5m2" if self.elem == "e4m3e5m2" else self.elem
 
 
@@ -190,6 +239,15 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
             Bs.append(to_bf16_codes(xb))
             sa.append(1.0)
             sb.append(1.0)
+        elif fmt == "mxfp4":
+            qa, ca = to_mx_fp4_codes(xa)
+            qb, cb = to_mx_fp4_codes(xb)
+            As.append(qa)
+            Bs.append(qb)
+            sa.append(1.0)
+            sb.append(1.0)
+            bsa_l.append(ca)
+            bsb_l.append(cb)
         elif fmt.startswith("mx"):
             fa = "e5m2" if fmt == "mxe5m2" else "e4m3"
             fb = "e4m3" if fmt == "mxe4m3" else "e5m2"

@@ -43,8 +43,9 @@ typedef enum gemm355_status {
                                   split factor, or C overlapping A/B */
     GEMM355_EALIGN = 2,        /* pointer not aligned to its element size */
     GEMM355_EUNSUPPORTED = 3,  /* extents beyond the 32-bit offsets the
-                                  kernels use, an unknown tile id, or an MX
-                                  dtype with K not a multiple of 128 */
+                                  kernels use, an unknown tile id, an MX
+                                  dtype with K not a multiple of 128, or an
+                                  MX FP4 call outside its limits */
     GEMM355_ENOMEM = 4,        /* caller workspace smaller than the plan's
                                   workspace_bytes, or allocation failed */
     GEMM355_EHIP = 5           /* a HIP runtime call failed (no device,
@@ -76,7 +77,14 @@ typedef enum gemm355_dtype {
     GEMM355_MXE5M2_F32 = 10,    /* MX E5M2 A, B; fp32 C                       */
     GEMM355_MXE5M2_BF16 = 11,   /* MX E5M2 A, B; bf16 C                       */
     GEMM355_MXE4M3_E5M2_F32 = 12,  /* MX E4M3 A, MX E5M2 B; fp32 C            */
-    GEMM355_MXE4M3_E5M2_BF16 = 13  /* MX E4M3 A, MX E5M2 B; bf16 C            */
+    GEMM355_MXE4M3_E5M2_BF16 = 13, /* MX E4M3 A, MX E5M2 B; bf16 C            */
+    /* MX FP4: OCP E2M1 elements (1 sign, 2 exponent bits with bias 1, 1
+     * mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, element
+     * 2i in the low nibble of byte i.  Native layout only (A row-major,
+     * B column-major), lda, ldb and strides even, rows 16-byte aligned,
+     * K a multiple of 256 (EUNSUPPORTED otherwise). */
+    GEMM355_MXFP4_F32 = 14,        /* MX FP4 A, B; fp32 C                     */
+    GEMM355_MXFP4_BF16 = 15        /* MX FP4 A, B; bf16 C                     */
 } gemm355_dtype;
 
 /* 8-bit formats of the quantiser. */
@@ -259,7 +267,8 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
 
 /* Number of entries in the tile table, and one entry's parameters.
  * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2), 2 = block-scaled
- * 8-bit inputs (the MX dtypes). */
+ * 8-bit inputs (the MX 8-bit dtypes), 3 = block-scaled FP4 inputs; T_K counts
+ * elements. */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
                                  int32_t *T_M, int32_t *T_N, int32_t *T_K,

@@ -11,7 +11,10 @@ version 1.0:
 * a block is 32 consecutive elements along the contraction dimension K,
   all sharing one scale;
 * the scale is an E8M0 code e, whose value is 2^(e - 127); e = 255 is NaN;
-* the elements are E4M3 or E5M2 codes, decoded as in ``gemm_oracle.c``;
+* the elements are E4M3 or E5M2 codes, decoded as in ``gemm_oracle.c``, or
+  FP4 E2M1 codes (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+  exponent field 0 is subnormal, m * 0.5; no infinity or NaN), two per byte
+  with element 2i in the low nibble of byte i;
 * an element's value is scale * element.
 
 For A (M x K) each row has ceil(K/32) scales. For B (K x N) each column has
@@ -44,19 +47,43 @@ def decode_e8m0(codes: np.ndarray) -> np.ndarray:
     return np.where(e == 255, np.nan, v)
 
 
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes (low nibble) -> binary64."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = c >> 3
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(sign == 1, -mag, mag)
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """rows x K/2 bytes -> rows x K codes (element 2i = low nibble)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
 def _element_table(fmt: str) -> np.ndarray:
     codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    if fmt == "e2m1":
+        return decode_e2m1(codes)
     if fmt == "e4m3":
         return reference.decode_e4m3(codes)
     if fmt == "e5m2":
         return reference.decode_e5m2(codes)
-    raise ValueError("block-scaled element format must be e4m3 or e5m2, not %r" % (fmt,))
+    raise ValueError("block-scaled element format must be e4m3, e5m2 or e2m1, not %r" % (fmt,))
 
 
 def scaled_operand(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
-    """Rows x K element codes and rows x ceil(K/32) E8M0 scales -> the
-    binary64 values 2^(s - 127) * element, rows x K."""
+    """Rows x K element codes (rows x K/2 packed bytes for e2m1) and
+    rows x ceil(K/32) E8M0 scales -> the binary64 values
+    2^(s - 127) * element, rows x K."""
     codes = np.asarray(codes, dtype=np.uint8)
+    if fmt == "e2m1":
+        codes = unpack_fp4(codes)
     rows, K = codes.shape
     nb = -(-K // BLOCK)
     scales = np.asarray(scales, dtype=np.uint8)
@@ -69,9 +96,9 @@ def scaled_operand(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarra
 
 def gemm(A: np.ndarray, sa: np.ndarray, B: np.ndarray, sb: np.ndarray, fmt_a: str = "e4m3",
          fmt_b: Optional[str] = None, alpha: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
-    """A: M x K codes (row-major), sa: M x ceil(K/32); B: N x K codes (column
-    j of B is row j), sb: N x ceil(K/32). Returns (C, W), both binary64
-    M x N."""
+    """A: M x K codes (row-major; M x K/2 bytes for e2m1), sa: M x ceil(K/32);
+    B: N x K codes (column j of B is row j), sb: N x ceil(K/32). Returns
+    (C, W), both binary64 M x N."""
     fmt_b = fmt_a if fmt_b is None else fmt_b
     a = scaled_operand(A, sa, fmt_a)
     b = scaled_operand(B, sb, fmt_b)

@@ -23,6 +23,7 @@ from tests import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 MX_TILES = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["dtype_class"] == 2]
+FP4_TILES = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["dtype_class"] == 3]
 
 
 def _bf16_ok(C, C_ref, W, fmt):
@@ -46,13 +47,28 @@ def test_mx_ragged_full(fmt, shape):
                 assert _bf16_ok(C, C_ref, W, fmt), (fmt, tile, shape)
 
 
+@pytest.mark.parametrize("shape", [(300, 520, 256), (257, 129, 512), (70, 90, 256), (1, 1, 256)])
+def test_mxfp4_ragged_full(shape):
+    M, N, K = shape
+    ops = inputs.make_operands(M, N, K, "mxfp4", "normal", 800 + M + K, 801 + N)
+    C_ref, W = H.oracle_full(ops)
+    for tile in [-1] + FP4_TILES:
+        for out in ("f32", "bf16"):
+            H.say("mxfp4 tile", tile, shape, out)
+            C = H.run(ops, out=out, tile=tile)
+            if out == "f32":
+                H.check(C, C_ref, W, "mxfp4", "mxfp4 tile %d %s" % (tile, shape))
+            else:
+                assert _bf16_ok(C, C_ref, W, "mxfp4"), (tile, shape)
+
+
 def _int_ops(M, N, K, fmt, seed, batch=0):
     """Elements in [-4, 4] and scales 125 .. 129 (2^-2 .. 2^2): every
     product is a multiple of 2^-4 of magnitude at most 2^8, so every partial
     sum is exact in binary32 for K <= 2^12."""
     ga, gb = inputs.rng(seed), inputs.rng(seed + 1)
-    fa = "e5m2" if fmt == "mxe5m2" else "e4m3"
-    fb = "e4m3" if fmt == "mxe4m3" else "e5m2"
+    fa = "e2m1" if fmt == "mxfp4" else "e5m2" if fmt == "mxe5m2" else "e4m3"
+    fb = "e2m1" if fmt == "mxfp4" else "e4m3" if fmt == "mxe4m3" else "e5m2"
     nb = max(batch, 1)
     A = np.stack([inputs.small_int_codes(ga, (M, K), fa) for _ in range(nb)])
     B = np.stack([inputs.small_int_codes(gb, (N, K), fb) for _ in range(nb)])
@@ -63,12 +79,12 @@ def _int_ops(M, N, K, fmt, seed, batch=0):
     return inputs.Operands(M, N, K, fmt, A, B, [1.0] * nb, [1.0] * nb, (seed, seed + 1), sa, sb)
 
 
-@pytest.mark.parametrize("fmt", ["mxe4m3", "mxe5m2", "mxe4m3e5m2"])
+@pytest.mark.parametrize("fmt", ["mxe4m3", "mxe5m2", "mxe4m3e5m2", "mxfp4"])
 def test_mx_exact_integers_every_tile(fmt):
     M, N, K, batch = 200, 170, 512, 2
     ops = _int_ops(M, N, K, fmt, 81, batch=batch)
     refs = [H.oracle_full(ops, bi)[0] for bi in range(batch)]
-    for tile in MX_TILES:
+    for tile in (FP4_TILES if fmt == "mxfp4" else MX_TILES):
         for knobs in (dict(split_k=1, persistent=0), dict(split_k=3), dict(persistent=1)):
             H.say(fmt, "ints tile", tile, knobs)
             C = H.run(ops, out="f32", tile=tile, **knobs)
@@ -127,6 +143,38 @@ def test_mx_batch_split_and_persistent():
         C = H.run(ops, out="f32", **knobs)
         for bi in range(batch):
             H.check(C[bi], refs[bi][0], refs[bi][1], "mxe5m2", "batch %d %s" % (bi, knobs))
+
+
+def test_mxfp4_block_boundaries_and_batch():
+    """FP4: a different scale in each of the eight blocks of a K-tile of
+    256 values reaches only its own block; a batch with split-K and the
+    persistent grid."""
+    M, N, K = 64, 64, 512
+    ops = _int_ops(M, N, K, "mxfp4", 92)
+    ops.bsa[5] = np.tile(np.array([125, 126, 128, 129, 127, 129, 125, 126], dtype=np.uint8), K // 256)
+    ops.bsb[9] = np.tile(np.array([129, 125, 127, 128, 126, 125, 129, 127], dtype=np.uint8), K // 256)
+    C_ref, _ = H.oracle_full(ops)
+    for tile in [-1] + FP4_TILES:
+        C = H.run(ops, out="f32", tile=tile)
+        assert np.array_equal(C, C_ref), tile
+    M, N, K, batch = 300, 260, 768, 3
+    ops = inputs.make_operands(M, N, K, "mxfp4", "normal", 93, 94, batch=batch)
+    refs = [H.oracle_full(ops, bi) for bi in range(batch)]
+    for knobs in (dict(), dict(split_k=2), dict(persistent=1), dict(workspace="caller", split_k=3)):
+        H.say("mxfp4 batch", knobs)
+        C = H.run(ops, out="f32", **knobs)
+        for bi in range(batch):
+            H.check(C[bi], refs[bi][0], refs[bi][1], "mxfp4", "batch %d %s" % (bi, knobs))
+
+
+def test_mxfp4_4096_sampled():
+    M = N = K = 4096
+    ops = inputs.make_operands(M, N, K, "mxfp4", "normal", 101, 102)
+    H.say("mxfp4 4096^3")
+    C = H.run(ops, out="f32")
+    rows, cols = H.sample_positions(M, N, 3000, 12)
+    c_ref, w = H.oracle_entries(ops, rows, cols)
+    H.check(C[rows, cols], c_ref, w, "mxfp4", "mxfp4 4096^3 sampled")
 
 
 def test_mx_4096_sampled():

@@ -162,3 +162,67 @@ def test_mutants_are_caught(mutant, monkeypatch):
     else:
         C, _ = mx.gemm(A, sb, B, sa)
     assert not np.all(np.abs(C - Cr) <= 1e-6 * Wr)
+
+
+def test_e2m1_decoder_matches_spec_table():
+    """Every FP4 E2M1 code against the value table of the OCP MX
+    specification (tests/golden/e2m1_values.json)."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "e2m1_values.json")
+    table = json.load(open(path))["values"]
+    got = mx.decode_e2m1(np.arange(16))
+    for code, v in table.items():
+        assert got[int(code)] == v and np.signbit(got[int(code)]) == np.signbit(v), code
+    # the high nibble is ignored by the decoder; packing puts element 2i low
+    assert np.array_equal(mx.unpack_fp4(np.array([[0x72, 0x1F]], dtype=np.uint8)),
+                          np.array([[2, 7, 15, 1]], dtype=np.uint8))
+
+
+def test_e2m1_input_rounding_is_nearest_even():
+    """The input generator's E2M1 rounding (inputs.to_e2m1_codes): nearest
+    value of the oracle's table, ties to the even code, saturation at 6."""
+    from dense_tiled_gemm_fp8_amd import inputs
+    vals = mx.decode_e2m1(np.arange(8))
+    g = np.random.Generator(np.random.PCG64(9))
+    y = np.concatenate([g.uniform(-7, 7, 4000), (vals[1:] + vals[:-1]) / 2, -(vals[1:] + vals[:-1]) / 2, vals])
+    c = inputs.to_e2m1_codes(y)
+    dec = mx.decode_e2m1(c)
+    mag = np.minimum(np.abs(y), 6.0)
+    err = np.abs(np.abs(dec) - mag)
+    best = np.min(np.abs(vals[None, :] - mag[:, None]), axis=1)
+    assert np.all(err == best)
+    tie = np.isclose(np.abs(vals[None, :] - mag[:, None]), best[:, None], rtol=0, atol=0).sum(axis=1) > 1
+    assert np.all((c[tie] & 1) == 0)
+    assert np.all(np.signbit(dec[y != 0]) == np.signbit(y[y != 0]))
+
+
+def test_fp4_all_ones_closed_form():
+    """FP4 1.0 is code 2; packed all-ones operands give the closed form."""
+    g = np.random.Generator(np.random.PCG64(10))
+    M, N, K = 5, 6, 256
+    sa = g.integers(115, 135, size=(M, K // 32)).astype(np.uint8)
+    sb = g.integers(115, 135, size=(N, K // 32)).astype(np.uint8)
+    A = np.full((M, K // 2), 0x22, dtype=np.uint8)
+    B = np.full((N, K // 2), 0x22, dtype=np.uint8)
+    C, _ = mx.gemm(A, sa, B, sb, "e2m1")
+    want = np.array([[sum(32 * 2.0 ** (int(sa[i, b]) + int(sb[j, b]) - 254) for b in range(K // 32))
+                      for j in range(N)] for i in range(M)])
+    assert np.array_equal(C, want)
+
+
+def test_fp4_block_decomposition_through_e4m3():
+    """Every E2M1 value is an E4M3 value: the FP4 product equals the 8-bit
+    product of the same values re-encoded as E4M3 by torch's cast, through
+    the C oracle, block by block."""
+    g = np.random.Generator(np.random.PCG64(11))
+    M, N, K = 9, 7, 256
+    A4 = g.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
+    B4 = g.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+    sa = g.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    sb = g.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    C4, W4 = mx.gemm(A4, sa, B4, sb, "e2m1")
+    to8 = lambda p: torch.from_numpy(mx.decode_e2m1(mx.unpack_fp4(p)).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    Cr, Wr = _blockwise(to8(A4), sa, to8(B4), sb, "e4m3", "e4m3")
+    assert np.all(np.abs(C4 - Cr) <= 1e-12 * Wr)
