@@ -5,7 +5,7 @@ executes anything in this package.  Only the test suite, the smoke check and
 the benchmark's CPU-baseline leg use it.  It shares no code with the GPU path
 and does not import the product package.
 
-Four parts:
+Five parts:
 
 * ``gemm_oracle.c`` (wrapped by :mod:`oracle.reference`): the plain binary64
   triple-loop product C = alpha * A @ B, plus the magnitude W = |alpha| *
@@ -16,6 +16,8 @@ Four parts:
 * :mod:`oracle.mx`: the block-scaled (microscaled) 8-bit product: 32-element
   blocks along K sharing one E8M0 power-of-two scale, written out as the
   scaled elements' binary64 dot products.
+* :mod:`oracle.conv`: two-dimensional convolution (NHWC images, KRSC
+  filters, padding, stride, dilation) as tap-by-tap binary64 products.
 * :mod:`oracle.bookkeeping`: exact-rational tile bookkeeping: the FLOP count,
   the tile grid G, wave efficiency, padding efficiency, K-slices, resident
   workgroups and schedule efficiency.
