@@ -378,6 +378,58 @@ def mx_products(torch, g, inputs, args):
     return out
 
 
+def conv_layers(torch, g, inputs, args):
+    """Implicit-GEMM convolutions (bf16 NHWC images and KRSC filters, fp32
+    accumulate, bf16 NPQK output) of ResNet-like shapes, each next to the
+    plain product of the same M x N x K (A given as a matrix) on the same
+    box."""
+    import numpy as np
+    layers = [
+        # N, H, W, C, K, R, S, pad
+        (32, 56, 56, 128, 128, 3, 3, 1),
+        (64, 28, 28, 256, 256, 3, 3, 1),
+        (32, 56, 56, 256, 64, 1, 1, 0),
+    ]
+    out = []
+    for (N, Hh, W, C, K, R, S, pad) in layers:
+        log("bench: detail convolution", (N, Hh, W, C, K, R, S, pad))
+        P, Q = g.conv_out_size(Hh, W, R, S, pad, pad)
+        M, Kg = N * P * Q, R * S * C
+        flops = 2.0 * M * K * Kg
+        gen = np.random.Generator(np.random.PCG64(7000 + C + K + R))
+        x = torch.from_numpy(gen.standard_normal((N, Hh, W, C), dtype=np.float32)).to(torch.bfloat16).cuda()
+        w = torch.from_numpy(gen.standard_normal((K, R, S, C), dtype=np.float32)).to(torch.bfloat16).cuda()
+        y = torch.empty((N, P, Q, K), dtype=torch.bfloat16, device="cuda")
+        a = g.make_conv_args(N, Hh, W, C, K, R, S, x=x, w=w, y=y, pad_h=pad, pad_w=pad, dtype=g.BF16_BF16)
+        p = g.gemm355_conv2d_plan(a)
+        A = torch.empty((M, Kg), dtype=torch.bfloat16, device="cuda").normal_()
+        ga = g.make_args(M, K, Kg, A=A, B=w, C=y, dtype=g.BF16_BF16)
+        res = {}
+        for name, fn in (("conv", lambda sp, a=a: g.gemm355_conv2d(a, sp)),
+                         ("gemm", lambda sp, ga=ga: g.gemm355_gemm_ex(ga, sp))):
+            c = _Steps(fn, flops)
+            settle(c, torch, args.settle / 4)
+            reps = []
+            for _ in range(3):
+                n = max(10, args.steps // 10)
+                _, ev = time_case(c, torch, n, max(3, args.warmup // 10))
+                reps.append(ev / n)
+            reps.sort()
+            res[name] = reps[1]
+        out.append({
+            "workload": "convolution N=%d %dx%dx%d -> %d, %dx%d filter, pad %d (implicit GEMM M=%d N=%d K=%d, "
+                        "bf16 in, bf16 out)" % (N, Hh, W, C, K, R, S, pad, M, K, Kg),
+            "dtype": "bf16", "out": "bf16", "us_median": round(res["conv"] * 1e6, 2),
+            "tflops": round(flops / res["conv"] / 1e12, 1),
+            "pct_mfma_peak": round(100 * flops / res["conv"] / 1e12 / PEAK_TFLOPS["bf16"], 1),
+            "us_same_size_gemm": round(res["gemm"] * 1e6, 2),
+            "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"], "grid": p["grid"],
+        })
+        del x, w, y, A
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(torch, budget_s=15.0):
     """The oracle (as it stands) on a bounded sample of the headline product:
     the first R rows of A against all of B, R sized from a short probe to
@@ -510,6 +562,8 @@ def main():
         detail.extend(fp8_end_to_end(torch, g, inputs, args))
     if not args.no_detail and (args.workload in (None, "block-scaled")):
         detail.extend(mx_products(torch, g, inputs, args))
+    if not args.no_detail and (args.workload in (None, "convolution")):
+        detail.extend(conv_layers(torch, g, inputs, args))
 
     cpu = None
     if not args.no_cpu_baseline:

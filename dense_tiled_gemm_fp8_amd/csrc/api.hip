@@ -60,7 +60,7 @@ int32_t planning_cus(const gemm355_args &a)
 /* Plan cache: the plan depends on the shape arguments, the knobs and the
  * 16-byte alignment of A and B, never on the data. */
 struct PlanKey {
-    int64_t v[16];
+    int64_t v[32];
     bool operator==(const PlanKey &o) const { return memcmp(v, o.v, sizeof v) == 0; }
 };
 struct PlanKeyHash {
@@ -76,10 +76,15 @@ struct PlanKeyHash {
 };
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 
-PlanKey key_of(const gemm355_args &a, int32_t S)
+PlanKey key_of(const gemm355_args &a, int32_t S, const ConvShape *conv)
 {
     PlanKey k;
     memset(&k, 0, sizeof k);
+    if (conv) {
+        const int64_t *f = &conv->N;
+        for (int i = 0; i < 14; ++i) k.v[16 + i] = f[i];
+        k.v[30] = 1;
+    }
     k.v[0] = a.M;
     k.v[1] = a.N;
     k.v[2] = a.K;
@@ -102,20 +107,20 @@ PlanKey key_of(const gemm355_args &a, int32_t S)
     return k;
 }
 
-gemm355_status get_plan(const gemm355_args &a, Plan &out)
+gemm355_status get_plan(const gemm355_args &a, Plan &out, const ConvShape *conv = nullptr)
 {
     const int32_t S = planning_cus(a);
     if (S < 1) return GEMM355_EINVAL;
-    const PlanKey k = key_of(a, S);
+    const PlanKey k = key_of(a, S, conv);
     {
         std::lock_guard<std::mutex> lk(g_mu);
         auto it = g_plans.find(k);
         if (it != g_plans.end()) {
             out = it->second;
-            return check_pointers(a);
+            return check_pointers(a, conv);
         }
     }
-    gemm355_status st = make_plan(a, S, out);
+    gemm355_status st = make_plan(a, S, out, conv);
     if (st != GEMM355_OK) return st;
     /* pointer overlap is not part of the key: check_pointers runs on hits */
     std::lock_guard<std::mutex> lk(g_mu);
@@ -165,10 +170,10 @@ struct ScratchReaper {
     }
 } g_reaper;
 
-gemm355_status run(const gemm355_args &a, void *stream)
+gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = nullptr)
 {
     Plan P;
-    gemm355_status st = get_plan(a, P);
+    gemm355_status st = get_plan(a, P, conv);
     if (st != GEMM355_OK) return st;
     if (a.M == 0 || a.N == 0) return GEMM355_OK;
     hipStream_t hs = (hipStream_t)stream;
@@ -271,6 +276,22 @@ gemm355_status run(const gemm355_args &a, void *stream)
         if (launch_pack_scales(sp, hs) != hipSuccess) return GEMM355_EHIP;
         gp.bsb = (const uint8_t *)sp.dst;
     }
+    gp.cv_H = gp.cv_W = gp.cv_C = gp.cv_S = gp.cv_P = gp.cv_Q = 0;
+    gp.cv_ph = gp.cv_pw = gp.cv_sh = gp.cv_sw = gp.cv_dh = gp.cv_dw = 0;
+    if (conv) {
+        gp.cv_H = (int32_t)conv->H;
+        gp.cv_W = (int32_t)conv->W;
+        gp.cv_C = (int32_t)conv->C;
+        gp.cv_S = (int32_t)conv->S;
+        gp.cv_P = (int32_t)conv->P;
+        gp.cv_Q = (int32_t)conv->Q;
+        gp.cv_ph = (int32_t)conv->pad_h;
+        gp.cv_pw = (int32_t)conv->pad_w;
+        gp.cv_sh = (int32_t)conv->stride_h;
+        gp.cv_sw = (int32_t)conv->stride_w;
+        gp.cv_dh = (int32_t)conv->dil_h;
+        gp.cv_dw = (int32_t)conv->dil_w;
+    }
     gp.s = P.s;
     /* operand-format pair of an 8-bit product: 0 E4M3 x E4M3, 1 E5M2 x E5M2,
      * 2 E4M3 x E5M2 */
@@ -297,9 +318,87 @@ gemm355_status run(const gemm355_args &a, void *stream)
     return GEMM355_OK;
 }
 
+/* A convolution's implicit product: validation, output size, the product's
+ * arguments and the shape the main loop gathers A with. */
+gemm355_status conv_setup(const gemm355_conv_args *c, gemm355_args &a, ConvShape &cs)
+{
+    if (!c) return GEMM355_EINVAL;
+    if (c->N < 1 || c->H < 1 || c->W < 1 || c->C < 1 || c->K < 1 || c->R < 1 || c->S < 1) return GEMM355_EINVAL;
+    if (c->stride_h < 1 || c->stride_w < 1 || c->dil_h < 1 || c->dil_w < 1 || c->pad_h < 0 || c->pad_w < 0)
+        return GEMM355_EINVAL;
+    const int64_t lim = (int64_t)1 << 30;
+    if (c->N > lim || c->H > lim || c->W > lim || c->C > lim || c->K > lim || c->R > lim || c->S > lim ||
+        c->pad_h > lim || c->pad_w > lim || c->stride_h > lim || c->stride_w > lim || c->dil_h > lim ||
+        c->dil_w > lim)
+        return GEMM355_EUNSUPPORTED;
+    const int64_t ph = c->H + 2 * c->pad_h - c->dil_h * (c->R - 1) - 1;
+    const int64_t pw = c->W + 2 * c->pad_w - c->dil_w * (c->S - 1) - 1;
+    if (ph < 0 || pw < 0) return GEMM355_EINVAL;
+    if ((int)c->dtype < 0 || (int)c->dtype > 15) return GEMM355_EINVAL;
+    if (c->dtype != GEMM355_BF16_F32 && c->dtype != GEMM355_BF16_BF16) return GEMM355_EUNSUPPORTED;
+    cs.N = c->N;
+    cs.H = c->H;
+    cs.W = c->W;
+    cs.C = c->C;
+    cs.R = c->R;
+    cs.S = c->S;
+    cs.P = ph / c->stride_h + 1;
+    cs.Q = pw / c->stride_w + 1;
+    cs.pad_h = c->pad_h;
+    cs.pad_w = c->pad_w;
+    cs.stride_h = c->stride_h;
+    cs.stride_w = c->stride_w;
+    cs.dil_h = c->dil_h;
+    cs.dil_w = c->dil_w;
+    if (cs.N * cs.P * cs.Q > lim || cs.R * cs.S * cs.C > lim) return GEMM355_EUNSUPPORTED;
+    memset(&a, 0, sizeof a);
+    a.M = cs.N * cs.P * cs.Q;
+    a.N = c->K;
+    a.K = cs.R * cs.S * cs.C;
+    a.A = c->x;
+    a.lda = a.K;
+    a.B = c->w;
+    a.ldb = a.K;
+    a.C = c->y;
+    a.ldc = c->K;
+    a.batch = 1;
+    a.dtype = c->dtype;
+    a.layout = GEMM355_A_ROW_B_COL;
+    a.split_k = c->split_k;
+    a.persistent = c->persistent;
+    a.tile = c->tile;
+    a.cus = c->cus;
+    a.workspace = c->workspace;
+    a.workspace_bytes = c->workspace_bytes;
+    return GEMM355_OK;
+}
+
 } /* namespace */
 
 extern "C" {
+
+gemm355_status gemm355_conv2d(const gemm355_conv_args *args, void *stream)
+{
+    gemm355_args a;
+    ConvShape cs;
+    const gemm355_status st = conv_setup(args, a, cs);
+    if (st != GEMM355_OK) return st;
+    return run(a, stream, &cs);
+}
+
+gemm355_status gemm355_conv2d_plan(const gemm355_conv_args *args, gemm355_plan_t *out)
+{
+    if (!out) return GEMM355_EINVAL;
+    gemm355_args a;
+    ConvShape cs;
+    gemm355_status st = conv_setup(args, a, cs);
+    if (st != GEMM355_OK) return st;
+    Plan P;
+    st = get_plan(a, P, &cs);
+    if (st != GEMM355_OK) return st;
+    *out = P.pub;
+    return GEMM355_OK;
+}
 
 gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                             const void *B, int64_t ldb, void *C, int64_t ldc, gemm355_dtype dtype,
@@ -416,7 +515,7 @@ int32_t gemm355_num_tiles(void) { return kNumTiles; }
 
 gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_M, int32_t *T_N,
                                  int32_t *T_K, int32_t *stages, int32_t *waves, int32_t *lds_bytes,
-                                 int32_t *b_max)
+                                 int32_t *b_max, int32_t *op)
 {
     if (tile < 0 || tile >= kNumTiles) return GEMM355_EINVAL;
     const TileCfg &c = kTiles[tile];
@@ -428,6 +527,7 @@ gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_
     if (waves) *waves = tile_waves(c);
     if (lds_bytes) *lds_bytes = c.lds_bytes;
     if (b_max) *b_max = resident_workgroups(tile);
+    if (op) *op = c.op;
     return GEMM355_OK;
 }
 

@@ -31,6 +31,10 @@ struct GemmParams {
     const uint8_t *bsa, *bsb;
     int64_t ktp_a, ktp_b;         /* bytes between K-tiles: 4 M, 4 N        */
     int64_t stride_bsa, stride_bsb;   /* bytes between batch entries        */
+    /* convolution tiles: A row m = (n, p, q) gathers x[n][p*sh - ph + r*dh]
+     * [q*sw - pw + s*dw][c] for K-tile (r, s, 64-channel block) */
+    int32_t cv_H, cv_W, cv_C, cv_S, cv_P, cv_Q;
+    int32_t cv_ph, cv_pw, cv_sh, cv_sw, cv_dh, cv_dw;
     Sched s;
 };
 

@@ -174,13 +174,15 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * issued into the stage just freed, and the last step's MFMAs overlap the
  * reads of the next tile's first fragments.
  */
-template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
+template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int OP, int MI, int FMT>
 __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
     /* element class: 0 bf16, 1 8-bit, 2 8-bit with E8M0 block scales, 3 FP4
      * (E2M1, two per byte) with E8M0 block scales.  FP8 marks the f8f6f4
      * matrix instructions (classes 1-3). */
     constexpr bool FP8 = EL != 0, MX = EL >= 2, FP4 = EL == 3;
+    /* OP 1: convolution, A gathered from NHWC images (kernels.h) */
+    constexpr bool CONV = OP == 1;
     /* operand formats (instruction format codes: 0 E4M3, 1 E5M2, 4 E2M1):
      * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B); FP4 both 4 */
     constexpr int FA = FP4 ? 4 : FMT == 1 ? 1 : 0, FB = FP4 ? 4 : FMT >= 1 ? 1 : 0;
@@ -222,6 +224,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
      * before its second-to-last step, copies over its last two steps */
     static_assert(SPREAD != 2 || (KSTEPS == 4 && STAGES == 2 && LOADS % 2 == 0), "two-step prefetch schedule");
     static_assert(SPREAD != 3 || STAGES >= 3, "producer wavefronts run two K-tiles ahead");
+    static_assert(!CONV || (!FP8 && SPREAD == 0 && RB == 128), "convolution: bf16, 64-channel K-tiles copied in one step");
     static_assert(A_LOADS * CW * ROWS_PER_DMA == TM && B_LOADS * CW * ROWS_PER_DMA == TN, "whole copies");
     static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == SW * (TM + TN)),
                   "block scales: whole dwords per row and K-tile, whole 64-row copies per wavefront");
@@ -263,14 +266,35 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         }
         const Unit un = decode_unit(p.s, u);
         const int32_t m0 = un.tile_m * TM, n0 = un.tile_n * TN;
-        const i32x4 ra = rsrc_words(p.A + (int64_t)un.batch * p.stride_a + (int64_t)m0 * p.lda);
+        /* convolution: A's offsets are taken from the first image */
+        const i32x4 ra = rsrc_words(CONV ? p.A : p.A + (int64_t)un.batch * p.stride_a + (int64_t)m0 * p.lda);
         const i32x4 rb = rsrc_words(p.B + (int64_t)un.batch * p.stride_b + (int64_t)n0 * p.ldb);
 
         uint32_t aoff[A_LOADS], boff[B_LOADS];
+        /* convolution: the lane's output pixel (n, p, q) per A copy, as the
+         * window's top-left input position (ch0, cw0) and the byte offset of
+         * that position plus the lane's chunk (negative while the window
+         * starts in the padding; only in-image taps are read) */
+        int32_t ch0[CONV ? A_LOADS : 1], cw0[CONV ? A_LOADS : 1];
 #pragma unroll
         for (int i = 0; i < A_LOADS; ++i) {
             const int r = (i * CW + cw) * ROWS_PER_DMA + drow;
-            aoff[i] = (m0 + r < p.M) ? (uint32_t)(r * p.lda + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
+            if constexpr (CONV) {
+                const int32_t m = m0 + r, pq_n = p.cv_P * p.cv_Q;
+                if (m < p.M) {
+                    const int32_t n = m / pq_n, pq = m - n * pq_n, pp = pq / p.cv_Q, qq = pq - pp * p.cv_Q;
+                    ch0[i] = pp * p.cv_sh - p.cv_ph;
+                    cw0[i] = qq * p.cv_sw - p.cv_pw;
+                    aoff[i] = (uint32_t)(((n * p.cv_H + ch0[i]) * p.cv_W + cw0[i]) * p.cv_C * 2 +
+                                         lchunk[TWO ? i & 1 : 0] * 16);
+                } else {
+                    ch0[i] = -(1 << 29);
+                    cw0[i] = 0;
+                    aoff[i] = 0;
+                }
+            } else {
+                aoff[i] = (m0 + r < p.M) ? (uint32_t)(r * p.lda + lchunk[TWO ? i & 1 : 0] * 16) : kOOB;
+            }
         }
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
@@ -324,12 +348,47 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             k.v[1] = TWO ? ((int32_t)(kb + lchunk[1] * 16) < p.Kb) && (i < nkt) : k.v[0];
             return k;
         };
+        /* convolution: filter tap and channel block of the next K-tile to
+         * be copied (K-tiles are copied once each, in order); ctap holds the
+         * one whose copies are being issued */
+        struct Tap {
+            int32_t rd, sd;   /* r dh, s dw */
+            uint32_t off;     /* byte offset of the tap and channel block */
+        };
+        int32_t t_cb = 0, t_s = 0, t_r = 0;
+        const int32_t n_cb = CONV ? p.cv_C / 64 : 1;
+        if constexpr (CONV) {
+            const int32_t rs = un.kt_begin / n_cb;
+            t_cb = un.kt_begin - rs * n_cb;
+            t_r = rs / p.cv_S;
+            t_s = rs - t_r * p.cv_S;
+        }
+        Tap ctap{0, 0, 0u};
+        auto next_tap = [&]() __attribute__((always_inline)) {
+            if constexpr (CONV) {
+                ctap.rd = t_r * p.cv_dh;
+                ctap.sd = t_s * p.cv_dw;
+                ctap.off = (uint32_t)((ctap.rd * p.cv_W + ctap.sd) * p.cv_C * 2 + t_cb * 128);
+                if (++t_cb == n_cb) {
+                    t_cb = 0;
+                    if (++t_s == p.cv_S) {
+                        t_s = 0;
+                        ++t_r;
+                    }
+                }
+            }
+        };
         auto dma = [&](auto dc, uint32_t so, uint32_t kb, const KV &kv) __attribute__((always_inline)) {
             constexpr int d = decltype(dc)::value;
             constexpr int di = d < A_LOADS ? d : d - A_LOADS;
             const bool ok = kv.v[TWO ? di & 1 : 0];
             const uint32_t dst = smem_base + so + cw * 1024;
-            if constexpr (d < A_LOADS) {
+            if constexpr (d < A_LOADS && CONV) {
+                /* only taps inside the image are read; the rest are zero */
+                const bool in = ok && (uint32_t)(ch0[d] + ctap.rd) < (uint32_t)p.cv_H &&
+                                (uint32_t)(cw0[d] + ctap.sd) < (uint32_t)p.cv_W;
+                dma16<d * CW * 1024>(ra, dst, in ? aoff[d] + ctap.off : kOOB);
+            } else if constexpr (d < A_LOADS) {
                 dma16<d * CW * 1024>(ra, dst, ok ? aoff[d] + kb : kOOB);
             } else if constexpr (d < A_LOADS + B_LOADS) {
                 dma16<A_BYTES + (d - A_LOADS) * CW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
@@ -342,6 +401,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
             const KV kv = kvalid(i);
             const uint32_t kb = (uint32_t)ktile(i) * RB;
+            next_tap();
             unroll<LOADS>([&](auto dc) __attribute__((always_inline)) { dma(dc, so, kb, kv); });
         };
 
@@ -569,6 +629,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             } else {
                 kv = kvalid(kt + STAGES);
                 kb = (uint32_t)ktile(kt + STAGES) * RB;
+                next_tap();
                 step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, 0, so, kb, kv, IC<KSTEPS - 1>{});
             }
         };
@@ -998,31 +1059,31 @@ __global__ __launch_bounds__(256) void zero_kernel(void *C, int32_t M, int32_t N
 
 /* ------------------------------------------------------------------ launch */
 
-template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI, int FMT>
+template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int OP, int MI, int FMT>
 static hipError_t launch_one(const GemmParams &p, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, FMT>), dim3(p.s.grid),
+    hipLaunchKernelGGL((gemm_tile_kernel<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, OP, MI, FMT>), dim3(p.s.grid),
                        dim3((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 /* bf16 tiles have one instantiation; 8-bit tiles one per operand-format pair */
-template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int MI>
+template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN, int SPREAD, int OP, int MI>
 static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stream)
 {
     if constexpr (EL == 3) {
         if (fmt != 0) return hipErrorInvalidValue;
-        return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+        return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, OP, MI, 0>(p, stream);
     } else if constexpr (EL != 0) {
         switch (fmt) {
-        case 0: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
-        case 1: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 1>(p, stream);
-        case 2: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 2>(p, stream);
+        case 0: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, OP, MI, 0>(p, stream);
+        case 1: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, OP, MI, 1>(p, stream);
+        case 2: return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, OP, MI, 2>(p, stream);
         default: return hipErrorInvalidValue;
         }
     } else {
         if (fmt != 0) return hipErrorInvalidValue;
-        return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, MI, 0>(p, stream);
+        return launch_one<TM, TN, EL, MINB, RB, STAGES, WGM, WGN, SPREAD, OP, MI, 0>(p, stream);
     }
 }
 
@@ -1030,84 +1091,89 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
  * id, TM, TN, element class (false bf16, true 8-bit, 2 block-scaled 8-bit,
  * 3 block-scaled FP4),
  * groups per CU, K-tile bytes, stages, waves along M, N, copy schedule,
- * MFMA block edge */
+ * MFMA block edge, operation (0 matrix product, 1 convolution) */
 #define GEMM355_TILES(X)                                                                          \
-    X(0, 256, 256, false, 1, 128, 2, 2, 2, 0, 32)                                                       \
-    X(1, 128, 128, false, 2, 128, 2, 2, 2, 0, 32)                                                       \
-    X(2, 64, 64, false, 4, 128, 2, 2, 2, 0, 32)                                                         \
-    X(3, 256, 256, true, 1, 128, 2, 2, 2, 0, 32)                                                        \
-    X(4, 128, 128, true, 2, 128, 2, 2, 2, 0, 32)                                                        \
-    X(5, 64, 64, true, 4, 128, 2, 2, 2, 0, 32)                                                          \
-    X(6, 256, 256, false, 1, 64, 4, 2, 2, 0, 32)                                                        \
-    X(7, 256, 256, false, 1, 64, 5, 2, 2, 0, 32)                                                        \
-    X(8, 256, 256, true, 1, 64, 4, 2, 2, 0, 32)                                                         \
-    X(9, 256, 256, true, 1, 64, 5, 2, 2, 0, 32)                                                         \
-    X(10, 256, 256, false, 1, 128, 2, 2, 4, 0, 32)                                                      \
-    X(11, 256, 256, false, 1, 64, 4, 2, 4, 0, 32)                                                       \
-    X(12, 256, 256, true, 1, 128, 2, 2, 4, 0, 32)                                                       \
-    X(13, 256, 256, true, 1, 64, 4, 2, 4, 0, 32)                                                        \
-    X(14, 64, 64, false, 1, 128, 8, 2, 2, 0, 32)                                                        \
-    X(15, 64, 64, false, 2, 128, 4, 2, 2, 0, 32)                                                        \
-    X(16, 128, 128, false, 1, 128, 4, 2, 2, 0, 32)                                                      \
-    X(17, 64, 64, true, 1, 128, 8, 2, 2, 0, 32)                                                         \
-    X(18, 64, 64, true, 2, 128, 4, 2, 2, 0, 32)                                                         \
-    X(19, 128, 128, true, 1, 128, 4, 2, 2, 0, 32)                                                       \
-    X(20, 64, 64, false, 4, 128, 2, 1, 1, 0, 32)                                                        \
-    X(21, 64, 64, false, 2, 128, 4, 1, 1, 0, 32)                                                        \
-    X(22, 64, 64, true, 4, 128, 2, 1, 1, 0, 32)                                                         \
-    X(23, 64, 64, true, 2, 128, 4, 1, 1, 0, 32)                                                         \
-    X(24, 256, 256, false, 1, 64, 4, 2, 2, 1, 32)                                                       \
-    X(25, 256, 256, false, 1, 64, 5, 2, 2, 1, 32)                                                       \
-    X(26, 256, 256, false, 1, 64, 4, 2, 4, 1, 32)                                                       \
-    X(27, 256, 256, false, 1, 64, 5, 2, 4, 1, 32)                                                       \
-    X(28, 256, 256, true, 1, 64, 4, 2, 2, 1, 32)                                                        \
-    X(29, 256, 256, true, 1, 64, 5, 2, 2, 1, 32)                                                        \
-    X(30, 256, 256, true, 1, 64, 4, 2, 4, 1, 32)                                                        \
-    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1, 32)                                                        \
-    X(32, 256, 256, false, 1, 128, 2, 4, 4, 0, 32)                                                      \
-    X(33, 256, 256, false, 1, 64, 4, 4, 4, 0, 32)                                                       \
-    X(34, 256, 256, false, 1, 64, 4, 4, 4, 1, 32)                                                   \
-    X(35, 256, 256, false, 1, 128, 2, 2, 2, 0, 16)                                                  \
-    X(36, 256, 256, false, 1, 128, 2, 2, 4, 0, 16)                                                  \
-    X(37, 256, 256, false, 1, 64, 4, 2, 4, 0, 16)                                                   \
-    X(38, 256, 256, false, 1, 64, 4, 2, 2, 0, 16)                                                   \
-    X(39, 256, 256, false, 1, 64, 4, 2, 2, 1, 16)                                                   \
-    X(40, 256, 256, false, 1, 64, 5, 2, 2, 0, 16)                                                   \
-    X(41, 256, 256, false, 1, 128, 2, 2, 2, 2, 32)                                                  \
-    X(42, 256, 256, false, 1, 128, 2, 2, 4, 2, 32)                                                  \
-    X(43, 128, 128, false, 2, 128, 2, 2, 2, 2, 32)                                                  \
-    X(44, 256, 128, false, 1, 128, 3, 2, 2, 3, 32)                                                  \
-    X(45, 256, 128, false, 1, 128, 3, 2, 2, 3, 16)                                                  \
-    X(46, 256, 128, true, 1, 128, 3, 2, 2, 3, 32)                                                   \
-    X(47, 256, 128, false, 1, 128, 3, 2, 2, 0, 32)                                                  \
-    X(48, 256, 256, 2, 1, 128, 2, 2, 2, 0, 32)                                                      \
-    X(49, 128, 128, 2, 2, 128, 2, 2, 2, 0, 32)                                                      \
-    X(50, 128, 128, 2, 1, 128, 4, 2, 2, 0, 32)                                                      \
-    X(51, 256, 256, 3, 1, 128, 2, 2, 2, 0, 32)                                                      \
-    X(52, 128, 128, 3, 2, 128, 2, 2, 2, 0, 32)                                                      \
-    X(53, 128, 128, 3, 1, 128, 4, 2, 2, 0, 32)
+    X(0, 256, 256, false, 1, 128, 2, 2, 2, 0, 32, 0)                                                       \
+    X(1, 128, 128, false, 2, 128, 2, 2, 2, 0, 32, 0)                                                       \
+    X(2, 64, 64, false, 4, 128, 2, 2, 2, 0, 32, 0)                                                         \
+    X(3, 256, 256, true, 1, 128, 2, 2, 2, 0, 32, 0)                                                        \
+    X(4, 128, 128, true, 2, 128, 2, 2, 2, 0, 32, 0)                                                        \
+    X(5, 64, 64, true, 4, 128, 2, 2, 2, 0, 32, 0)                                                          \
+    X(6, 256, 256, false, 1, 64, 4, 2, 2, 0, 32, 0)                                                        \
+    X(7, 256, 256, false, 1, 64, 5, 2, 2, 0, 32, 0)                                                        \
+    X(8, 256, 256, true, 1, 64, 4, 2, 2, 0, 32, 0)                                                         \
+    X(9, 256, 256, true, 1, 64, 5, 2, 2, 0, 32, 0)                                                         \
+    X(10, 256, 256, false, 1, 128, 2, 2, 4, 0, 32, 0)                                                      \
+    X(11, 256, 256, false, 1, 64, 4, 2, 4, 0, 32, 0)                                                       \
+    X(12, 256, 256, true, 1, 128, 2, 2, 4, 0, 32, 0)                                                       \
+    X(13, 256, 256, true, 1, 64, 4, 2, 4, 0, 32, 0)                                                        \
+    X(14, 64, 64, false, 1, 128, 8, 2, 2, 0, 32, 0)                                                        \
+    X(15, 64, 64, false, 2, 128, 4, 2, 2, 0, 32, 0)                                                        \
+    X(16, 128, 128, false, 1, 128, 4, 2, 2, 0, 32, 0)                                                      \
+    X(17, 64, 64, true, 1, 128, 8, 2, 2, 0, 32, 0)                                                         \
+    X(18, 64, 64, true, 2, 128, 4, 2, 2, 0, 32, 0)                                                         \
+    X(19, 128, 128, true, 1, 128, 4, 2, 2, 0, 32, 0)                                                       \
+    X(20, 64, 64, false, 4, 128, 2, 1, 1, 0, 32, 0)                                                        \
+    X(21, 64, 64, false, 2, 128, 4, 1, 1, 0, 32, 0)                                                        \
+    X(22, 64, 64, true, 4, 128, 2, 1, 1, 0, 32, 0)                                                         \
+    X(23, 64, 64, true, 2, 128, 4, 1, 1, 0, 32, 0)                                                         \
+    X(24, 256, 256, false, 1, 64, 4, 2, 2, 1, 32, 0)                                                       \
+    X(25, 256, 256, false, 1, 64, 5, 2, 2, 1, 32, 0)                                                       \
+    X(26, 256, 256, false, 1, 64, 4, 2, 4, 1, 32, 0)                                                       \
+    X(27, 256, 256, false, 1, 64, 5, 2, 4, 1, 32, 0)                                                       \
+    X(28, 256, 256, true, 1, 64, 4, 2, 2, 1, 32, 0)                                                        \
+    X(29, 256, 256, true, 1, 64, 5, 2, 2, 1, 32, 0)                                                        \
+    X(30, 256, 256, true, 1, 64, 4, 2, 4, 1, 32, 0)                                                        \
+    X(31, 256, 256, true, 1, 64, 5, 2, 4, 1, 32, 0)                                                        \
+    X(32, 256, 256, false, 1, 128, 2, 4, 4, 0, 32, 0)                                                      \
+    X(33, 256, 256, false, 1, 64, 4, 4, 4, 0, 32, 0)                                                       \
+    X(34, 256, 256, false, 1, 64, 4, 4, 4, 1, 32, 0)                                                   \
+    X(35, 256, 256, false, 1, 128, 2, 2, 2, 0, 16, 0)                                                  \
+    X(36, 256, 256, false, 1, 128, 2, 2, 4, 0, 16, 0)                                                  \
+    X(37, 256, 256, false, 1, 64, 4, 2, 4, 0, 16, 0)                                                   \
+    X(38, 256, 256, false, 1, 64, 4, 2, 2, 0, 16, 0)                                                   \
+    X(39, 256, 256, false, 1, 64, 4, 2, 2, 1, 16, 0)                                                   \
+    X(40, 256, 256, false, 1, 64, 5, 2, 2, 0, 16, 0)                                                   \
+    X(41, 256, 256, false, 1, 128, 2, 2, 2, 2, 32, 0)                                                  \
+    X(42, 256, 256, false, 1, 128, 2, 2, 4, 2, 32, 0)                                                  \
+    X(43, 128, 128, false, 2, 128, 2, 2, 2, 2, 32, 0)                                                  \
+    X(44, 256, 128, false, 1, 128, 3, 2, 2, 3, 32, 0)                                                  \
+    X(45, 256, 128, false, 1, 128, 3, 2, 2, 3, 16, 0)                                                  \
+    X(46, 256, 128, true, 1, 128, 3, 2, 2, 3, 32, 0)                                                   \
+    X(47, 256, 128, false, 1, 128, 3, 2, 2, 0, 32, 0)                                                  \
+    X(48, 256, 256, 2, 1, 128, 2, 2, 2, 0, 32, 0)                                                      \
+    X(49, 128, 128, 2, 2, 128, 2, 2, 2, 0, 32, 0)                                                      \
+    X(50, 128, 128, 2, 1, 128, 4, 2, 2, 0, 32, 0)                                                      \
+    X(51, 256, 256, 3, 1, 128, 2, 2, 2, 0, 32, 0)                                                      \
+    X(52, 128, 128, 3, 2, 128, 2, 2, 2, 0, 32, 0)                                                      \
+    X(53, 128, 128, 3, 1, 128, 4, 2, 2, 0, 32, 0)                                                   \
+    X(54, 256, 256, false, 1, 128, 2, 2, 2, 0, 32, 1)                                               \
+    X(55, 128, 128, false, 2, 128, 2, 2, 2, 0, 32, 1)                                               \
+    X(56, 64, 64, false, 4, 128, 2, 2, 2, 0, 32, 1)                                                 \
+    X(57, 256, 256, false, 1, 128, 2, 2, 4, 0, 16, 1)                                               \
+    X(58, 128, 128, false, 1, 128, 4, 2, 2, 0, 32, 1)
 
 /* every instantiation agrees with its tile-table entry */
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi)                                                      \
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn)                                                      \
     static_assert(kTiles[id].dtype_class == (int)(f8) && kTiles[id].TM == tm &&                  \
                       kTiles[id].TN == tn && kTiles[id].min_blocks == mb &&                      \
                       kTiles[id].row_bytes == rb && kTiles[id].stages == st &&                   \
                       kTiles[id].waves_m == wm && kTiles[id].waves_n == wn &&                    \
                       kTiles[id].TK == ((f8) == 3 ? 2 * rb : (f8) ? rb : rb / 2) &&             \
                       kTiles[id].spread == sp &&                                                 \
-                      kTiles[id].mfma == mi,                                                     \
+                      kTiles[id].mfma == mi && kTiles[id].op == opn,                              \
                   "tile table entry " #id);
 GEMM355_TILES(X)
 #undef X
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) +1
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn) +1
 static_assert(0 GEMM355_TILES(X) == kNumTiles, "one instantiation per tile-table entry");
 #undef X
 
 hipError_t launch_gemm(int32_t tile, int32_t fmt, const GemmParams &p, hipStream_t stream)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) \
-    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp, mi>(fmt, p, stream);
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn) \
+    case id: return launch_tile<tm, tn, f8, mb, rb, st, wm, wn, sp, opn, mi>(fmt, p, stream);
         GEMM355_TILES(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -1117,8 +1183,8 @@ hipError_t launch_gemm(int32_t tile, int32_t fmt, const GemmParams &p, hipStream
 const void *gemm_kernel_symbol(int32_t tile)
 {
     switch (tile) {
-#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi) \
-    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp, mi, 0>;
+#define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn) \
+    case id: return (const void *)gemm_tile_kernel<tm, tn, f8, mb, rb, st, wm, wn, sp, opn, mi, 0>;
         GEMM355_TILES(X)
 #undef X
     default: return nullptr;

@@ -63,12 +63,20 @@ inline int32_t dtype_fmt_b(gemm355_dtype d)
             (d >= GEMM355_MXE5M2_F32 && d <= GEMM355_MXE4M3_E5M2_BF16)) ? 1 : 0;
 }
 
+/* A convolution planned as its implicit product (conv != null below): the
+ * product's A is not a matrix in memory, so its pointer checks and repack
+ * decisions come from here. */
+struct ConvShape {
+    int64_t N, H, W, C, R, S, P, Q;
+    int64_t pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
+};
+
 /* Validate `a` and plan it for S compute units.  Never touches a device. */
-gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &out);
+gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &out, const ConvShape *conv = nullptr);
 
 /* Null, alignment and overlap checks of the pointers in `a` (run on every
  * call, also when the plan comes from the cache). */
-gemm355_status check_pointers(const gemm355_args &a);
+gemm355_status check_pointers(const gemm355_args &a, const ConvShape *conv = nullptr);
 
 /* Exact rational -> nearest binary64 (ties to even). */
 double rational_to_double(uint64_t num, uint64_t den);

@@ -272,7 +272,7 @@ int32_t resident_workgroups(int32_t tile)
     return std::min(by_lds, std::min(by_regs, by_waves));
 }
 
-gemm355_status check_pointers(const gemm355_args &a)
+gemm355_status check_pointers(const gemm355_args &a, const ConvShape *conv)
 {
     const int32_t ebits = dtype_ebits(a.dtype);
     const int32_t esize = ebits >= 8 ? ebits / 8 : 1;   /* alignment */
@@ -301,9 +301,11 @@ gemm355_status check_pointers(const gemm355_args &a)
     const int64_t a_rows = a_row ? M : K, a_cols = a_row ? K : M;
     const int64_t b_rows = b_col ? N : K, b_cols = b_col ? K : N;
     const uintptr_t a_lo = (uintptr_t)a.A;
-    /* element counts to bytes, rounded up (4-bit elements pack two a byte) */
+    /* element counts to bytes, rounded up (4-bit elements pack two a byte);
+     * a convolution's A is its input images */
     auto span = [ebits](int64_t elems) { return (uintptr_t)((elems * ebits + 7) / 8); };
-    const uintptr_t a_hi = a_lo + span((batch - 1) * a.stride_a + (a_rows - 1) * a.lda + a_cols);
+    const uintptr_t a_hi = a_lo + (conv ? span(conv->N * conv->H * conv->W * conv->C)
+                                        : span((batch - 1) * a.stride_a + (a_rows - 1) * a.lda + a_cols));
     const uintptr_t b_lo = (uintptr_t)a.B;
     const uintptr_t b_hi = b_lo + span((batch - 1) * a.stride_b + (b_rows - 1) * a.ldb + b_cols);
     if ((c_lo < a_hi && a_lo < c_hi) || (c_lo < b_hi && b_lo < c_hi)) return GEMM355_EINVAL;
@@ -318,7 +320,7 @@ gemm355_status check_pointers(const gemm355_args &a)
     return GEMM355_OK;
 }
 
-gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
+gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvShape *conv)
 {
     memset(&P, 0, sizeof P);
     if ((int)a.dtype < 0 || (int)a.dtype >= kNumDtypes) return GEMM355_EINVAL;
@@ -336,7 +338,8 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
-    if (a.tile >= 0 && kTiles[a.tile].dtype_class != dclass) return GEMM355_EINVAL;
+    const int32_t want_op = conv ? 1 : 0;
+    if (a.tile >= 0 && (kTiles[a.tile].dtype_class != dclass || kTiles[a.tile].op != want_op)) return GEMM355_EINVAL;
 
     const int64_t M = a.M, N = a.N, K = a.K, batch = a.batch;
     if (a.lda < std::max<int64_t>(1, a_row ? K : M)) return GEMM355_EINVAL;
@@ -362,7 +365,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
 
     const bool work = M > 0 && N > 0;
     {
-        const gemm355_status pst = check_pointers(a);
+        const gemm355_status pst = check_pointers(a, conv);
         if (pst != GEMM355_OK) return pst;
     }
 
@@ -378,6 +381,14 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
                (batch > 1 && bytes_of(a.stride_b) % 16);
     /* the repack passes move whole bytes per element */
     if (fp4 && (P.pack_a || P.pack_b)) return GEMM355_EUNSUPPORTED;
+    if (conv) {
+        /* the main loop gathers A from the images itself: 64-channel K-tiles
+         * of 16-byte aligned pixels; B (the filters) must be native */
+        if (P.pack_b || misaligned16(a.A) || (conv->C * 2) % 128) return GEMM355_EUNSUPPORTED;
+        /* pixel offsets are 32-bit from the first image */
+        if (conv->N * conv->H * conv->W * conv->C * 2 > kMaxOffset) return GEMM355_EUNSUPPORTED;
+        P.pack_a = 0;
+    }
     if (P.pack_a) {
         P.lda_b = packed_ld;
         P.stride_a_b = M * packed_ld;
@@ -401,7 +412,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P)
     Cand best;
     for (int32_t t = 0; t < kNumTiles; ++t) {
         const TileCfg &cfg = kTiles[t];
-        if (cfg.dtype_class != dclass) continue;
+        if (cfg.dtype_class != dclass || cfg.op != want_op) continue;
         if (a.tile >= 0 && a.tile != t) continue;
         Cand base;
         base.tile = t;

@@ -50,6 +50,9 @@ struct TileCfg {
     /* planning prior: fraction of the sustained HBM rate the tile reaches
      * when the product is bound by memory (measured on the long-K shapes) */
     float stream_eff;
+    int32_t op;            /* 0 matrix product; 1 convolution (A gathered
+                              from NHWC images, K-tiles of 64 channels of
+                              one filter tap); omitted entries are 0       */
 };
 
 /* gfx950 compute-unit resources used by the occupancy arithmetic. */
@@ -133,6 +136,13 @@ constexpr TileCfg kTiles[] = {
     {3, 256, 256, 256, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 136, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
     {3, 128, 128, 256, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 136, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
     {3, 128, 128, 256, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 136, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
+    /* convolution (bf16): the matrix tiles 0, 1, 2, 36 and 16 with A
+     * gathered from the images */
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f, 1},
+    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f, 1},
+    {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f, 1},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f, 1},
+    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f, 1},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

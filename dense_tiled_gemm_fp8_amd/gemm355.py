@@ -69,6 +69,19 @@ class gemm355_plan_t(ctypes.Structure):
     ]
 
 
+class gemm355_conv_args(ctypes.Structure):
+    _fields_ = [
+        ("N", _i64), ("H", _i64), ("W", _i64), ("C", _i64),
+        ("K", _i64), ("R", _i64), ("S", _i64),
+        ("pad_h", _i64), ("pad_w", _i64), ("stride_h", _i64), ("stride_w", _i64),
+        ("dil_h", _i64), ("dil_w", _i64),
+        ("x", _vp), ("w", _vp), ("y", _vp),
+        ("dtype", ctypes.c_int),
+        ("split_k", _i32), ("persistent", _i32), ("tile", _i32), ("cus", _i32),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
 _lib.gemm355_gemm.restype = ctypes.c_int
 _lib.gemm355_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                               ctypes.c_int, ctypes.c_int, _i32, _i32, _vp]
@@ -87,18 +100,22 @@ _lib.gemm355_unit.argtypes = [ctypes.POINTER(gemm355_args), _i64] + [ctypes.POIN
 _lib.gemm355_num_tiles.restype = _i32
 _lib.gemm355_num_tiles.argtypes = []
 _lib.gemm355_tile_info.restype = ctypes.c_int
-_lib.gemm355_tile_info.argtypes = [_i32] + [ctypes.POINTER(_i32)] * 8
+_lib.gemm355_tile_info.argtypes = [_i32] + [ctypes.POINTER(_i32)] * 9
 _lib.gemm355_tile_occupancy.restype = ctypes.c_int
 _lib.gemm355_tile_occupancy.argtypes = [_i32, ctypes.POINTER(_i32)]
 _lib.gemm355_quantize.restype = ctypes.c_int
 _lib.gemm355_quantize.argtypes = [_vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]
+_lib.gemm355_conv2d.restype = ctypes.c_int
+_lib.gemm355_conv2d.argtypes = [ctypes.POINTER(gemm355_conv_args), _vp]
+_lib.gemm355_conv2d_plan.restype = ctypes.c_int
+_lib.gemm355_conv2d_plan.argtypes = [ctypes.POINTER(gemm355_conv_args), ctypes.POINTER(gemm355_plan_t)]
 _lib.gemm355_status_string.restype = ctypes.c_char_p
 _lib.gemm355_status_string.argtypes = [ctypes.c_int]
 
 EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_plan", "gemm355_eta_wave",
             "gemm355_eta_pad", "gemm355_kslice", "gemm355_unit", "gemm355_num_tiles",
             "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_quantize",
-            "gemm355_status_string")
+            "gemm355_conv2d", "gemm355_conv2d_plan", "gemm355_status_string")
 
 
 class Gemm355Error(RuntimeError):
@@ -197,9 +214,9 @@ def gemm355_num_tiles() -> int:
 
 
 def gemm355_tile_info(tile: int) -> Dict[str, int]:
-    vals = [_i32() for _ in range(8)]
+    vals = [_i32() for _ in range(9)]
     _check(_lib.gemm355_tile_info(tile, *[ctypes.byref(v) for v in vals]), "gemm355_tile_info")
-    names = ("dtype_class", "T_M", "T_N", "T_K", "stages", "waves", "lds_bytes", "b_max")
+    names = ("dtype_class", "T_M", "T_N", "T_K", "stages", "waves", "lds_bytes", "b_max", "op")
     return dict(zip(names, (v.value for v in vals)))
 
 
@@ -207,6 +224,31 @@ def gemm355_tile_occupancy(tile: int) -> int:
     n = _i32()
     _check(_lib.gemm355_tile_occupancy(tile, ctypes.byref(n)), "gemm355_tile_occupancy")
     return n.value
+
+
+def conv_out_size(H, W, R, S, pad_h=0, pad_w=0, stride_h=1, stride_w=1, dil_h=1, dil_w=1):
+    """(P, Q) of a convolution, as the library computes them."""
+    return ((H + 2 * pad_h - dil_h * (R - 1) - 1) // stride_h + 1,
+            (W + 2 * pad_w - dil_w * (S - 1) - 1) // stride_w + 1)
+
+
+def make_conv_args(N, H, W, C, K, R, S, x=None, w=None, y=None, pad_h=0, pad_w=0, stride_h=1,
+                   stride_w=1, dil_h=1, dil_w=1, dtype=BF16_F32, split_k=0, persistent=-1, tile=-1,
+                   cus=0, workspace=None, workspace_bytes=0) -> gemm355_conv_args:
+    return gemm355_conv_args(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                             _ptr(x), _ptr(w), _ptr(y), dtype, split_k, persistent, tile, cus,
+                             _ptr(workspace), workspace_bytes)
+
+
+def gemm355_conv2d(args: gemm355_conv_args, stream=None) -> None:
+    _check(_lib.gemm355_conv2d(ctypes.byref(args), _stream(stream)), "gemm355_conv2d")
+
+
+def gemm355_conv2d_plan(args: gemm355_conv_args) -> Dict[str, int]:
+    out = gemm355_plan_t()
+    _check(_lib.gemm355_conv2d_plan(ctypes.byref(args) if args is not None else None, ctypes.byref(out)),
+           "gemm355_conv2d_plan")
+    return {name: getattr(out, name) for name, _ in gemm355_plan_t._fields_}
 
 
 def gemm355_quantize(x, n, batch, src, fmt, q, scale, stream=None) -> None:

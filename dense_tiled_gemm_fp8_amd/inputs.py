@@ -279,6 +279,15 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
     return Operands(M, N, K, fmt, A, B, sa, sb, (seed_a, seed_b), bsa, bsb)
 
 
+def conv_operands(N: int, H: int, W: int, C: int, K: int, R: int, S: int, dist: str, seed_x: int,
+                  seed_w: int) -> Tuple[np.ndarray, np.ndarray]:
+    """bf16 codes of NHWC images x and KRSC filters w ('normal_sqrtk' scales
+    by the R S C terms of each output)."""
+    x = draw(rng(seed_x), (N, H, W, C), dist, R * S * C)
+    w = draw(rng(seed_w), (K, R, S, C), dist, R * S * C)
+    return to_bf16_codes(x), to_bf16_codes(w)
+
+
 @dataclass(frozen=True)
 class Workload:
     """A named synthetic workload: shapes, element format, value recipe."""

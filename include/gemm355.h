@@ -268,12 +268,13 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
 /* Number of entries in the tile table, and one entry's parameters.
  * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2), 2 = block-scaled
  * 8-bit inputs (the MX 8-bit dtypes), 3 = block-scaled FP4 inputs; T_K counts
- * elements. */
+ * elements; b_max: resident workgroups per compute unit; op: 0 matrix
+ * product, 1 convolution (gemm355_conv2d).  Null outputs are skipped. */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
                                  int32_t *T_M, int32_t *T_N, int32_t *T_K,
                                  int32_t *stages, int32_t *waves,
-                                 int32_t *lds_bytes, int32_t *b_max);
+                                 int32_t *lds_bytes, int32_t *b_max, int32_t *op);
 
 /* Workgroups of a tile's main-loop kernel that fit on one compute unit of
  * the current device, as the HIP runtime reports it
@@ -308,6 +309,52 @@ GEMM355_API gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_
  */
 GEMM355_API gemm355_status gemm355_quantize(const void *x, int64_t n, int64_t batch, gemm355_src src,
                                 gemm355_fp8 fmt, void *q, float *scale, void *stream);
+
+/*
+ * Two-dimensional convolution as an implicit matrix product (page "The
+ * Tensor Core": convolutions reduce to GEMM; page "Grid 24 is not headroom"
+ * profiles a convolution kernel beside the GEMM).  Cross-correlation, as in
+ * deep-learning frameworks (the filter is not flipped):
+ *
+ *   y[n][p][q][k] = sum_{r, s, c} x[n][p*stride_h - pad_h + r*dil_h]
+ *                                   [q*stride_w - pad_w + s*dil_w][c] * w[k][r][s][c]
+ *
+ * with x read as zero outside its H x W extent.  Layouts (dense): x NHWC,
+ * w KRSC, y NPQK with P = (H + 2 pad_h - dil_h (R - 1) - 1) / stride_h + 1
+ * and Q likewise.  It is the product C = A B with M = N P Q output pixels,
+ * N = K output channels and K = R S C: row (n, p, q) of A gathers the R x S
+ * input pixels of the window, a column of B is one filter, C is y.  The
+ * main loop forms A's addresses from the window instead of reading an
+ * im2col copy.
+ *   dtype: GEMM355_BF16_F32 or GEMM355_BF16_BF16 (EUNSUPPORTED otherwise).
+ *   C must be a multiple of 64 (one K-tile is 64 channels of one filter
+ *   tap), x and w 16-byte aligned, and x below 2 GiB (EUNSUPPORTED
+ *   otherwise).
+ *   split_k, persistent, tile, cus, workspace: as in gemm355_args (tile
+ *   must name a convolution tile).
+ * y must not overlap x or w (EINVAL).  Sizes must be positive, strides and
+ * dilations >= 1, pads >= 0 and P, Q >= 1 (EINVAL).
+ */
+typedef struct gemm355_conv_args {
+    int64_t N, H, W, C;          /* input images, NHWC                       */
+    int64_t K, R, S;             /* filters, KRSC                            */
+    int64_t pad_h, pad_w;
+    int64_t stride_h, stride_w;
+    int64_t dil_h, dil_w;
+    const void *x;               /* device, N*H*W*C elements                  */
+    const void *w;               /* device, K*R*S*C elements                  */
+    void *y;                     /* device, N*P*Q*K elements of the output
+                                    type, written                            */
+    gemm355_dtype dtype;
+    int32_t split_k, persistent, tile, cus;
+    void *workspace;
+    size_t workspace_bytes;
+} gemm355_conv_args;
+
+GEMM355_API gemm355_status gemm355_conv2d(const gemm355_conv_args *args, void *stream);
+
+/* The plan of that product (P and Q follow from the arguments). */
+GEMM355_API gemm355_status gemm355_conv2d_plan(const gemm355_conv_args *args, gemm355_plan_t *out);
 
 /* Static description of a status code. */
 GEMM355_API const char *gemm355_status_string(gemm355_status status);

@@ -377,3 +377,48 @@ def test_struct_layout_matches_header(g, tmp_path):
         assert int(out[cname]) == ctypes.sizeof(cls), cname
         for name, _ in cls._fields_:
             assert int(out["%s.%s" % (cname, name)]) == getattr(cls, name).offset, (cname, name)
+
+
+def test_conv_plan_and_argument_errors(g):
+    """The convolution's implicit product: M = N P Q, N = K, K = R S C with
+    the library's output size; argument checks before any device work."""
+    X, W, Y = 0x10000, 0x1000000000, 0x200000000000
+
+    def args(**kw):
+        a = dict(N=4, H=30, W=30, C=64, K=96, R=3, S=3, x=X, w=W, y=Y, pad_h=1, pad_w=1, cus=256)
+        a.update(kw)
+        return g.make_conv_args(**a)
+
+    p = g.gemm355_conv2d_plan(args())
+    assert (p["T_M"], p["T_N"], p["T_K"]) != (0, 0, 0)
+    P, Q = g.conv_out_size(30, 30, 3, 3, 1, 1)
+    assert (P, Q) == (30, 30)
+    assert p["G"] == bk.tile_grid(4 * P * Q, 96, p["T_M"], p["T_N"])
+    assert p["nK"] == bk.ceil_div(9 * 64, p["T_K"])
+    assert g.gemm355_tile_info(p["tile"])["op"] == 1
+    p2 = g.gemm355_conv2d_plan(args(stride_h=2, stride_w=3, dil_h=2, pad_h=0, pad_w=0))
+    P2, Q2 = g.conv_out_size(30, 30, 3, 3, 0, 0, 2, 3, 2, 1)
+    assert p2["G"] == bk.tile_grid(4 * P2 * Q2, 96, p2["T_M"], p2["T_N"])
+
+    def status(**kw):
+        try:
+            g.gemm355_conv2d(args(**kw), stream=0)
+            return g.OK
+        except g.Gemm355Error as e:
+            return e.status
+
+    assert status(C=3) == g.EUNSUPPORTED                    # 64-channel K-tiles
+    assert status(H=2, pad_h=0) == g.EINVAL                 # P < 1
+    assert status(stride_h=0) == g.EINVAL
+    assert status(dil_w=0) == g.EINVAL
+    assert status(pad_w=-1) == g.EINVAL
+    assert status(N=0) == g.EINVAL
+    assert status(dtype=g.E4M3_F32) == g.EUNSUPPORTED
+    assert status(dtype=99) == g.EINVAL
+    assert status(x=None) == g.EINVAL
+    assert status(y=X + 64) == g.EINVAL                     # output overlaps the images
+    assert status(x=X + 8) == g.EUNSUPPORTED                 # pixels not 16-byte aligned
+    assert status(tile=0) == g.EINVAL                       # a matrix-product tile
+    assert status(N=1 << 12, H=1 << 10, W=1 << 10) == g.EUNSUPPORTED   # images beyond 2 GiB
+    with pytest.raises(g.Gemm355Error):
+        g.gemm355_conv2d_plan(None)
