@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2, "fp4": 10066.3}   # MI355X dense MFMA, 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2, "fp4": 10066.3}   # MI355X dense MFMA, 2.4 GHz (fp6 as fp4)
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 KERNEL_SOURCES = ["dense_tiled_gemm_fp8_amd/csrc/kernels.hip", "dense_tiled_gemm_fp8_amd/csrc/sched.h",
@@ -339,13 +339,15 @@ def fp8_end_to_end(torch, g, inputs, args):
 
 def mx_products(torch, g, inputs, args):
     """8192^3 block-scaled products (E8M0 scale per 32 K-values of each row
-    of A and column of B), E4M3, E5M2 and FP4 (E2M1) elements, fp32 C, timed
+    of A and column of B), E4M3, E5M2, FP6 (E2M3, E3M2) and FP4 (E2M1)
+    elements, fp32 C, timed
     like the per-tensor E4M3 product beside them (same shape, same box)."""
     import numpy as np
     M = N = K = 8192
     flops = 2.0 * M * N * K
     out = []
-    for fmt, dt in (("mxe4m3", g.MXE4M3_F32), ("mxe5m2", g.MXE5M2_F32), ("mxfp4", g.MXFP4_F32)):
+    for fmt, dt in (("mxe4m3", g.MXE4M3_F32), ("mxe5m2", g.MXE5M2_F32), ("mxfp6e2m3", g.MXFP6_E2M3_F32),
+                    ("mxfp6e3m2", g.MXFP6_E3M2_F32), ("mxfp4", g.MXFP4_F32)):
         log("bench: detail block-scaled", fmt, (M, N, K))
         ops = inputs.make_operands(M, N, K, fmt, "normal", inputs.seed_for(6, 0, 0), inputs.seed_for(6, 0, 1))
         A = torch.from_numpy(ops.A).cuda()
@@ -370,7 +372,7 @@ def mx_products(torch, g, inputs, args):
                         "quantised per block, fp32 C)" % fmt,
             "dtype": fmt, "out": "f32", "us_median": round(med * 1e6, 2), "us_min": round(reps[0] * 1e6, 2),
             "tflops": round(flops / med / 1e12, 1),
-            "pct_mfma_peak": round(100 * flops / med / 1e12 / PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "e4m3"], 1),
+            "pct_mfma_peak": round(100 * flops / med / 1e12 / PEAK_TFLOPS["e4m3" if fmt in ("mxe4m3", "mxe5m2") else "fp4"], 1),
             "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"], "grid": p["grid"],
         })
         del A, B, sa, sb, C

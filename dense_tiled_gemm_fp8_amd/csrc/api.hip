@@ -295,7 +295,8 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
     gp.s = P.s;
     /* operand-format pair of an 8-bit product: 0 E4M3 x E4M3, 1 E5M2 x E5M2,
      * 2 E4M3 x E5M2 */
-    const int32_t fmt = !dtype_fp8(a.dtype) ? 0 : dtype_fmt_a(a.dtype) ? 1 : dtype_fmt_b(a.dtype) ? 2 : 0;
+    const int32_t fmt = !(dtype_fp8(a.dtype) || dtype_fp6(a.dtype)) ? 0
+                        : dtype_fmt_a(a.dtype) ? 1 : dtype_fmt_b(a.dtype) ? 2 : 0;
     if (P.s.grid > 0 && launch_gemm(P.pub.tile, fmt, gp, hs) != hipSuccess) return GEMM355_EHIP;
 
     if (P.reduce_tiles > 0) {
@@ -334,7 +335,7 @@ gemm355_status conv_setup(const gemm355_conv_args *c, gemm355_args &a, ConvShape
     const int64_t ph = c->H + 2 * c->pad_h - c->dil_h * (c->R - 1) - 1;
     const int64_t pw = c->W + 2 * c->pad_w - c->dil_w * (c->S - 1) - 1;
     if (ph < 0 || pw < 0) return GEMM355_EINVAL;
-    if ((int)c->dtype < 0 || (int)c->dtype > 15) return GEMM355_EINVAL;
+    if ((int)c->dtype < 0 || (int)c->dtype >= kNumDtypes) return GEMM355_EINVAL;
     if (c->dtype != GEMM355_BF16_F32 && c->dtype != GEMM355_BF16_BF16) return GEMM355_EUNSUPPORTED;
     cs.N = c->N;
     cs.H = c->H;

@@ -178,14 +178,17 @@ template <int TM, int TN, int EL, int MINB, int RB, int STAGES, int WGM, int WGN
 __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) void gemm_tile_kernel(GemmParams p)
 {
     /* element class: 0 bf16, 1 8-bit, 2 8-bit with E8M0 block scales, 3 FP4
-     * (E2M1, two per byte) with E8M0 block scales.  FP8 marks the f8f6f4
-     * matrix instructions (classes 1-3). */
-    constexpr bool FP8 = EL != 0, MX = EL >= 2, FP4 = EL == 3;
+     * (E2M1, two per byte) with E8M0 block scales, 4 FP6 (E2M3 or E3M2, four
+     * per three bytes) with E8M0 block scales.  FP8 marks the f8f6f4 matrix
+     * instructions (classes 1-4). */
+    constexpr bool FP8 = EL != 0, MX = EL >= 2, FP4 = EL == 3, FP6 = EL == 4;
     /* OP 1: convolution, A gathered from NHWC images (kernels.h) */
     constexpr bool CONV = OP == 1;
-    /* operand formats (instruction format codes: 0 E4M3, 1 E5M2, 4 E2M1):
-     * FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2 (A x B); FP4 both 4 */
-    constexpr int FA = FP4 ? 4 : FMT == 1 ? 1 : 0, FB = FP4 ? 4 : FMT >= 1 ? 1 : 0;
+    /* operand formats (instruction format codes: 0 E4M3, 1 E5M2, 2 E2M3,
+     * 3 E3M2, 4 E2M1): FMT 0 E4M3 x E4M3, 1 E5M2 x E5M2, 2 E4M3 x E5M2
+     * (A x B), and for FP6 E2M3 / E3M2 in the same places; FP4 both 4 */
+    constexpr int FA = FP4 ? 4 : (FP6 ? 2 : 0) + (FMT == 1 ? 1 : 0);
+    constexpr int FB = FP4 ? 4 : (FP6 ? 2 : 0) + (FMT >= 1 ? 1 : 0);
     constexpr int NW = WGM * WGN, WN = WGN;
     /* SPREAD 3 (warp specialisation): four more wavefronts, one per SIMD,
      * issue every copy and run no MFMA; the NW MFMA wavefronts only read LDS.
@@ -201,7 +204,12 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
      * rows as SW planes of TM + TN dwords (plane w: A's rows, then B's),
      * copied 64 rows per direct-to-LDS dword load, SC loads per wavefront. */
     constexpr int VPB = FP4 ? 2 : 1;
-    constexpr int SW = MX ? RB * VPB / 128 : 0;
+    /* values per row per K-tile, and the bytes they take in global memory
+     * (FP6: 128 values in 96 bytes, staged in 128-byte LDS rows whose last
+     * 32 bytes are not read) */
+    constexpr int VPT = FP6 ? 128 : RB * VPB;
+    constexpr int KTB = FP6 ? 96 : RB;
+    constexpr int SW = MX ? VPT / 128 : 0;
     constexpr int SCA_OFF = A_BYTES + B_BYTES, SCB_OFF = SCA_OFF + TM * 4, SPLANE = (TM + TN) * 4;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SW * SPLANE;
     constexpr int SC = SW * (TM + TN) / 64 / NW;
@@ -209,7 +217,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     constexpr int LOADS = A_LOADS + B_LOADS + SC;
     /* bytes of K per MFMA step: 32 x 32 blocks take 16 bf16, 64 E4M3 or 64
      * FP4 values, 16 x 16 blocks twice that; CPS 16-byte chunks */
-    constexpr int KB_STEP = (FP8 && !FP4 ? 64 : 32) * (MI == 32 ? 1 : 2);
+    constexpr int KB_STEP = FP6 ? 64 : (FP8 && !FP4 ? 64 : 32) * (MI == 32 ? 1 : 2);
     constexpr int CPS = KB_STEP / 16;
     constexpr int KSTEPS = RB / KB_STEP;
     constexpr int ACC_N = MI * MI / 64;
@@ -225,6 +233,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     static_assert(SPREAD != 2 || (KSTEPS == 4 && STAGES == 2 && LOADS % 2 == 0), "two-step prefetch schedule");
     static_assert(SPREAD != 3 || STAGES >= 3, "producer wavefronts run two K-tiles ahead");
     static_assert(!CONV || (!FP8 && SPREAD == 0 && RB == 128), "convolution: bf16, 64-channel K-tiles copied in one step");
+    static_assert(!FP6 || (RB == 128 && MI == 32), "FP6: 128-value K-tiles in 128-byte rows, 32 x 32 blocks");
     static_assert(A_LOADS * CW * ROWS_PER_DMA == TM && B_LOADS * CW * ROWS_PER_DMA == TN, "whole copies");
     static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == SW * (TM + TN)),
                   "block scales: whole dwords per row and K-tile, whole 64-row copies per wavefront");
@@ -336,16 +345,19 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         /* per parity class of the copy index (one class unless TWO) */
         struct KV {
             bool v[2];
+            bool tile;   /* the K-tile is in the unit's range (block scales:
+                            whole dwords, whatever the lane's chunk) */
         };
         /* iteration i of the unit's loop works on K-tile kt_begin + i */
         const int32_t nkt = un.kt_end - un.kt_begin;
         auto ktile = [&](int32_t i) __attribute__((always_inline)) { return un.kt_begin + i; };
         /* copies of iteration i; iterations past the range read zero */
         auto kvalid = [&](int32_t i) __attribute__((always_inline)) {
-            const uint32_t kb = (uint32_t)ktile(i) * RB;
+            const uint32_t kb = (uint32_t)ktile(i) * KTB;
             KV k;
             k.v[0] = ((int32_t)(kb + lchunk[0] * 16) < p.Kb) && (i < nkt);
             k.v[1] = TWO ? ((int32_t)(kb + lchunk[1] * 16) < p.Kb) && (i < nkt) : k.v[0];
+            k.tile = ((int32_t)kb < p.Kb) && (i < nkt);
             return k;
         };
         /* convolution: filter tap and channel block of the next K-tile to
@@ -393,14 +405,14 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             } else if constexpr (d < A_LOADS + B_LOADS) {
                 dma16<A_BYTES + (d - A_LOADS) * CW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
             } else {
-                /* K-tile kb / RB of the regrouped scales */
+                /* K-tile kb / KTB of the regrouped scales */
                 constexpr int q = d - A_LOADS - B_LOADS;
-                dma4(srs[q], smem_base + so + sdst[q], kv.v[0] ? soff[q] + (kb / RB) * stp[q] : kOOB);
+                dma4(srs[q], smem_base + so + sdst[q], kv.tile ? soff[q] + (kb / KTB) * stp[q] : kOOB);
             }
         };
         auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
             const KV kv = kvalid(i);
-            const uint32_t kb = (uint32_t)ktile(i) * RB;
+            const uint32_t kb = (uint32_t)ktile(i) * KTB;
             next_tap();
             unroll<LOADS>([&](auto dc) __attribute__((always_inline)) { dma(dc, so, kb, kv); });
         };
@@ -411,6 +423,20 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             const uint8_t *row = rows + (blk * MI + frow) * RB;
             if constexpr (!FP8) {
                 return *(const bf16x8 *)(row + (((CPS * ks + hi) ^ sw) * 16));
+            } else if constexpr (FP6) {
+                /* 32 values (one block, 24 bytes) per lane group: bytes
+                 * 48 ks + 24 hi .. + 23 of the row, three 8-byte reads, each
+                 * inside one 16-byte chunk */
+                const int o = 48 * ks + 24 * hi;
+                uint32_t d[6];
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const int b = o + 8 * j;
+                    const uint2 v = *(const uint2 *)(row + (((b >> 4) ^ sw) << 4) + (b & 15));
+                    d[2 * j] = v.x;
+                    d[2 * j + 1] = v.y;
+                }
+                return i32x8{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], 0, 0};
             } else if constexpr (FP4) {
                 /* 32 values (one block) per lane in the low four dwords */
                 const i32x4 v = *(const i32x4 *)(row + (((CPS * ks + hi) ^ sw) * 16));
@@ -518,7 +544,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
                     else if constexpr (MX) {
                         /* the step's first block: its plane and byte */
-                        constexpr int B0 = KS * (KB_STEP * VPB / 32), DW = B0 / 4, SH = 8 * (B0 % 4);
+                        constexpr int B0 = KS * (FP6 ? 2 : KB_STEP * VPB / 32), DW = B0 / 4, SH = 8 * (B0 % 4);
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, (int)(csa[DW][i] >> SH), 0,
                             (int)(csb[DW][j] >> SH));
@@ -581,7 +607,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * K-tile kt+2 into this stage over steps 2 and 3. */
         auto tile2 = [&](uint32_t so, uint32_t nso, int32_t kt) __attribute__((always_inline)) {
             const uint8_t *cs = smem + so;
-            const KV kv0{{false, false}};
+            const KV kv0{{false, false}, false};
             step(IC<0>{}, IC<0>{}, IC<0>{}, cs, 2, so, 0u, kv0, IC<0>{});
             step(IC<1>{}, IC<0>{}, IC<0>{}, cs, 3, so, 0u, kv0, IC<1>{});
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -590,7 +616,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             const KV kv = kvalid(kt + 2);
-            const uint32_t kb = (uint32_t)ktile(kt + 2) * RB;
+            const uint32_t kb = (uint32_t)ktile(kt + 2) * KTB;
             step(IC<2>{}, IC<0>{}, IC<LOADS / 2>{}, smem + nso, 0, so, kb, kv, IC<2>{});
             step(IC<3>{}, IC<LOADS / 2>{}, IC<LOADS / 2>{}, smem + nso, 1, so, kb, kv, IC<3>{});
         };
@@ -601,12 +627,12 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             constexpr bool SP1 = SPREAD == 1;
             constexpr int LPRE = SP1 ? (KSTEPS - 1) * LOADS / KSTEPS : 0;
             const uint8_t *cs = smem + so;
-            KV kv{{false, false}};
+            KV kv{{false, false}, false};
             uint32_t kb = 0;
             take_scales();
             if constexpr (SP1) {
                 kv = kvalid(kt + STAGES - 1);
-                kb = (uint32_t)ktile(kt + STAGES - 1) * RB;
+                kb = (uint32_t)ktile(kt + STAGES - 1) * KTB;
             }
             unroll<KSTEPS - 1>([&](auto kc) __attribute__((always_inline)) {
                 constexpr int ks = decltype(kc)::value;
@@ -628,7 +654,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<0>{}, smem + nso, 0, so, 0u, kv, IC<KSTEPS - 1>{});
             } else {
                 kv = kvalid(kt + STAGES);
-                kb = (uint32_t)ktile(kt + STAGES) * RB;
+                kb = (uint32_t)ktile(kt + STAGES) * KTB;
                 next_tap();
                 step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, 0, so, kb, kv, IC<KSTEPS - 1>{});
             }
@@ -1089,7 +1115,7 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
 
 /* Instantiations, in tile-table order (csrc/tiles.h):
  * id, TM, TN, element class (false bf16, true 8-bit, 2 block-scaled 8-bit,
- * 3 block-scaled FP4),
+ * 3 block-scaled FP4, 4 block-scaled FP6),
  * groups per CU, K-tile bytes, stages, waves along M, N, copy schedule,
  * MFMA block edge, operation (0 matrix product, 1 convolution) */
 #define GEMM355_TILES(X)                                                                          \
@@ -1151,7 +1177,10 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(55, 128, 128, false, 2, 128, 2, 2, 2, 0, 32, 1)                                               \
     X(56, 64, 64, false, 4, 128, 2, 2, 2, 0, 32, 1)                                                 \
     X(57, 256, 256, false, 1, 128, 2, 2, 4, 0, 16, 1)                                               \
-    X(58, 128, 128, false, 1, 128, 4, 2, 2, 0, 32, 1)
+    X(58, 128, 128, false, 1, 128, 4, 2, 2, 0, 32, 1)                                               \
+    X(59, 256, 256, 4, 1, 128, 2, 2, 2, 0, 32, 0)                                                   \
+    X(60, 128, 128, 4, 2, 128, 2, 2, 2, 0, 32, 0)                                                   \
+    X(61, 128, 128, 4, 1, 128, 4, 2, 2, 0, 32, 0)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn)                                                      \

@@ -33,34 +33,42 @@ struct Plan {
 };
 
 /* Element-type queries.  Dtypes come in pairs (fp32 C, bf16 C). */
-constexpr int kNumDtypes = 16;
+constexpr int kNumDtypes = 20;
 /* 8-bit inputs, with or without block scales */
 inline bool dtype_fp8(gemm355_dtype d) { return d >= GEMM355_E4M3_F32 && d <= GEMM355_MXE4M3_E5M2_BF16; }
 /* block-scaled 4-bit (E2M1) inputs */
 inline bool dtype_fp4(gemm355_dtype d) { return d == GEMM355_MXFP4_F32 || d == GEMM355_MXFP4_BF16; }
-/* block-scaled inputs (8- or 4-bit) */
+/* block-scaled 6-bit (E2M3 or E3M2) inputs */
+inline bool dtype_fp6(gemm355_dtype d) { return d >= GEMM355_MXFP6_E2M3_F32 && d <= GEMM355_MXFP6_E3M2_BF16; }
+/* block-scaled inputs (8-, 6- or 4-bit) */
 inline bool dtype_mx(gemm355_dtype d)
 {
-    return (d >= GEMM355_MXE4M3_F32 && d <= GEMM355_MXE4M3_E5M2_BF16) || dtype_fp4(d);
+    return (d >= GEMM355_MXE4M3_F32 && d <= GEMM355_MXE4M3_E5M2_BF16) || dtype_fp4(d) || dtype_fp6(d);
 }
 /* bits per input element */
-inline int32_t dtype_ebits(gemm355_dtype d) { return dtype_fp4(d) ? 4 : dtype_fp8(d) ? 8 : 16; }
+inline int32_t dtype_ebits(gemm355_dtype d)
+{
+    return dtype_fp4(d) ? 4 : dtype_fp6(d) ? 6 : dtype_fp8(d) ? 8 : 16;
+}
 inline bool dtype_out_bf16(gemm355_dtype d) { return ((int)d & 1) != 0; }
-/* tile-table class: 0 bf16, 1 8-bit, 2 block-scaled 8-bit, 3 block-scaled FP4 */
+/* tile-table class: 0 bf16, 1 8-bit, 2 block-scaled 8-bit, 3 block-scaled
+ * FP4, 4 block-scaled FP6 */
 inline int32_t dtype_class_of(gemm355_dtype d)
 {
-    return dtype_fp4(d) ? 3 : dtype_mx(d) ? 2 : dtype_fp8(d) ? 1 : 0;
+    return dtype_fp6(d) ? 4 : dtype_fp4(d) ? 3 : dtype_mx(d) ? 2 : dtype_fp8(d) ? 1 : 0;
 }
-/* 8-bit format codes of the MFMA operands: 0 E4M3, 1 E5M2 */
+/* format codes of the MFMA operands relative to the element class: 0 E4M3
+ * (FP6: E2M3), 1 E5M2 (FP6: E3M2) */
 inline int32_t dtype_fmt_a(gemm355_dtype d)
 {
     return (d == GEMM355_E5M2_F32 || d == GEMM355_E5M2_BF16 || d == GEMM355_MXE5M2_F32 ||
-            d == GEMM355_MXE5M2_BF16) ? 1 : 0;
+            d == GEMM355_MXE5M2_BF16 || d == GEMM355_MXFP6_E3M2_F32 || d == GEMM355_MXFP6_E3M2_BF16) ? 1 : 0;
 }
 inline int32_t dtype_fmt_b(gemm355_dtype d)
 {
     return ((d >= GEMM355_E5M2_F32 && d <= GEMM355_E4M3_E5M2_BF16) ||
-            (d >= GEMM355_MXE5M2_F32 && d <= GEMM355_MXE4M3_E5M2_BF16)) ? 1 : 0;
+            (d >= GEMM355_MXE5M2_F32 && d <= GEMM355_MXE4M3_E5M2_BF16) || d == GEMM355_MXFP6_E3M2_F32 ||
+            d == GEMM355_MXFP6_E3M2_BF16) ? 1 : 0;
 }
 
 /* A convolution planned as its implicit product (conv != null below): the

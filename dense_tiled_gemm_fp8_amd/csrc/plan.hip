@@ -160,7 +160,7 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
      * workgroups.  Memory side: algorithmic bytes plus split-K partial
      * traffic (written, then read), at a sustained HBM rate scaled by how
      * evenly the work is spread over the compute units. */
-    const double cu_peak = cfg.dtype_class == 3 ? kPeakFp4PerCu : cfg.dtype_class ? kPeakFp8PerCu : kPeakBf16PerCu;
+    const double cu_peak = cfg.dtype_class >= 3 ? kPeakFp4PerCu : cfg.dtype_class ? kPeakFp8PerCu : kPeakBf16PerCu;
     /* workgroups actually sharing a compute unit */
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(c.b, cdiv(std::max<int64_t>(c.grid, 1), S)));
     const double eff = cfg.mfma_eff[std::min<int64_t>(per_cu, 4) - 1];
@@ -331,10 +331,10 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
     if (S < 1) return GEMM355_EINVAL;
     if (a.stride_a < 0 || a.stride_b < 0 || a.stride_c < 0) return GEMM355_EINVAL;
 
-    const bool fp8 = dtype_fp8(a.dtype), fp4 = dtype_fp4(a.dtype);
+    const bool fp8 = dtype_fp8(a.dtype), fp4 = dtype_fp4(a.dtype), fp6 = dtype_fp6(a.dtype);
     const int32_t dclass = dtype_class_of(a.dtype);
     const int32_t ebits = dtype_ebits(a.dtype);
-    const int32_t esize = fp8 || fp4 ? 1 : 2;    /* bytes per element of the repack passes */
+    const int32_t esize = fp8 || fp4 || fp6 ? 1 : 2;    /* bytes per element of the repack passes */
     const int32_t out_esize = dtype_out_bf16(a.dtype) ? 2 : 4;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
@@ -353,6 +353,11 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
      * K-tiles of 256 values (two scale dwords per row) */
     if (fp4 && (a.layout != GEMM355_A_ROW_B_COL || K % 256 != 0 || a.lda % 2 || a.ldb % 2 ||
                 (batch > 1 && (a.stride_a % 2 || a.stride_b % 2))))
+        return GEMM355_EUNSUPPORTED;
+    /* FP6: native layout, rows and batch entries of whole 16-byte groups
+     * (64 values), whole K-tiles of 128 values */
+    if (fp6 && (a.layout != GEMM355_A_ROW_B_COL || K % 128 != 0 || a.lda % 64 || a.ldb % 64 ||
+                (batch > 1 && (a.stride_a % 64 || a.stride_b % 64))))
         return GEMM355_EUNSUPPORTED;
     /* the regrouped scales of one batch entry are addressed with 32-bit
      * offsets */
@@ -380,7 +385,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
     P.pack_b = !b_col || misaligned16(a.B) || bytes_of(a.ldb) % 16 || kbytes % 16 ||
                (batch > 1 && bytes_of(a.stride_b) % 16);
     /* the repack passes move whole bytes per element */
-    if (fp4 && (P.pack_a || P.pack_b)) return GEMM355_EUNSUPPORTED;
+    if ((fp4 || fp6) && (P.pack_a || P.pack_b)) return GEMM355_EUNSUPPORTED;
     if (conv) {
         /* the main loop gathers A from the images itself: 64-channel K-tiles
          * of 16-byte aligned pixels; B (the filters) must be native */

@@ -22,9 +22,11 @@ namespace g355 {
 struct TileCfg {
     int32_t dtype_class;   /* 0 bf16 inputs, 1 8-bit inputs, 2 8-bit inputs
                               with E8M0 block scales (MX), 3 FP4 inputs
-                              with E8M0 block scales                        */
+                              with E8M0 block scales, 4 FP6 inputs with
+                              E8M0 block scales                             */
     int32_t TM, TN, TK;    /* TK in elements                                 */
-    int32_t row_bytes;     /* RB: K bytes per tile row per stage             */
+    int32_t row_bytes;     /* RB: LDS bytes per tile row per stage (FP6 uses
+                              96 of 128)                                    */
     int32_t stages;
     int32_t waves_m, waves_n;
     int32_t spread;        /* copy schedule: 0 copies of a K-tile in the last
@@ -143,6 +145,11 @@ constexpr TileCfg kTiles[] = {
     {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.15f, 0.25f, 0.28f, 0.30f}, 0.70f, 1},
     {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f, 1},
     {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.95f, 1},
+    /* block-scaled FP6: K-tiles of 128 values (96 bytes) staged in 128-byte
+     * rows, one scale dword per row and stage */
+    {4, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 132, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
+    {4, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 132, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
+    {4, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 132, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

@@ -26,7 +26,8 @@ OK, EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP = range(6)
 # dtypes (input -> output)
 (BF16_F32, BF16_BF16, E4M3_F32, E4M3_BF16, E5M2_F32, E5M2_BF16, E4M3_E5M2_F32,
  E4M3_E5M2_BF16, MXE4M3_F32, MXE4M3_BF16, MXE5M2_F32, MXE5M2_BF16, MXE4M3_E5M2_F32,
- MXE4M3_E5M2_BF16, MXFP4_F32, MXFP4_BF16) = range(16)
+ MXE4M3_E5M2_BF16, MXFP4_F32, MXFP4_BF16, MXFP6_E2M3_F32, MXFP6_E2M3_BF16, MXFP6_E3M2_F32,
+ MXFP6_E3M2_BF16) = range(20)
 # 8-bit formats and source types of the quantiser
 FP8_E4M3, FP8_E5M2 = range(2)
 SRC_F32, SRC_BF16 = range(2)

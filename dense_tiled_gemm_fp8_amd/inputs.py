@@ -78,7 +78,7 @@ def to_e4m3_codes(x: np.ndarray, scale: Optional[float] = None) -> Tuple[np.ndar
     return to_fp8_codes(x, "e4m3", scale)
 
 
-FP8_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}     # exponent of the largest finite value
+FP8_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2, "e2m3": 2, "e3m2": 4}   # exponent of the largest finite value
 E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # codes 0..7 (OCP FP4)
 
 
@@ -94,6 +94,57 @@ def to_e2m1_codes(y: np.ndarray) -> np.ndarray:
                  np.where(mag < 4.0, np.rint(mag), np.minimum(2.0 * np.rint(mag / 2.0), 6.0)))
     code = np.searchsorted(E2M1_VALUES, q).astype(np.uint8)
     return code | (np.signbit(y).astype(np.uint8) << 3)
+
+
+def _fp6_grid(fmt: str) -> np.ndarray:
+    """Non-negative values of the 6-bit format, indexed by code 0..31."""
+    eb, mb, bias = (2, 3, 1) if fmt == "e2m3" else (3, 2, 3)
+    vals = []
+    for code in range(32):
+        e, m = code >> mb, code & ((1 << mb) - 1)
+        vals.append(m / 2.0 ** mb * 2.0 ** (1 - bias) if e == 0 else (1 + m / 2.0 ** mb) * 2.0 ** (e - bias))
+    return np.array(vals)
+
+
+def to_fp6_codes(y: np.ndarray, fmt: str) -> np.ndarray:
+    """Round to the nearest E2M3 / E3M2 value, ties to the even code,
+    saturating at the largest; 6-bit codes (sign in bit 5) as uint8."""
+    grid = _fp6_grid(fmt)
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.minimum(np.abs(y), grid[-1])
+    hi = np.clip(np.searchsorted(grid, mag, side="left"), 1, 31)
+    lo = hi - 1
+    dlo, dhi = mag - grid[lo], grid[hi] - mag
+    pick = np.where(dhi == dlo, (hi & 1) == 0, dhi < dlo)
+    code = np.where(pick, hi, lo).astype(np.uint8)
+    return code | (np.signbit(y).astype(np.uint8) << 5)
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """rows x K 6-bit codes -> rows x 3K/4 bytes, a little-endian bit
+    stream (element i in bits 6i .. 6i+5)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    rows, K = c.shape
+    bits = ((c[:, :, None] >> np.arange(6)) & 1).astype(np.uint8).reshape(rows, K * 6)
+    return np.packbits(bits, axis=1, bitorder="little")
+
+
+def to_mx_fp6_codes(x: np.ndarray, fmt: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Block-scaled FP6 quantisation (OCP MX v1.0 conversion, as
+    to_mx_codes with emax 2 for E2M3 and 4 for E3M2): (rows x 3K/4 packed
+    bytes, rows x K/32 scale codes)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    rows, K = x64.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x64.reshape(rows, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    _, e = np.frexp(amax)
+    code = np.where(amax > 0, e - 1 - FP8_EMAX[fmt] + 127, 127)
+    code = np.clip(code, 0, 254).astype(np.uint8)
+    scale = np.ldexp(1.0, code.astype(np.int64) - 127)
+    q = to_fp6_codes((blocks / scale[:, :, None]).reshape(rows, K), fmt)
+    return pack_fp6(q), code
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
@@ -158,6 +209,9 @@ def small_int_codes(gen: np.random.Generator, shape, fmt: str, lo: int = -4,
         # integers of E2M1: 0, 1, 2, 3, 4, 6 (packed two per byte)
         v = np.where(np.abs(v) == 5, np.sign(v) * 4, v)
         return pack_nibbles(to_e2m1_codes(v))
+    if fmt in ("e2m3", "e3m2"):
+        # every integer up to 7 is an E2M3 value and up to 8 an E3M2 value
+        return pack_fp6(to_fp6_codes(v, fmt))
     q, _ = to_fp8_codes(v, "e5m2" if fmt == "e5m2" else "e4m3", scale=1.0)
     return q
 
@@ -186,8 +240,9 @@ class Operands:
     N: int
     K: int
     fmt: str                      # "bf16", "e4m3", "e5m2" or "e4m3e5m2" (A E4M3, B E5M2);
-                                  # "mx" + one of the 8-bit names, or "mxfp4":
-                                  # block-scaled (FP4 A and B hold K/2 bytes a row)
+                                  # "mx" + one of the 8-bit names, "mxfp4",
+                                  # "mxfp6e2m3" or "mxfp6e3m2": block-scaled
+                                  # (FP4 rows hold K/2 bytes, FP6 rows 3K/4)
     A: np.ndarray                 # (batch, M, K) or (M, K)
     B: np.ndarray                 # (batch, N, K) or (N, K)  (column-major B)
     scale_a: List[float] = field(default_factory=list)
@@ -212,12 +267,16 @@ class Operands:
 
     @property
     def fmt_a(self) -> str:
+        if self.elem.startswith("fp6"):
+            return self.elem[3:]
         if self.elem == "fp4":
             return "e2m1"
         return "e4m3" if self.elem == "e4m3e5m2" else self.elem
 
     @property
     def fmt_b(self) -> str:
+        if self.elem.startswith("fp6"):
+            return self.elem[3:]
         if self.elem == "fp4":
             return "e2m1"
         return "e5m2" if self.elem == "e4m3e5m2" else self.elem
@@ -239,6 +298,16 @@ def make_operands(M: int, N: int, K: int, fmt: str, dist: str, seed_a: int,
             Bs.append(to_bf16_codes(xb))
             sa.append(1.0)
             sb.append(1.0)
+        elif fmt in ("mxfp6e2m3", "mxfp6e3m2"):
+            f6 = fmt[5:]
+            qa, ca = to_mx_fp6_codes(xa, f6)
+            qb, cb = to_mx_fp6_codes(xb, f6)
+            As.append(qa)
+            Bs.append(qb)
+            sa.append(1.0)
+            sb.append(1.0)
+            bsa_l.append(ca)
+            bsb_l.append(cb)
         elif fmt == "mxfp4":
             qa, ca = to_mx_fp4_codes(xa)
             qb, cb = to_mx_fp4_codes(xb)

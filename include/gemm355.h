@@ -45,7 +45,7 @@ typedef enum gemm355_status {
     GEMM355_EUNSUPPORTED = 3,  /* extents beyond the 32-bit offsets the
                                   kernels use, an unknown tile id, an MX
                                   dtype with K not a multiple of 128, or an
-                                  MX FP4 call outside its limits */
+                                  MX FP4 / FP6 call outside its limits */
     GEMM355_ENOMEM = 4,        /* caller workspace smaller than the plan's
                                   workspace_bytes, or allocation failed */
     GEMM355_EHIP = 5           /* a HIP runtime call failed (no device,
@@ -84,7 +84,18 @@ typedef enum gemm355_dtype {
      * B column-major), lda, ldb and strides even, rows 16-byte aligned,
      * K a multiple of 256 (EUNSUPPORTED otherwise). */
     GEMM355_MXFP4_F32 = 14,        /* MX FP4 A, B; fp32 C                     */
-    GEMM355_MXFP4_BF16 = 15        /* MX FP4 A, B; bf16 C                     */
+    GEMM355_MXFP4_BF16 = 15,       /* MX FP4 A, B; bf16 C                     */
+    /* MX FP6: OCP E2M3 (1 sign, 2 exponent bits with bias 1, 3 mantissa
+     * bits; largest 7.5) or E3M2 (3 exponent bits with bias 3, 2 mantissa
+     * bits; largest 28) elements, no infinities or NaN, packed four per
+     * three bytes as a little-endian bit stream (element i in bits
+     * 6i .. 6i+5 of its row).  Native layout only, lda, ldb and strides
+     * multiples of 64, rows 16-byte aligned, K a multiple of 128
+     * (EUNSUPPORTED otherwise). */
+    GEMM355_MXFP6_E2M3_F32 = 16,   /* MX E2M3 A, B; fp32 C                    */
+    GEMM355_MXFP6_E2M3_BF16 = 17,  /* MX E2M3 A, B; bf16 C                    */
+    GEMM355_MXFP6_E3M2_F32 = 18,   /* MX E3M2 A, B; fp32 C                    */
+    GEMM355_MXFP6_E3M2_BF16 = 19   /* MX E3M2 A, B; bf16 C                    */
 } gemm355_dtype;
 
 /* 8-bit formats of the quantiser. */
@@ -267,7 +278,8 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
 
 /* Number of entries in the tile table, and one entry's parameters.
  * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2), 2 = block-scaled
- * 8-bit inputs (the MX 8-bit dtypes), 3 = block-scaled FP4 inputs; T_K counts
+ * 8-bit inputs (the MX 8-bit dtypes), 3 = block-scaled FP4 inputs, 4 =
+ * block-scaled FP6 inputs; T_K counts
  * elements; b_max: resident workgroups per compute unit; op: 0 matrix
  * product, 1 convolution (gemm355_conv2d).  Null outputs are skipped. */
 GEMM355_API int32_t gemm355_num_tiles(void);

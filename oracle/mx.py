@@ -14,7 +14,10 @@ version 1.0:
 * the elements are E4M3 or E5M2 codes, decoded as in ``gemm_oracle.c``, or
   FP4 E2M1 codes (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
   exponent field 0 is subnormal, m * 0.5; no infinity or NaN), two per byte
-  with element 2i in the low nibble of byte i;
+  with element 2i in the low nibble of byte i, or FP6 E2M3 codes (2
+  exponent bits with bias 1, 3 mantissa bits) or E3M2 codes (3 exponent bits
+  with bias 3, 2 mantissa bits), no infinity or NaN, packed as a
+  little-endian bit stream (element i in bits 6i .. 6i+5 of its row);
 * an element's value is scale * element.
 
 For A (M x K) each row has ceil(K/32) scales. For B (K x N) each column has
@@ -57,6 +60,40 @@ def decode_e2m1(codes: np.ndarray) -> np.ndarray:
     return np.where(sign == 1, -mag, mag)
 
 
+def _decode_minifloat(codes: np.ndarray, ebits: int, mbits: int, bias: int) -> np.ndarray:
+    """Sign, ebits exponent bits, mbits mantissa bits; exponent field 0 is
+    subnormal; every other code is a normal number (no infinity or NaN)."""
+    width = 1 + ebits + mbits
+    c = np.asarray(codes, dtype=np.int64) & ((1 << width) - 1)
+    sign = c >> (width - 1)
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    m = c & ((1 << mbits) - 1)
+    frac = m / float(1 << mbits)
+    mag = np.where(e == 0, np.ldexp(frac, 1 - bias), np.ldexp(1.0 + frac, e - bias))
+    return np.where(sign == 1, -mag, mag)
+
+
+def decode_e2m3(codes: np.ndarray) -> np.ndarray:
+    """6-bit E2M3 codes -> binary64."""
+    return _decode_minifloat(codes, 2, 3, 1)
+
+
+def decode_e3m2(codes: np.ndarray) -> np.ndarray:
+    """6-bit E3M2 codes -> binary64."""
+    return _decode_minifloat(codes, 3, 2, 3)
+
+
+def unpack_fp6(packed: np.ndarray) -> np.ndarray:
+    """rows x 3K/4 bytes -> rows x K 6-bit codes (little-endian bit stream:
+    element i in bits 6i .. 6i+5)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    rows, nbytes = b.shape
+    bits = np.unpackbits(b, axis=1, bitorder="little")          # bit j of the row
+    k = nbytes * 8 // 6
+    bits = bits[:, :k * 6].reshape(rows, k, 6).astype(np.int64)
+    return (bits * (1 << np.arange(6))).sum(axis=2).astype(np.uint8)
+
+
 def unpack_fp4(packed: np.ndarray) -> np.ndarray:
     """rows x K/2 bytes -> rows x K codes (element 2i = low nibble)."""
     b = np.asarray(packed, dtype=np.uint8)
@@ -70,20 +107,27 @@ def _element_table(fmt: str) -> np.ndarray:
     codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
     if fmt == "e2m1":
         return decode_e2m1(codes)
+    if fmt == "e2m3":
+        return decode_e2m3(codes)
+    if fmt == "e3m2":
+        return decode_e3m2(codes)
     if fmt == "e4m3":
         return reference.decode_e4m3(codes)
     if fmt == "e5m2":
         return reference.decode_e5m2(codes)
-    raise ValueError("block-scaled element format must be e4m3, e5m2 or e2m1, not %r" % (fmt,))
+    raise ValueError("block-scaled element format must be e4m3, e5m2, e2m3, e3m2 or e2m1, not %r" % (fmt,))
 
 
 def scaled_operand(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
-    """Rows x K element codes (rows x K/2 packed bytes for e2m1) and
+    """Rows x K element codes (rows x K/2 packed bytes for e2m1, rows x
+    3K/4 for e2m3 / e3m2) and
     rows x ceil(K/32) E8M0 scales -> the binary64 values
     2^(s - 127) * element, rows x K."""
     codes = np.asarray(codes, dtype=np.uint8)
     if fmt == "e2m1":
         codes = unpack_fp4(codes)
+    elif fmt in ("e2m3", "e3m2"):
+        codes = unpack_fp6(codes)
     rows, K = codes.shape
     nb = -(-K // BLOCK)
     scales = np.asarray(scales, dtype=np.uint8)

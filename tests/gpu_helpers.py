@@ -19,7 +19,8 @@ from oracle import mx as mx_oracle
 from oracle import reference as oracle
 
 TOL = {"bf16": (1e-3, 1e-6), "e4m3": (2e-2, 0.0), "e5m2": (2e-2, 0.0), "e4m3e5m2": (2e-2, 0.0),
-       "mxe4m3": (2e-2, 0.0), "mxe5m2": (2e-2, 0.0), "mxe4m3e5m2": (2e-2, 0.0), "mxfp4": (2e-2, 0.0)}
+       "mxe4m3": (2e-2, 0.0), "mxe5m2": (2e-2, 0.0), "mxe4m3e5m2": (2e-2, 0.0), "mxfp4": (2e-2, 0.0),
+       "mxfp6e2m3": (2e-2, 0.0), "mxfp6e3m2": (2e-2, 0.0)}
 
 
 def say(*a):
@@ -41,7 +42,8 @@ def out_dtype(fmt: str, out: str) -> int:
     table = {"bf16": (g.BF16_F32, g.BF16_BF16), "e4m3": (g.E4M3_F32, g.E4M3_BF16),
              "e5m2": (g.E5M2_F32, g.E5M2_BF16), "e4m3e5m2": (g.E4M3_E5M2_F32, g.E4M3_E5M2_BF16),
              "mxe4m3": (g.MXE4M3_F32, g.MXE4M3_BF16), "mxe5m2": (g.MXE5M2_F32, g.MXE5M2_BF16),
-             "mxe4m3e5m2": (g.MXE4M3_E5M2_F32, g.MXE4M3_E5M2_BF16), "mxfp4": (g.MXFP4_F32, g.MXFP4_BF16)}
+             "mxe4m3e5m2": (g.MXE4M3_E5M2_F32, g.MXE4M3_E5M2_BF16), "mxfp4": (g.MXFP4_F32, g.MXFP4_BF16),
+             "mxfp6e2m3": (g.MXFP6_E2M3_F32, g.MXFP6_E2M3_BF16), "mxfp6e3m2": (g.MXFP6_E3M2_F32, g.MXFP6_E3M2_BF16)}
     return table[fmt][1 if out == "bf16" else 0]
 
 

@@ -88,9 +88,10 @@ PLAN_SHAPES = [
     (512, 1024, 4096, 64, 2), (1, 1, 1, 1, 0), (17, 300, 40, 3, 2), (5000, 33, 9000, 1, 0),
     (1000, 900, 700, 1, 3), (64, 4096, 8192, 2, 4), (8192, 8192, 8192, 1, 5),
     (512, 1024, 4096, 64, 5), (1000, 900, 768, 1, 5), (100, 70, 131072, 1, 5),
-    (8192, 8192, 8192, 1, 6), (300, 500, 512, 3, 6),
+    (8192, 8192, 8192, 1, 6), (300, 500, 512, 3, 6), (4096, 4096, 4096, 1, 7), (300, 520, 384, 2, 7),
 ]
-PLAN_DTYPES = ["BF16_F32", "BF16_BF16", "E4M3_F32", "E5M2_F32", "E4M3_E5M2_BF16", "MXE4M3_F32", "MXFP4_F32"]
+PLAN_DTYPES = ["BF16_F32", "BF16_BF16", "E4M3_F32", "E5M2_F32", "E4M3_E5M2_BF16", "MXE4M3_F32", "MXFP4_F32",
+               "MXFP6_E3M2_BF16"]
 
 KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1, persistent=1),
          dict(split_k=5, persistent=1), dict(tile=1), dict(tile=2, persistent=1, split_k=1)]
@@ -103,7 +104,9 @@ def _plan_and_check(g, M, N, K, batch, dtype, knobs):
         knobs = dict(knobs, tile=knobs["tile"] + 48)           # the block-scaled 128x128 tiles
     elif "tile" in knobs and dtype == g.MXFP4_F32:
         knobs = dict(knobs, tile=knobs["tile"] + 51)           # the FP4 128x128 tiles
-    if dtype in (g.MXE4M3_F32, g.MXFP4_F32):
+    elif "tile" in knobs and dtype == g.MXFP6_E3M2_BF16:
+        knobs = dict(knobs, tile=knobs["tile"] + 59)           # the FP6 128x128 tiles
+    if dtype in (g.MXE4M3_F32, g.MXFP4_F32, g.MXFP6_E3M2_BF16):
         knobs = dict(knobs, block_scale_a=0x300000000000, block_scale_b=0x380000000000)
     a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, dtype=dtype,
                     batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N, cus=256, **knobs)
@@ -235,7 +238,13 @@ def test_argument_errors(g):
     assert status(unit_stamps=0x300000000004) == g.EALIGN  # stamps need 8-byte alignment
     assert status(C=0x200000000002) == g.EALIGN            # fp32 C
     assert status(scale_a=0x3001) == g.EALIGN
-    assert status(dtype=16) == g.EINVAL
+    assert status(dtype=20) == g.EINVAL
+    # MX FP6: native layout, leading dimensions multiples of 64, K a multiple of 128
+    FP6 = dict(dtype=g.MXFP6_E2M3_F32, block_scale_a=0x300000000000, block_scale_b=0x380000000000)
+    g.gemm355_plan(g.make_args(64, 64, 128, **P, **FP6))      # valid
+    assert status(K=64, **FP6) == g.EUNSUPPORTED
+    assert status(K=128, lda=160, **FP6) == g.EUNSUPPORTED
+    assert status(K=128, layout=g.A_ROW_B_ROW, ldb=64, **FP6) == g.EUNSUPPORTED
     # MX FP4: native layout, even leading dimensions, K a multiple of 256
     FP4 = dict(dtype=g.MXFP4_F32, block_scale_a=0x300000000000, block_scale_b=0x380000000000)
     g.gemm355_plan(g.make_args(64, 64, 256, **P, **FP4))      # valid
@@ -314,7 +323,7 @@ def test_tile_table(g):
         assert row_bytes in (64, 128)
         # block-scaled tiles keep one dword of E8M0 scales (four 32-value
         # blocks) per 128 values, per row and stage
-        scale_bytes = {2: 4, 3: 8}.get(cls, 0)
+        scale_bytes = {2: 4, 3: 8, 4: 4}.get(cls, 0)
         assert info["lds_bytes"] == info["stages"] * (info["T_M"] + info["T_N"]) * (row_bytes + scale_bytes)
         assert info["lds_bytes"] <= 160 * 1024
         seen.add((info["dtype_class"], info["T_M"], info["T_N"]))
@@ -331,7 +340,7 @@ def test_main_loop_uses_mfma(g, tmp_path):
     asm = open(build.device_asm("kernels.hip")).read()
     bodies = re.split(r"\n(?=_ZN4g35516gemm_tile_kernel\w+:)", asm)
     kernels = [b for b in bodies if re.match(r"_ZN4g35516gemm_tile_kernel\w+:", b)]
-    n8 = sum(g.gemm355_tile_info(t)["dtype_class"] in (1, 2) for t in range(g.gemm355_num_tiles()))
+    n8 = sum(g.gemm355_tile_info(t)["dtype_class"] in (1, 2, 4) for t in range(g.gemm355_num_tiles()))
     assert len(kernels) == g.gemm355_num_tiles() + 2 * n8      # three format pairs per 8-bit tile
     for body in kernels:
         name = body.split(":")[0]
@@ -340,13 +349,18 @@ def test_main_loop_uses_mfma(g, tmp_path):
         fp8 = el != 0
         want = {(1, 32): "v_mfma_f32_32x32x64_f8f6f4", (0, 32): "v_mfma_f32_32x32x16_bf16",
                 (1, 16): "v_mfma_f32_16x16x128_f8f6f4", (0, 16): "v_mfma_f32_16x16x32_bf16",
-                (2, 32): "v_mfma_scale_f32_32x32x64_f8f6f4", (3, 32): "v_mfma_scale_f32_32x32x64_f8f6f4"}[(el, mi)]
+                (2, 32): "v_mfma_scale_f32_32x32x64_f8f6f4", (3, 32): "v_mfma_scale_f32_32x32x64_f8f6f4",
+                (4, 32): "v_mfma_scale_f32_32x32x64_f8f6f4"}[(el, mi)]
         code = body.split("s_endpgm")[0]
         lines = [l for l in code.splitlines() if want in l]
         assert lines, name
         if el == 3:
             # FP4 (E2M1) is format 4 for both operands
             assert all("cbsz:4" in l and "blgp:4" in l for l in lines), name
+        elif el == 4:
+            # FP6: E2M3 format 2, E3M2 format 3
+            assert all(("cbsz:3" if fmt == 1 else "cbsz:2") in l for l in lines), name
+            assert all(("blgp:3" if fmt >= 1 else "blgp:2") in l for l in lines), name
         elif fp8:
             # E4M3 is format 0 (no modifier printed), E5M2 format 1
             assert all(("cbsz:1" in l) == (fmt == 1) for l in lines), name

@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 MX_TILES = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["dtype_class"] == 2]
 FP4_TILES = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["dtype_class"] == 3]
+FP6_TILES = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["dtype_class"] == 4]
 
 
 def _bf16_ok(C, C_ref, W, fmt):
@@ -67,8 +68,11 @@ def _int_ops(M, N, K, fmt, seed, batch=0):
     product is a multiple of 2^-4 of magnitude at most 2^8, so every partial
     sum is exact in binary32 for K <= 2^12."""
     ga, gb = inputs.rng(seed), inputs.rng(seed + 1)
-    fa = "e2m1" if fmt == "mxfp4" else "e5m2" if fmt == "mxe5m2" else "e4m3"
-    fb = "e2m1" if fmt == "mxfp4" else "e4m3" if fmt == "mxe4m3" else "e5m2"
+    if fmt.startswith("mxfp6"):
+        fa = fb = fmt[5:]
+    else:
+        fa = "e2m1" if fmt == "mxfp4" else "e5m2" if fmt == "mxe5m2" else "e4m3"
+        fb = "e2m1" if fmt == "mxfp4" else "e4m3" if fmt == "mxe4m3" else "e5m2"
     nb = max(batch, 1)
     A = np.stack([inputs.small_int_codes(ga, (M, K), fa) for _ in range(nb)])
     B = np.stack([inputs.small_int_codes(gb, (N, K), fb) for _ in range(nb)])
@@ -79,12 +83,13 @@ def _int_ops(M, N, K, fmt, seed, batch=0):
     return inputs.Operands(M, N, K, fmt, A, B, [1.0] * nb, [1.0] * nb, (seed, seed + 1), sa, sb)
 
 
-@pytest.mark.parametrize("fmt", ["mxe4m3", "mxe5m2", "mxe4m3e5m2", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["mxe4m3", "mxe5m2", "mxe4m3e5m2", "mxfp4", "mxfp6e2m3", "mxfp6e3m2"])
 def test_mx_exact_integers_every_tile(fmt):
     M, N, K, batch = 200, 170, 512, 2
     ops = _int_ops(M, N, K, fmt, 81, batch=batch)
     refs = [H.oracle_full(ops, bi)[0] for bi in range(batch)]
-    for tile in (FP4_TILES if fmt == "mxfp4" else MX_TILES):
+    tiles = FP4_TILES if fmt == "mxfp4" else FP6_TILES if fmt.startswith("mxfp6") else MX_TILES
+    for tile in tiles:
         for knobs in (dict(split_k=1, persistent=0), dict(split_k=3), dict(persistent=1)):
             H.say(fmt, "ints tile", tile, knobs)
             C = H.run(ops, out="f32", tile=tile, **knobs)
@@ -165,6 +170,40 @@ def test_mxfp4_block_boundaries_and_batch():
         C = H.run(ops, out="f32", **knobs)
         for bi in range(batch):
             H.check(C[bi], refs[bi][0], refs[bi][1], "mxfp4", "batch %d %s" % (bi, knobs))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp6e2m3", "mxfp6e3m2"])
+@pytest.mark.parametrize("shape", [(300, 520, 256), (257, 129, 384), (70, 90, 128), (1, 1, 128)])
+def test_mxfp6_ragged_full(fmt, shape):
+    M, N, K = shape
+    ops = inputs.make_operands(M, N, K, fmt, "normal", 850 + M + K, 851 + N)
+    C_ref, W = H.oracle_full(ops)
+    for tile in [-1] + FP6_TILES:
+        for out in ("f32", "bf16"):
+            H.say(fmt, "tile", tile, shape, out)
+            C = H.run(ops, out=out, tile=tile)
+            if out == "f32":
+                H.check(C, C_ref, W, fmt, "%s tile %d %s" % (fmt, tile, shape))
+            else:
+                assert _bf16_ok(C, C_ref, W, fmt), (fmt, tile, shape)
+
+
+def test_mxfp6_batch_split_and_4096_sampled():
+    M, N, K, batch = 300, 260, 640, 3
+    ops = inputs.make_operands(M, N, K, "mxfp6e3m2", "normal", 95, 96, batch=batch)
+    refs = [H.oracle_full(ops, bi) for bi in range(batch)]
+    for knobs in (dict(), dict(split_k=2), dict(persistent=1), dict(workspace="caller", split_k=3)):
+        H.say("mxfp6 batch", knobs)
+        C = H.run(ops, out="f32", **knobs)
+        for bi in range(batch):
+            H.check(C[bi], refs[bi][0], refs[bi][1], "mxfp6e3m2", "batch %d %s" % (bi, knobs))
+    M = N = K = 4096
+    ops = inputs.make_operands(M, N, K, "mxfp6e2m3", "normal", 103, 104)
+    H.say("mxfp6 4096^3")
+    C = H.run(ops, out="f32")
+    rows, cols = H.sample_positions(M, N, 3000, 13)
+    c_ref, w = H.oracle_entries(ops, rows, cols)
+    H.check(C[rows, cols], c_ref, w, "mxfp6e2m3", "mxfp6 4096^3 sampled")
 
 
 def test_mxfp4_4096_sampled():

@@ -226,3 +226,62 @@ def test_fp4_block_decomposition_through_e4m3():
         torch.float8_e4m3fn).view(torch.uint8).numpy()
     Cr, Wr = _blockwise(to8(A4), sa, to8(B4), sb, "e4m3", "e4m3")
     assert np.all(np.abs(C4 - Cr) <= 1e-12 * Wr)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_decoders_match_spec_values(fmt):
+    """Every 6-bit code against the magnitudes of the OCP specification's
+    format parameters (tests/golden/fp6_values.json: bias, mantissa width
+    and the listed extremes), sign in bit 5."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp6_values.json")
+    table = json.load(open(path))[fmt]
+    dec = mx.decode_e2m3 if fmt == "e2m3" else mx.decode_e3m2
+    got = dec(np.arange(64))
+    for code, v in table.items():
+        assert got[int(code)] == v
+        assert got[int(code) | 32] == -v and np.signbit(got[int(code) | 32])
+    assert np.all(np.diff(got[:32]) > 0)
+
+
+def test_fp6_bit_stream_order():
+    """Element i sits in bits 6i .. 6i+5 of its row (little-endian)."""
+    packed = np.array([[0b11000001, 0b00000000, 0b00000000]], dtype=np.uint8)   # e0 = 1, e1 = 3
+    assert mx.unpack_fp6(packed).tolist() == [[1, 3, 0, 0]]
+    packed = np.array([[0, 0, 0b11111100]], dtype=np.uint8)                     # e3 = 63
+    assert mx.unpack_fp6(packed).tolist() == [[0, 0, 0, 63]]
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_product_through_e4m3(fmt):
+    """Every E2M3 and E3M2 value is an E4M3 value: the FP6 product equals
+    the 8-bit product of the same values re-encoded as E4M3 by torch's cast,
+    block by block through the C oracle."""
+    from dense_tiled_gemm_fp8_amd import inputs
+    g = np.random.Generator(np.random.PCG64(13))
+    M, N, K = 9, 7, 256
+    A6 = inputs.pack_fp6(g.integers(0, 64, size=(M, K)).astype(np.uint8))
+    B6 = inputs.pack_fp6(g.integers(0, 64, size=(N, K)).astype(np.uint8))
+    sa = g.integers(110, 140, size=(M, K // 32)).astype(np.uint8)
+    sb = g.integers(110, 140, size=(N, K // 32)).astype(np.uint8)
+    C6, _ = mx.gemm(A6, sa, B6, sb, fmt)
+    dec = mx.decode_e2m3 if fmt == "e2m3" else mx.decode_e3m2
+    to8 = lambda p: torch.from_numpy(dec(mx.unpack_fp6(p)).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    Cr, Wr = _blockwise(to8(A6), sa, to8(B6), sb, "e4m3", "e4m3")
+    assert np.all(np.abs(C6 - Cr) <= 1e-12 * Wr)
+
+
+def test_fp6_input_rounding_is_nearest_even():
+    from dense_tiled_gemm_fp8_amd import inputs
+    for fmt, dec in (("e2m3", mx.decode_e2m3), ("e3m2", mx.decode_e3m2)):
+        vals = dec(np.arange(32))
+        g = np.random.Generator(np.random.PCG64(14))
+        y = np.concatenate([g.uniform(-40, 40, 3000), (vals[1:] + vals[:-1]) / 2, vals])
+        c = inputs.to_fp6_codes(y, fmt)
+        mag = np.minimum(np.abs(y), vals[-1])
+        best = np.min(np.abs(vals[None, :] - mag[:, None]), axis=1)
+        assert np.all(np.abs(np.abs(dec(c)) - mag) == best)
+        tie = (np.abs(vals[None, :] - mag[:, None]) == best[:, None]).sum(axis=1) > 1
+        assert np.all((c[tie] & 1) == 0)
