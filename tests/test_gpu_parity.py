@@ -250,6 +250,27 @@ def test_degenerate_sizes():
     H.check(Cg.cpu().numpy().astype(np.float64), C_ref, W, "bf16", "gemm355_gemm")
 
 
+def test_largest_row_offsets_sampled():
+    """K = 4,000,000 bf16 (8 MB rows): a tile's 256 rows span just under the
+    2^31 bytes of 32-bit buffer offsets the main loop uses, and the split-K
+    slices reach the far end of every row.  Sampled outputs (corners and
+    ragged edges included) against the oracle."""
+    M, N, K = 300, 200, 4_000_000
+    r = np.random.Generator(np.random.PCG64(1234))
+    lut = inputs.to_bf16_codes(np.arange(-4, 5, dtype=np.float64))
+    A = lut[r.integers(0, 9, size=(M, K), dtype=np.uint8)]
+    B = lut[r.integers(0, 9, size=(N, K), dtype=np.uint8)]
+    ops = inputs.Operands(M, N, K, "bf16", A, B, [1.0], [1.0], (1234, 1234))
+    a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
+    p = g.gemm355_plan(a)
+    assert 256 * K * 2 <= 0x7FFF0000
+    H.say("K = 4e6, plan", p["T_M"], p["T_N"], "split", p["split"], "tail", p["tail_tiles"], p["tail_split"])
+    C = H.run(ops, out="f32")
+    rows, cols = H.sample_positions(M, N, 40, 3)
+    c, w = H.oracle_entries(ops, rows, cols)
+    H.check(C[rows, cols], c, w, "bf16", "K = 4e6")
+
+
 # ------------------------------------------------------------ full-size workloads
 
 def _sampled(ops, out, n=3000, batch_entries=(0,), what=""):
