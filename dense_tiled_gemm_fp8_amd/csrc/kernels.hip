@@ -2,9 +2,10 @@
  * kernels.hip -- gfx950 kernels of libgemm355.
  *
  *   gemm_tile_kernel  the MFMA main loop over work units (tile x K-range):
- *                     LDS-staged A/B tiles in a two-stage ring fed by
- *                     direct-to-LDS buffer loads, fp32 accumulators,
- *                     epilogue to C or to a split-K partial slot
+ *                     LDS-staged A/B tiles (and block scales) in a ring fed
+ *                     by direct-to-LDS buffer loads, fp32 accumulators,
+ *                     epilogue to C or to a split-K partial slot; also the
+ *                     implicit-GEMM convolution (A gathered from images)
  *   reduce_kernel     the split-K combine: sums a tile's partial slots in
  *                     ascending slice order, scales, converts, stores C
  *   pack_rows_kernel, pack_transpose_kernel
@@ -19,7 +20,8 @@
  * Source pages: "10. Tensor Cores, shapes, and tile alignment" (tile grid,
  * split-K, persistent loop) and "The Tensor Core" (stage A and B tiles in
  * on-chip memory once and feed many matrix-unit operations from them; low
- * precision inputs with a wide accumulator).
+ * precision inputs with a wide accumulator; the precision table's FP8 and
+ * microscaled rows; convolutions as GEMM).
  */
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -148,12 +150,16 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
 }
 
 /*
- * One workgroup of WGM x WGN wavefronts (4 or 8) computes a TM x TN tile;
- * wavefront (wm, wn) owns a (TM/WGM) x (TN/WGN) block made of 32 x 32 MFMA
- * blocks.  With 8 wavefronts two share each SIMD, so one issues MFMAs while
- * the other waits on LDS or at the barrier.  A
- * K-tile is RB bytes of K per row (64 or 128: 32/64 bf16 or 64/128 E4M3
- * values); the LDS holds a ring of STAGES K-tiles.
+ * One workgroup of WGM x WGN wavefronts (4, 8 or 16) computes a TM x TN
+ * tile; wavefront (wm, wn) owns a (TM/WGM) x (TN/WGN) block made of MI x MI
+ * MFMA blocks (32 or 16).  With 8 wavefronts two share each SIMD, so one
+ * issues MFMAs while the other waits on LDS or at the barrier.  A K-tile is
+ * RB bytes of K per row (64 or 128: 32/64 bf16, 64/128 8-bit, 256 FP4 or 128
+ * FP6 values); the LDS holds a ring of STAGES K-tiles.  Template knobs
+ * beyond the shape: EL, the element class (bf16, 8-bit, block-scaled 8-, 4-
+ * and 6-bit); SPREAD, the copy schedule (0-3, tiles.h); OP, the operation
+ * (matrix product, or a convolution whose A rows are gathered from NHWC
+ * images); FMT, the operand-format pair of the 8- and 6-bit classes.
  *
  * LDS layout of one stage of A (B alike): TM rows of RB bytes.  The LDS
  * serves a 128-bit read 16 lanes at a time from 64 four-byte banks, i.e. one
