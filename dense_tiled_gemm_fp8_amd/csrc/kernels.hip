@@ -240,6 +240,11 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     static_assert(SPREAD != 3 || STAGES >= 3, "producer wavefronts run two K-tiles ahead");
     static_assert(!CONV || (!FP8 && SPREAD == 0 && RB == 128), "convolution: bf16, 64-channel K-tiles copied in one step");
     static_assert(!FP6 || (RB == 128 && MI == 32), "FP6: 128-value K-tiles in 128-byte rows, 32 x 32 blocks");
+    /* SPREAD 4: copies as in schedule 0; A's fragments single-buffered, each
+     * row's next fragment read into its own registers right after the row's
+     * last MFMA (B's double-buffered), so the fragments take FM fewer
+     * registers */
+    static_assert(SPREAD != 4 || (!FP8 && !CONV && FM + FN - 1 <= 15), "in-place A fragments: bf16 matrix products");
     static_assert(A_LOADS * CW * ROWS_PER_DMA == TM && B_LOADS * CW * ROWS_PER_DMA == TN, "whole copies");
     static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == SW * (TM + TN)),
                   "block scales: whole dwords per row and K-tile, whole 64-row copies per wavefront");
@@ -535,19 +540,31 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 /* this step's fragments (read two steps ago) are in; the NR
                  * reads of the previous step may still be outstanding */
                 asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NR < 15 ? NR : 15) : "memory");
+            } else if constexpr (SPREAD == 4) {
+                /* waits per row, below */
             } else {
                 /* this step's fragments (read during the previous step) are
                  * in; nothing else is outstanding on the LDS counter here */
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
+            /* A's fragment buffer (SPREAD 4: one) */
+            constexpr int CA = SPREAD == 4 ? 0 : CUR;
             unroll<SLOTS>([&](auto tc) __attribute__((always_inline)) {
                 constexpr int t = decltype(tc)::value;
+                if constexpr (SPREAD == 4 && t < NM && t % FN == 0) {
+                    /* row t / FN's A fragment (read after that row of the
+                     * previous step) is in: newer reads are the later rows'
+                     * (FM - 1 - row), and this step's B reads and earlier
+                     * rows' A reads (FN + row) once row 0 has issued them */
+                    constexpr int ROW = t / FN, NEWER = ROW == 0 ? FM - 1 : FM + FN - 1;
+                    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NEWER) : "memory");
+                }
                 if constexpr (t < NM) {
                     constexpr int i = t / FN, j = t % FN;
                     if constexpr (!FP8 && MI == 32)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CA][i], fb[CUR][j], acc[i][j], 0, 0, 0);
                     else if constexpr (!FP8)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CA][i], fb[CUR][j], acc[i][j], 0, 0, 0);
                     else if constexpr (MX) {
                         /* the step's first block: its plane and byte */
                         constexpr int B0 = KS * (FP6 ? 2 : KB_STEP * VPB / 32), DW = B0 / 4, SH = 8 * (B0 % 4);
@@ -564,7 +581,14 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             fa[CUR][i], fb[CUR][j], acc[i][j], FA, FB, 0, 0, 0, 0);
                 }
-                if constexpr (t < FM)
+                if constexpr (SPREAD == 4) {
+                    /* B's next fragments during row 0; row i's next A
+                     * fragment right after its last MFMA */
+                    if constexpr (t < FN)
+                        fb[TGT][t] = frag(ns + A_BYTES + wn * WTN * RB, nks, t);
+                    if constexpr (t < NM && t % FN == FN - 1)
+                        fa[0][t / FN] = frag(ns + wm * WTM * RB, nks, t / FN);
+                } else if constexpr (t < FM)
                     fa[TGT][t] = frag(ns + wm * WTM * RB, nks, t);
                 else if constexpr (t < NR)
                     fb[TGT][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
@@ -1186,7 +1210,8 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(58, 128, 128, false, 1, 128, 4, 2, 2, 0, 32, 1)                                               \
     X(59, 256, 256, 4, 1, 128, 2, 2, 2, 0, 32, 0)                                                   \
     X(60, 128, 128, 4, 2, 128, 2, 2, 2, 0, 32, 0)                                                   \
-    X(61, 128, 128, 4, 1, 128, 4, 2, 2, 0, 32, 0)
+    X(61, 128, 128, 4, 1, 128, 4, 2, 2, 0, 32, 0)                                                   \
+    X(62, 256, 256, false, 1, 128, 2, 2, 2, 4, 16, 0)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn)                                                      \

@@ -38,7 +38,9 @@ struct TileCfg {
                               3 warp specialisation: four more wavefronts
                               (one per SIMD) issue every copy, STAGES-1
                               K-tiles ahead, and the waves_m x waves_n MFMA
-                              wavefronts only read LDS (3 stages or more)  */
+                              wavefronts only read LDS (3 stages or more);
+                              4 as 0 with A's fragments read in place, one
+                              row at a time (bf16)                          */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
     int32_t lds_bytes;     /* stages * (TM + TN) * RB, plus 4 (8 for FP4)
                               bytes of block scales per row and stage for
@@ -150,6 +152,8 @@ constexpr TileCfg kTiles[] = {
     {4, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 132, 1, 512, {0.80f, 0.80f, 0.80f, 0.80f}, 0.80f},
     {4, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 132, 2, 256, {0.45f, 0.60f, 0.60f, 0.60f}, 0.70f},
     {4, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 132, 1, 512, {0.45f, 0.45f, 0.45f, 0.45f}, 0.55f},
+    /* 16 x 16 blocks with A's fragments read in place (copy schedule 4) */
+    {0, 256, 256, 64, 128, 2, 2, 2, 4, 16, 2 * (256 + 256) * 128, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 0.80f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 
