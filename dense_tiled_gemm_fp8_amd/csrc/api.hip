@@ -203,8 +203,10 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
     const uint8_t *Bop = (const uint8_t *)a.B;
     const bool a_row = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_ROW_B_ROW;
     const bool b_col = a.layout == GEMM355_A_ROW_B_COL || a.layout == GEMM355_A_COL_B_COL;
+    PackParams pks[2];
+    int npk = 0;
     if (P.pack_a) {
-        PackParams pk;
+        PackParams &pk = pks[npk++];
         pk.src = a.A;
         pk.dst = ws + P.ws_pack_a_off;
         pk.ld = a.lda;
@@ -216,11 +218,10 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
         pk.batch = (int32_t)a.batch;
         pk.esize = P.esize;
         pk.kmajor = a_row ? 1 : 0;
-        if (launch_pack(pk, hs) != hipSuccess) return GEMM355_EHIP;
         Aop = pk.dst;
     }
     if (P.pack_b) {
-        PackParams pk;
+        PackParams &pk = pks[npk++];
         pk.src = a.B;
         pk.dst = ws + P.ws_pack_b_off;
         pk.ld = a.ldb;
@@ -232,9 +233,9 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
         pk.batch = (int32_t)a.batch;
         pk.esize = P.esize;
         pk.kmajor = b_col ? 1 : 0;
-        if (launch_pack(pk, hs) != hipSuccess) return GEMM355_EHIP;
         Bop = pk.dst;
     }
+    if (npk && launch_pack(pks, npk, hs) != hipSuccess) return GEMM355_EHIP;
 
     GemmParams gp;
     gp.A = Aop;

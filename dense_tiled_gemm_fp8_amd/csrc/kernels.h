@@ -88,7 +88,8 @@ hipError_t launch_quantize(const QuantParams &qp, hipStream_t stream);
 hipError_t launch_gemm(int32_t tile, int32_t fmt, const GemmParams &p, hipStream_t stream);
 const void *gemm_kernel_symbol(int32_t tile);
 hipError_t launch_reduce(const ReduceParams &r, int32_t tiles, hipStream_t stream);
-hipError_t launch_pack(const PackParams &pk, hipStream_t stream);
+/* repack n (1 or 2) operands in one launch */
+hipError_t launch_pack(const PackParams *pk, int n, hipStream_t stream);
 hipError_t launch_pack_scales(const ScalePackParams &sp, hipStream_t stream);
 hipError_t launch_zero(void *C, int32_t M, int32_t N, int64_t ldc, int64_t stride_c,
                        int32_t batch, int32_t esize, hipStream_t stream);

@@ -8,11 +8,10 @@
  *                     implicit-GEMM convolution (A gathered from images)
  *   reduce_kernel     the split-K combine: sums a tile's partial slots in
  *                     ascending slice order, scales, converts, stores C
- *   pack_rows_kernel, pack_transpose_kernel
- *                     repack an operand into the K-contiguous, 16-byte
- *                     aligned layout the main loop reads (misaligned rows
- *                     or K not a multiple of 16 bytes; the three other
- *                     operand layouts)
+ *   pack_kernel       repack A and/or B (one launch) into the K-contiguous,
+ *                     16-byte aligned layout the main loop reads
+ *                     (misaligned rows or K not a multiple of 16 bytes;
+ *                     the three other operand layouts)
  *   pack_scales_kernel
  *                     regroup block scales (MX) K-tile-major
  *   zero_kernel       C = 0 for K == 0
@@ -948,21 +947,50 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
  * Repack one operand to K-contiguous rows of ldd_bytes (a multiple of 16),
  * zero-filled beyond K.  Source element (row, k) of batch entry g is at
  * src[g*stride + (kmajor ? row*ld + k : k*ld + row)] (elements of esize
- * bytes).
+ * bytes).  pack_kernel repacks up to two operands in one launch: blocks
+ * [0, nb0) work on the first, the rest on the second.
  *
- * pack_rows_kernel (K-contiguous source whose rows are misaligned or whose
- * K is not a whole number of 16-byte chunks): one wavefront per row.  The
- * row is read through a buffer resource based at the 16-byte boundary at
- * or below the row's first byte and ending at the 16-byte boundary at or
- * above its last byte, so every 16-byte block read lies in a block that
- * holds a byte of the row (never past the allocation) and blocks beyond
- * read as zero.  Output chunk c is bytes [sh + 16c, sh + 16c + 16) of that
- * window (sh = the row's offset from the boundary): two aligned 16-byte
- * loads and a byte funnel shift.  Bytes at or beyond K are cleared.
+ * pack_rows (K-contiguous source whose rows are misaligned or whose K is
+ * not a whole number of 16-byte chunks): one wavefront per row.  The row
+ * is read through a buffer resource based at the 16-byte boundary at or
+ * below the row's first byte and ending at the 16-byte boundary at or above
+ * its last byte, so every 16-byte block read lies in a block that holds a
+ * byte of the row (never past the allocation) and blocks beyond read as
+ * zero.  Output chunk c is bytes [sh + 16c, sh + 16c + 16) of that window
+ * (sh = the row's offset from the boundary): two aligned 16-byte loads and
+ * a byte funnel shift.  A lane takes chunks lane + 64i and issues the loads
+ * of four of them before the first store.  Bytes at or beyond K are
+ * cleared.
  */
-__global__ __launch_bounds__(256) void pack_rows_kernel(PackParams pk)
+__device__ __forceinline__ i32x4 pack_chunk(const i32x4 lo, const i32x4 hi, uint32_t q, uint32_t rb, uint32_t valid)
 {
-    const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    int o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        /* dword j of the chunk: bytes sh + 4j .. sh + 4j + 3 of the window,
+         * i.e. (w[q + j + 1] : w[q + j]) >> (8 rb) */
+        int d0 = w[j], d1 = w[j + 1];
+        if (q == 1) { d0 = w[j + 1]; d1 = w[j + 2]; }
+        if (q == 2) { d0 = w[j + 2]; d1 = w[j + 3]; }
+        if (q == 3) { d0 = w[j + 3]; d1 = w[j + 4]; }
+        o[j] = (int)__builtin_amdgcn_alignbyte((uint32_t)d1, (uint32_t)d0, rb);
+    }
+    if (valid < 16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int32_t vb = (int32_t)valid - 4 * j;
+            const uint32_t keep = vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+            o[j] = (int)((uint32_t)o[j] & keep);
+        }
+    }
+    return i32x4{o[0], o[1], o[2], o[3]};
+}
+
+__device__ __forceinline__ void pack_rows(const PackParams &pk, int64_t blk)
+{
+    constexpr int NC = 4; /* chunks per lane per round */
+    const int64_t row_id = blk * 4 + (threadIdx.x >> 6);
     if (row_id >= (int64_t)pk.batch * pk.rows) return;
     const int lane = threadIdx.x & 63;
     const int64_t g = row_id / pk.rows, r = row_id - g * pk.rows;
@@ -976,54 +1004,38 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(PackParams pk)
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)nrec, 0x00020000);
     uint8_t *drow = pk.dst + g * pk.dst_stride_bytes + r * pk.ldd_bytes;
     const uint32_t q = sh >> 2, rb = sh & 3u;
-    const int32_t chunks = (int32_t)(pk.ldd_bytes / 16);
-    for (int32_t c = lane; c < chunks; c += 64) {
-        const uint32_t off = (uint32_t)c * 16u;
-        i32x4 out{0, 0, 0, 0};
-        if (off < kbytes) {
-            const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-            const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
-            const int w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            int o[4];
+    const uint32_t chunks = (uint32_t)(pk.ldd_bytes / 16);
+    for (uint32_t c0 = (uint32_t)lane; c0 < chunks; c0 += 64 * NC) {
+        i32x4 lo[NC], hi[NC];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                /* dword j of the chunk: bytes sh + 4j .. sh + 4j + 3 of the
-                 * window, i.e. (w[q + j + 1] : w[q + j]) >> (8 rb) */
-                int d0 = w[j], d1 = w[j + 1];
-                if (q == 1) { d0 = w[j + 1]; d1 = w[j + 2]; }
-                if (q == 2) { d0 = w[j + 2]; d1 = w[j + 3]; }
-                if (q == 3) { d0 = w[j + 3]; d1 = w[j + 4]; }
-                o[j] = (int)__builtin_amdgcn_alignbyte((uint32_t)d1, (uint32_t)d0, rb);
-            }
-            /* clear bytes at or beyond K */
-            const uint32_t valid = kbytes - off;
-            if (valid < 16) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int32_t vb = (int32_t)valid - 4 * j;
-                    const uint32_t keep = vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
-                    o[j] = (int)((uint32_t)o[j] & keep);
-                }
-            }
-            out = i32x4{o[0], o[1], o[2], o[3]};
+        for (int i = 0; i < NC; ++i) {
+            /* offsets past the window read as zero; no test needed */
+            const uint32_t off = (c0 + 64u * i) * 16u;
+            lo[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            hi[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
         }
-        *(i32x4 *)(drow + off) = out;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const uint32_t c = c0 + 64u * i;
+            if (c >= chunks) break;
+            const uint32_t off = c * 16u;
+            const i32x4 out = off < kbytes ? pack_chunk(lo[i], hi[i], q, rb, kbytes - off) : i32x4{0, 0, 0, 0};
+            *(i32x4 *)(drow + off) = out;
+        }
     }
 }
 
 /*
- * pack_transpose_kernel (source with rows contiguous along the operand's
- * M or N index, i.e. element (row, k) at k*ld + row): a workgroup moves a
- * 64-row x 64-k block through LDS: reads along rows (consecutive lanes,
- * consecutive rows), writes 16-byte chunks of the K-contiguous output.
- * Blocks along k cover the whole padded row; k >= K reads as zero.
+ * pack_transpose (source with rows contiguous along the operand's M or N
+ * index, i.e. element (row, k) at k*ld + row): a workgroup moves a 64-row x
+ * 64-k block through LDS: reads along rows (consecutive lanes, consecutive
+ * rows), writes 16-byte chunks of the K-contiguous output.  Blocks along k
+ * cover the whole padded row; k >= K reads as zero.
  */
-__global__ __launch_bounds__(256) void pack_transpose_kernel(PackParams pk)
+__device__ __forceinline__ void pack_transpose(const PackParams &pk, int64_t bid, uint16_t (*tile)[65])
 {
-    __shared__ uint16_t tile[64][65];
     const int32_t kblocks = (int32_t)((pk.ldd_bytes / pk.esize + 63) / 64);
     const int32_t rblocks = (pk.rows + 63) / 64;
-    const int64_t bid = blockIdx.x;
     const int32_t kb = (int32_t)(bid % kblocks);
     const int64_t t2 = bid / kblocks;
     const int32_t rbk = (int32_t)(t2 % rblocks);
@@ -1065,6 +1077,18 @@ __global__ __launch_bounds__(256) void pack_transpose_kernel(PackParams pk)
         __builtin_memcpy(&w, out, 16);
         *(i32x4 *)(pk.dst + g * pk.dst_stride_bytes + (int64_t)row * pk.ldd_bytes + boff) = w;
     }
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(PackParams p0, PackParams p1, uint32_t nb0)
+{
+    __shared__ uint16_t tile[64][65];
+    const bool first = blockIdx.x < nb0;
+    const PackParams &pk = first ? p0 : p1;
+    const int64_t blk = first ? (int64_t)blockIdx.x : (int64_t)(blockIdx.x - nb0);
+    if (pk.kmajor)
+        pack_rows(pk, blk);
+    else
+        pack_transpose(pk, blk, tile);
 }
 
 /*
@@ -1266,17 +1290,21 @@ hipError_t launch_reduce(const ReduceParams &r0, int32_t tiles, hipStream_t stre
     return hipGetLastError();
 }
 
-hipError_t launch_pack(const PackParams &pk, hipStream_t stream)
+static int64_t pack_blocks(const PackParams &pk)
 {
-    if (pk.kmajor) {
-        const int64_t rows = (int64_t)pk.batch * pk.rows;
-        hipLaunchKernelGGL(pack_rows_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream, pk);
-    } else {
-        const int64_t kblocks = (pk.ldd_bytes / pk.esize + 63) / 64;
-        const int64_t rblocks = (pk.rows + 63) / 64;
-        hipLaunchKernelGGL(pack_transpose_kernel, dim3((uint32_t)((int64_t)pk.batch * rblocks * kblocks)), dim3(256), 0,
-                           stream, pk);
-    }
+    if (pk.kmajor) return ((int64_t)pk.batch * pk.rows + 3) / 4;
+    const int64_t kblocks = (pk.ldd_bytes / pk.esize + 63) / 64;
+    const int64_t rblocks = (pk.rows + 63) / 64;
+    return (int64_t)pk.batch * rblocks * kblocks;
+}
+
+hipError_t launch_pack(const PackParams *pk, int n, hipStream_t stream)
+{
+    const int64_t nb0 = pack_blocks(pk[0]);
+    const int64_t nb = nb0 + (n > 1 ? pack_blocks(pk[1]) : 0);
+    if (nb >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)nb), dim3(256), 0, stream, pk[0], n > 1 ? pk[1] : pk[0],
+                       (uint32_t)nb0);
     return hipGetLastError();
 }
 
