@@ -46,6 +46,8 @@ constexpr double kPeakFp4PerCu = 10066.3e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
 constexpr double kExtraPassSec = 4.0e-6;              /* one launch: main, combine or repack */
 constexpr double kCopyBytesPerSecPerCu = 100.0e9;     /* L2 -> LDS copies per compute unit */
+constexpr double kUnitSec = 3.0e-6;                   /* per unit run in turn on one slot: pipeline
+                                                         fill and epilogue */
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -157,9 +159,13 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
                            (c.nK * cfg.TK));
     /* Time model (planning only).  MFMA side: the busiest compute unit's
      * K-tile iterations at the tile's sustained rate for this many resident
-     * workgroups.  Memory side: algorithmic bytes plus split-K partial
-     * traffic (written, then read), at a sustained HBM rate scaled by how
-     * evenly the work is spread over the compute units. */
+     * workgroups.  Memory side: algorithmic bytes plus the split-K partial
+     * sums the main pass writes, at a sustained HBM rate scaled by how
+     * evenly the work is spread over the compute units.  The three sides
+     * overlap only in part: they combine as a 4-norm (between their sum and
+     * their maximum).  Each unit a workgroup slot runs in turn adds a fixed
+     * pipeline fill and epilogue; the combine pass reads the partial sums
+     * back after the main pass. */
     const double cu_peak = cfg.dtype_class >= 3 ? kPeakFp4PerCu : cfg.dtype_class ? kPeakFp8PerCu : kPeakBf16PerCu;
     /* workgroups actually sharing a compute unit */
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(c.b, cdiv(std::max<int64_t>(c.grid, 1), S)));
@@ -186,26 +192,26 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
             partial += (double)rows * cols * 4.0 * nsl;
         }
     }
-    const double bytes = (double)batch * ((double)(M + N) * kbytes + (double)M * N * out_esize) +
-                         2.0 * partial;
+    const double bytes = (double)batch * ((double)(M + N) * kbytes + (double)M * N * out_esize) + partial;
     const double spread = busiest_cu ? (double)total / ((double)S * busiest_cu) : 1.0;
     const double t_mem = bytes / (kHbmBytesPerSec * cfg.stream_eff * spread);
     /* the busiest unit's copies from L2 into LDS (operand panels shared by
      * several tiles are fetched once per tile) */
     const double t_copy = (double)busiest_cu * (cfg.TM + cfg.TN) * cfg.row_bytes / kCopyBytesPerSecPerCu;
-    c.t = kExtraPassSec + std::max(std::max(t_mfma, t_mem), t_copy) + (partial > 0 ? kExtraPassSec : 0.0) +
-          pack_passes * kExtraPassSec;
+    const double p4 = std::pow(t_mfma, 4.0) + std::pow(t_mem, 4.0) + std::pow(t_copy, 4.0);
+    const int64_t in_turn = cdiv(std::max<int64_t>(c.units, 1), std::min<int64_t>(std::max<int64_t>(c.grid, 1), slots));
+    c.t = kExtraPassSec + std::pow(p4, 0.25) + (double)in_turn * kUnitSec +
+          (partial > 0 ? kExtraPassSec + partial / kHbmBytesPerSec : 0.0) + (pack_passes ? kExtraPassSec : 0.0);
 }
 
-/* true if x should be preferred over y.  Modelled times within 20 % of each
- * other count as equal (the model is coarser than that: on small products
- * launch costs it only estimates dominate); among those a schedule that
- * fills the device more than 3 % better (eta_sched * eta_pad) wins, and
- * otherwise the modelled time decides. */
+/* true if x should be preferred over y.  Modelled times within 15 % of each
+ * other count as equal (the model is coarser than that); among those a
+ * schedule that fills the device more than 3 % better (eta_sched * eta_pad)
+ * wins, and otherwise the modelled time decides. */
 bool better(const Cand &x, const Cand &y)
 {
     if (y.tile < 0) return true;
-    const bool close = x.t <= y.t * 1.2 && y.t <= x.t * 1.2;
+    const bool close = x.t <= y.t * 1.15 && y.t <= x.t * 1.15;
     if (!close) return x.t < y.t;
     const double ex = rational_to_double(x.eta_sched.num, x.eta_sched.den) *
                       rational_to_double(x.eta_pad.num, x.eta_pad.den);
