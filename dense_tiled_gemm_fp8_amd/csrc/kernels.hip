@@ -1009,10 +1009,15 @@ __device__ __forceinline__ void pack_rows(const PackParams &pk, int64_t blk)
         i32x4 lo[NC], hi[NC];
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            /* offsets past the window read as zero; no test needed */
+            /* only chunks holding bytes of the row are read (a wave whose
+             * lanes are all past them issues nothing) */
             const uint32_t off = (c0 + 64u * i) * 16u;
-            lo[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-            hi[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+            lo[i] = i32x4{0, 0, 0, 0};
+            hi[i] = i32x4{0, 0, 0, 0};
+            if (off < kbytes) {
+                lo[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                hi[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+            }
         }
 #pragma unroll
         for (int i = 0; i < NC; ++i) {

@@ -202,6 +202,26 @@ def test_plan_reports_efficiency_levers(g):
         assert Fraction(p["eta_sched_num"], p["eta_sched_den"]) >= Fraction(95, 100), (M, N, K)
 
 
+def test_plan_fits_short_k_and_narrow_shapes(g):
+    """The time model charges a pipeline fill and epilogue per unit a slot
+    runs in turn, so short-K products with narrow N, which the 128x128
+    four-stage tile streams slowly, go to tiles with several resident
+    workgroups per compute unit, while the square product keeps its
+    256x256 tile."""
+    base = dict(A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
+    p = g.gemm355_plan(g.make_args(100352, 64, 256, dtype=g.BF16_BF16, **base))
+    assert (p["T_M"], p["T_N"]) == (64, 64) and p["b"] >= 2
+    p = g.gemm355_plan(g.make_args(100352, 128, 1152, dtype=g.BF16_BF16, **base))
+    assert p["T_N"] == 128 and g.gemm355_tile_info(p["tile"])["b_max"] >= 2
+    p = g.gemm355_plan(g.make_args(4096, 4096, 4096, dtype=g.BF16_BF16, **base))
+    assert (p["T_M"], p["T_N"], p["grid"], p["split"]) == (256, 256, 256, 1)
+    # a 1x1 convolution with 64 output channels: 64x64 tiles, several per CU
+    a = g.make_conv_args(32, 56, 56, 256, 64, 1, 1, x=0x10000, w=0x1000000000, y=0x200000000000,
+                         dtype=g.BF16_BF16)
+    p = g.gemm355_conv2d_plan(a)
+    assert (p["T_M"], p["T_N"]) == (64, 64) and p["b"] >= 2
+
+
 def test_repack_decisions(g):
     base = dict(A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
     assert g.gemm355_plan(g.make_args(1000, 3000, 777, **base))["repack"] == 3     # rows 2-byte aligned
