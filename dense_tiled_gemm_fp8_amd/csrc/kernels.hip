@@ -362,11 +362,14 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         const int32_t nkt = un.kt_end - un.kt_begin;
         auto ktile = [&](int32_t i) __attribute__((always_inline)) { return un.kt_begin + i; };
         /* copies of iteration i; iterations past the range read zero */
+        /* chunks of a row that belong to the K-tile (FP6: 6 of the 8; the
+         * last two would be the next K-tile's bytes and are not read) */
+        constexpr int KCH = KTB / 16;
         auto kvalid = [&](int32_t i) __attribute__((always_inline)) {
             const uint32_t kb = (uint32_t)ktile(i) * KTB;
             KV k;
-            k.v[0] = ((int32_t)(kb + lchunk[0] * 16) < p.Kb) && (i < nkt);
-            k.v[1] = TWO ? ((int32_t)(kb + lchunk[1] * 16) < p.Kb) && (i < nkt) : k.v[0];
+            k.v[0] = ((int32_t)(kb + lchunk[0] * 16) < p.Kb) && (i < nkt) && lchunk[0] < KCH;
+            k.v[1] = TWO ? ((int32_t)(kb + lchunk[1] * 16) < p.Kb) && (i < nkt) && lchunk[1] < KCH : k.v[0];
             k.tile = ((int32_t)kb < p.Kb) && (i < nkt);
             return k;
         };
@@ -435,18 +438,16 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 return *(const bf16x8 *)(row + (((CPS * ks + hi) ^ sw) * 16));
             } else if constexpr (FP6) {
                 /* 32 values (one block, 24 bytes) per lane group: bytes
-                 * 48 ks + 24 hi .. + 23 of the row, three 8-byte reads, each
-                 * inside one 16-byte chunk */
-                const int o = 48 * ks + 24 * hi;
-                uint32_t d[6];
-#pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int b = o + 8 * j;
-                    const uint2 v = *(const uint2 *)(row + (((b >> 4) ^ sw) << 4) + (b & 15));
-                    d[2 * j] = v.x;
-                    d[2 * j + 1] = v.y;
-                }
-                return i32x8{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], 0, 0};
+                 * 48 ks + 24 hi .. + 23 of the row, i.e. chunks 3 ks (all)
+                 * and 3 ks + 1 (first half) for lane group 0, chunks 3 ks + 1
+                 * (second half) and 3 ks + 2 (all) for lane group 1.  Two
+                 * whole-chunk reads per lane (its own chunk and the shared
+                 * middle one) keep the 8-row read groups of the swizzle free
+                 * of bank conflicts, which 8-byte reads of 16 rows are not. */
+                const i32x4 f = *(const i32x4 *)(row + (((3 * ks + 2 * hi) ^ sw) << 4));
+                const i32x4 m = *(const i32x4 *)(row + (((3 * ks + 1) ^ sw) << 4));
+                return hi ? i32x8{m[2], m[3], f[0], f[1], f[2], f[3], 0, 0}
+                          : i32x8{f[0], f[1], f[2], f[3], m[0], m[1], 0, 0};
             } else if constexpr (FP4) {
                 /* 32 values (one block) per lane in the low four dwords */
                 const i32x4 v = *(const i32x4 *)(row + (((CPS * ks + hi) ^ sw) * 16));
