@@ -106,6 +106,9 @@ struct Cand {
     Frac eta_sched{0, 1};
     Frac eta_pad{0, 1};
     double t = 0;
+    /* inputs of t (reported with the plan) */
+    double mfma_peak_s = 0, mfma_eff = 0, bytes = 0, spread = 1, stream_eff = 0, copy_s = 0, fixed_s = 0;
+    int64_t in_turn = 0;
 };
 
 /* Work (K-tile iterations) of a unit queue: total, the busiest workgroup's
@@ -200,8 +203,17 @@ void finish_candidate(Cand &c, const TileCfg &cfg, int32_t S, int64_t M, int64_t
     const double t_copy = (double)busiest_cu * (cfg.TM + cfg.TN) * cfg.row_bytes / kCopyBytesPerSecPerCu;
     const double p4 = std::pow(t_mfma, 4.0) + std::pow(t_mem, 4.0) + std::pow(t_copy, 4.0);
     const int64_t in_turn = cdiv(std::max<int64_t>(c.units, 1), std::min<int64_t>(std::max<int64_t>(c.grid, 1), slots));
-    c.t = kExtraPassSec + std::pow(p4, 0.25) + (double)in_turn * kUnitSec +
-          (partial > 0 ? kExtraPassSec + partial / kHbmBytesPerSec : 0.0) + (pack_passes ? kExtraPassSec : 0.0);
+    const double fixed = kExtraPassSec + (partial > 0 ? kExtraPassSec + partial / kHbmBytesPerSec : 0.0) +
+                         (pack_passes ? kExtraPassSec : 0.0);
+    c.t = fixed + std::pow(p4, 0.25) + (double)in_turn * kUnitSec;
+    c.mfma_peak_s = (double)busiest_cu * 2.0 * cfg.TM * cfg.TN * cfg.TK / cu_peak;
+    c.mfma_eff = eff;
+    c.bytes = bytes;
+    c.spread = spread;
+    c.stream_eff = cfg.stream_eff;
+    c.copy_s = t_copy;
+    c.fixed_s = fixed;
+    c.in_turn = in_turn;
 }
 
 /* true if x should be preferred over y.  Modelled times within 15 % of each
@@ -502,6 +514,14 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
     gemm355_plan_t &o = P.pub;
     o.tile = best.tile;
     o.model_seconds = best.t;
+    o.model_mfma_peak_seconds = best.mfma_peak_s;
+    o.model_mfma_eff = best.mfma_eff;
+    o.model_bytes = best.bytes;
+    o.model_spread = best.spread;
+    o.model_stream_eff = best.stream_eff;
+    o.model_copy_seconds = best.copy_s;
+    o.model_fixed_seconds = best.fixed_s;
+    o.model_units_in_turn = best.in_turn;
     o.T_M = cfg.TM;
     o.T_N = cfg.TN;
     o.T_K = cfg.TK;

@@ -67,6 +67,10 @@ class gemm355_plan_t(ctypes.Structure):
         ("eta_sched_num", _i64), ("eta_sched_den", _i64),
         ("workspace_bytes", _sz),
         ("model_seconds", ctypes.c_double),
+        ("model_mfma_peak_seconds", ctypes.c_double), ("model_mfma_eff", ctypes.c_double),
+        ("model_bytes", ctypes.c_double), ("model_spread", ctypes.c_double),
+        ("model_stream_eff", ctypes.c_double), ("model_copy_seconds", ctypes.c_double),
+        ("model_fixed_seconds", ctypes.c_double), ("model_units_in_turn", _i64),
     ]
 
 

@@ -199,6 +199,23 @@ typedef struct gemm355_plan_t {
     size_t workspace_bytes;       /* scratch this call needs               */
     double model_seconds;         /* the planner's time estimate (planning
                                      model only, not a measurement)        */
+    /* The estimate's inputs for this schedule, so that a calibration can
+     * refit the tile priors from timed plans:
+     *   model_seconds = model_fixed_seconds
+     *     + (t_mfma^4 + t_mem^4 + t_copy^4)^(1/4)
+     *     + model_units_in_turn * (the per-unit fill and epilogue time),
+     *   t_mfma = model_mfma_peak_seconds / model_mfma_eff,
+     *   t_mem  = model_bytes / (5e12 * model_stream_eff * model_spread),
+     *   t_copy = model_copy_seconds. */
+    double model_mfma_peak_seconds; /* busiest CU's MFMA work at the dense
+                                       peak of the input class           */
+    double model_mfma_eff;        /* tile prior for the resident groups    */
+    double model_bytes;           /* algorithmic bytes + partial-sum writes */
+    double model_spread;          /* all work / (S x busiest CU's work)    */
+    double model_stream_eff;      /* tile prior                            */
+    double model_copy_seconds;    /* busiest CU's L2 -> LDS copies         */
+    double model_fixed_seconds;   /* launches and the combine read-back    */
+    int64_t model_units_in_turn;  /* units one workgroup slot runs in turn */
 } gemm355_plan_t;
 
 /*

@@ -137,10 +137,14 @@ def test_power_of_two_scales_exact():
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
-def test_all_layouts(fmt):
+@pytest.mark.parametrize("K", [136, 137])
+def test_all_layouts(fmt, K):
     """Every storage layout (repacked on the device) against the oracle, and
-    the transpose identity (A B)^T = B^T A^T through the layout flags."""
-    M, N, K = 150, 98, 136
+    the transpose identity (A B)^T = B^T A^T through the layout flags.  With
+    K = 137 the K-contiguous operand's rows are not whole 16-byte chunks, so
+    one repack launch moves one operand by rows and the other by transposed
+    blocks."""
+    M, N = 150, 98
     ops = ops_from(M, N, K, fmt, 17, dist="normal")
     a_log = ops.A                       # M x K logical
     b_log = np.ascontiguousarray(ops.B.T)  # K x N logical
