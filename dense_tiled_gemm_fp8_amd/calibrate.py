@@ -1,7 +1,7 @@
 """Refit the planner's tile priors from timed forced plans on this device.
 
     python -m dense_tiled_gemm_fp8_amd.calibrate sweep OUT.json [--groups bf16,e4m3,conv]
-    python -m dense_tiled_gemm_fp8_amd.calibrate fit OUT.json
+    python -m dense_tiled_gemm_fp8_amd.calibrate fit OUT.json [--per-tile]
 
 sweep (GPU): for each calibration shape of a group, every tile of the group,
 one-shot and persistent, timed with HIP events around a sustained loop.
@@ -13,7 +13,9 @@ inputs of its time estimate (gemm355_plan_t.model_*).
 fit (CPU): per tile a new stream_eff, per group one scale of the mfma_eff
 priors and one per-unit fill and epilogue time, minimising the squared log
 error of the planning model against the timings, weighted toward plans
-within 30 % of their shape's best.  It prints the refitted priors (to be
+within 30 % of their shape's best (--per-tile: one mfma_eff scale per tile;
+more parameters than the sweep pins down, so the picks it gives are not
+better overall).  It prints the refitted priors (to be
 written into csrc/tiles.h, and the per-unit time into csrc/plan.hip) and,
 per shape, the measured time of the model's pick among the timed plans over
 the best timed plan, with the current and with the refitted priors.
@@ -150,9 +152,10 @@ def predict(r, f_mfma, stream_eff, unit_s):
     return r["model_fixed_seconds"] + (t_m ** 4 + t_b ** 4 + t_c ** 4) ** 0.25 + r["model_units_in_turn"] * unit_s
 
 
-def fit_group(recs, cap=2.5, sweeps=8):
-    """Coordinate descent on grids: per tile stream_eff, one mfma scale, one
-    per-unit time.  Returns (f_mfma, {tile: stream_eff}, unit_s, rms)."""
+def fit_group(recs, cap=2.5, sweeps=8, per_tile=False):
+    """Coordinate descent on grids: per tile stream_eff, one mfma scale (per
+    tile too with per_tile), one per-unit time.  Returns (f_mfma, {tile:
+    stream_eff}, unit_s, rms); f_mfma is a {tile: scale} dict with per_tile."""
     best = {}
     for r in recs:
         k = tuple(r["shape"])
@@ -163,14 +166,14 @@ def fit_group(recs, cap=2.5, sweeps=8):
         s = n = 0.0
         for i in (range(len(recs)) if idx is None else idx):
             r = recs[i]
-            e = math.log(predict(r, fm, fs[r["tile"]], u) / r["seconds"])
+            e = math.log(predict(r, fm[r["tile"]] if per_tile else fm, fs[r["tile"]], u) / r["seconds"])
             s += w[i] * e * e
             n += w[i]
         return s / max(n, 1e-30)
 
     tiles = sorted(set(r["tile"] for r in recs))
     by_tile = {t: [i for i, r in enumerate(recs) if r["tile"] == t] for t in tiles}
-    fm, u = 1.0, 3e-6
+    fm, u = ({t: 1.0 for t in tiles} if per_tile else 1.0), 3e-6
     fs = {t: recs[by_tile[t][0]]["model_stream_eff"] for t in tiles}
     grid_s = [x / 100 for x in range(20, int(cap * 100) + 1, 2)]
     grid_m = [x / 100 for x in range(20, 161, 2)]
@@ -178,7 +181,10 @@ def fit_group(recs, cap=2.5, sweeps=8):
     for _ in range(sweeps):
         for t in tiles:
             fs[t] = min(grid_s, key=lambda a: loss(fm, {**fs, t: a}, u, by_tile[t]))
-        fm = min(grid_m, key=lambda a: loss(a, fs, u))
+            if per_tile:
+                fm[t] = min(grid_m, key=lambda a: loss({**fm, t: a}, fs, u, by_tile[t]))
+        if not per_tile:
+            fm = min(grid_m, key=lambda a: loss(a, fs, u))
         u = min(grid_u, key=lambda a: loss(fm, fs, a))
     return fm, fs, u, math.sqrt(loss(fm, fs, u))
 
@@ -192,23 +198,25 @@ def picks(recs, fm=1.0, fs=None, u=None):
         if fs is None:
             pick = min(rs, key=lambda r: r["model_seconds"])
         else:
-            pick = min(rs, key=lambda r: predict(r, fm, fs[r["tile"]], u))
+            pick = min(rs, key=lambda r: predict(r, fm[r["tile"]] if isinstance(fm, dict) else fm, fs[r["tile"]], u))
         out[k] = pick["seconds"] / min(r["seconds"] for r in rs)
     return out
 
 
-def fit(path):
+def fit(path, per_tile=False):
     recs = json.load(open(path))
     for group in GROUPS:
         rs = [r for r in recs if r["group"] == group]
         if not rs:
             continue
-        fm, fs, u, rms = fit_group(rs)
-        print("%s: %d timed plans, rms log error %.3f, mfma_eff scale %.2f, per-unit time %.1f us"
-              % (group, len(rs), rms, fm, u * 1e6))
+        fm, fs, u, rms = fit_group(rs, per_tile=per_tile)
+        scale = (lambda t: fm[t]) if per_tile else (lambda t: fm)
+        print("%s: %d timed plans, rms log error %.3f, %s, per-unit time %.1f us"
+              % (group, len(rs), rms, "per-tile mfma_eff scales" if per_tile else "mfma_eff scale %.2f" % fm,
+                 u * 1e6))
         for t in sorted(fs):
             old = next(r["model_stream_eff"] for r in rs if r["tile"] == t)
-            print("  tile %2d: stream_eff %.2f -> %.2f, mfma_eff x %.2f" % (t, old, fs[t], fm))
+            print("  tile %2d: stream_eff %.2f -> %.2f, mfma_eff x %.2f" % (t, old, fs[t], scale(t)))
         before, after = picks(rs), picks(rs, fm, fs, u)
         for k in before:
             print("  %-32s model's pick / best: %.2f -> %.2f" % ("x".join(map(str, k)), before[k], after[k]))
@@ -224,11 +232,12 @@ def main(argv=None):
     s.add_argument("--groups", default=",".join(GROUPS))
     f = sub.add_parser("fit")
     f.add_argument("path")
+    f.add_argument("--per-tile", action="store_true", help="one mfma_eff scale per tile")
     a = ap.parse_args(argv)
     if a.cmd == "sweep":
         sweep(a.out, [x for x in a.groups.split(",") if x])
     else:
-        fit(a.path)
+        fit(a.path, a.per_tile)
     return 0
 
 
