@@ -126,6 +126,33 @@ def test_exact_bf16_output(fmt):
         assert np.array_equal(C, ref), knobs
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_bf16_output_every_tile(fmt):
+    """bf16 C from every product tile, exact integers, with an odd N and a
+    leading dimension of N or N + 1: the padding column beyond N stays
+    untouched."""
+    M, N, K = 130, 99, 64
+    ops = int_ops(M, N, K, fmt, 23, lo=-2, hi=2)
+    ref, _ = H.oracle_full(ops, alpha=1.0)
+    assert np.abs(ref).max() <= 256
+    A, B = H.dev(ops.A), H.dev(ops.B)
+    sa = sb = None
+    if fmt != "bf16":
+        sa = torch.tensor(ops.scale_a, dtype=torch.float32, device="cuda")
+        sb = torch.tensor(ops.scale_b, dtype=torch.float32, device="cuda")
+    for ldc in (N, N + 1):
+        for t in (BF16_TILES if fmt == "bf16" else E4M3_TILES):
+            H.say(fmt, "bf16 C, tile", t, "ldc", ldc)
+            C = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+            args = g.make_args(M, N, K, A=A, B=B, C=C, ldc=ldc, dtype=H.out_dtype(fmt, "bf16"), tile=t,
+                               scale_a=sa, scale_b=sb)
+            g.gemm355_gemm_ex(args)
+            torch.cuda.synchronize()
+            got = C.float().cpu().numpy().astype(np.float64)
+            assert np.array_equal(got[:, :N], ref), (t, ldc)
+            assert np.isnan(got[:, N:]).all(), (t, ldc)
+
+
 def test_power_of_two_scales_exact():
     M, N, K = 128, 192, 256
     ops = int_ops(M, N, K, "e4m3", 13)
