@@ -395,7 +395,7 @@ def conv_layers(torch, g, inputs, args):
     out = []
     for (N, Hh, W, C, K, R, S, pad) in layers:
         log("bench: detail convolution", (N, Hh, W, C, K, R, S, pad))
-        P, Q = g.conv_out_size(Hh, W, R, S, pad, pad)
+        P, Q = g.gemm355_conv2d_out_size(g.make_conv_args(N, Hh, W, C, K, R, S, pad_h=pad, pad_w=pad))
         M, Kg = N * P * Q, R * S * C
         flops = 2.0 * M * K * Kg
         gen = np.random.Generator(np.random.PCG64(7000 + C + K + R))

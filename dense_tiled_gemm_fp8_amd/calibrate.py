@@ -94,7 +94,7 @@ def sweep(out_path, groups):
         for shape in SHAPES[group]:
             if group == "conv":
                 N, H, W, C, K, R, S, pad = shape
-                P, Q = g.conv_out_size(H, W, R, S, pad, pad)
+                P, Q = g.gemm355_conv2d_out_size(g.make_conv_args(N, H, W, C, K, R, S, pad_h=pad, pad_w=pad))
                 x = torch.randn(N, H, W, C, device="cuda").bfloat16()
                 w = torch.randn(K, R, S, C, device="cuda").bfloat16()
                 y = torch.empty(N, P, Q, K, device="cuda", dtype=torch.bfloat16)

@@ -5,8 +5,9 @@
  * shape), then enqueues on the caller's stream: optional operand repacks,
  * the main MFMA kernel over the plan's work units, and for split-K (or a
  * split tail of a persistent grid) the combine kernel.  Nothing here blocks
- * the host except the first use of a device (property query) and the growth
- * of library-owned scratch.
+ * the host except the first use of a device (property query), the growth
+ * of library-owned scratch, and waiting for another thread that is
+ * enqueueing on the same stream with that stream's scratch.
  */
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -14,7 +15,9 @@
 
 #include <algorithm>
 #include <map>
+#include <memory>
 #include <mutex>
+#include <thread>
 #include <tuple>
 #include <unordered_map>
 
@@ -129,36 +132,65 @@ gemm355_status get_plan(const gemm355_args &a, Plan &out, const ConvShape *conv 
     return GEMM355_OK;
 }
 
-/* Library-owned scratch, one buffer per (device, stream), grown on demand. */
+/* Library-owned scratch, one buffer per (device, stream), grown on demand.
+ *
+ * A call that uses the buffer holds its lock from the lookup until its last
+ * kernel is enqueued.  Calls on one stream therefore enqueue their kernels
+ * as whole groups, never interleaved (one call's main pass cannot overwrite
+ * partial sums another call's combine pass has yet to read), and the stream
+ * runs the groups in enqueue order.  A buffer is replaced (after the stream
+ * has drained the work of earlier calls) only by a call holding the lock,
+ * so no call can be handed a buffer that is then freed under it.  The
+ * per-thread default stream is one handle for many streams, so its buffers
+ * are kept per thread as well. */
 struct Scratch {
+    std::mutex mu;
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-std::map<std::pair<int, void *>, Scratch> g_scratch;
+struct ScratchKey {
+    int dev;
+    void *stream;
+    std::thread::id thread;
+    bool operator<(const ScratchKey &o) const
+    {
+        return std::tie(dev, stream, thread) < std::tie(o.dev, o.stream, o.thread);
+    }
+};
+std::map<ScratchKey, std::unique_ptr<Scratch>> g_scratch;
 
-gemm355_status library_scratch(size_t need, void *stream, void **out)
+gemm355_status library_scratch(size_t need, void *stream, void **out, std::unique_lock<std::mutex> &hold)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GEMM355_EHIP;
-    std::lock_guard<std::mutex> lk(g_mu);
-    Scratch &s = g_scratch[{dev, stream}];
-    if (s.bytes < need) {
-        if (s.ptr) {
+    Scratch *s;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        const ScratchKey key{dev, stream,
+                             (hipStream_t)stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+        std::unique_ptr<Scratch> &slot = g_scratch[key];
+        if (!slot) slot.reset(new Scratch);
+        s = slot.get();
+    }
+    /* entries are never erased before unload, so s stays valid */
+    hold = std::unique_lock<std::mutex>(s->mu);
+    if (s->bytes < need) {
+        if (s->ptr) {
             /* earlier calls on this stream may still read the old buffer */
             if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GEMM355_EHIP;
-            (void)hipFree(s.ptr);
-            s.ptr = nullptr;
-            s.bytes = 0;
+            (void)hipFree(s->ptr);
+            s->ptr = nullptr;
+            s->bytes = 0;
         }
         size_t grow = need + need / 4;
-        if (hipMalloc(&s.ptr, grow) != hipSuccess) {
+        if (hipMalloc(&s->ptr, grow) != hipSuccess) {
             (void)hipGetLastError();
-            s.ptr = nullptr;
+            s->ptr = nullptr;
             return GEMM355_ENOMEM;
         }
-        s.bytes = grow;
+        s->bytes = grow;
     }
-    *out = s.ptr;
+    *out = s->ptr;
     return GEMM355_OK;
 }
 
@@ -166,7 +198,7 @@ struct ScratchReaper {
     ~ScratchReaper()
     {
         for (auto &kv : g_scratch)
-            if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+            if (kv.second && kv.second->ptr) (void)hipFree(kv.second->ptr);
     }
 } g_reaper;
 
@@ -186,6 +218,8 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
     }
 
     uint8_t *ws = nullptr;
+    /* held until this call's last launch is enqueued (library scratch) */
+    std::unique_lock<std::mutex> hold;
     if (P.pub.workspace_bytes) {
         if (a.workspace) {
             if (a.workspace_bytes < P.pub.workspace_bytes) return GEMM355_ENOMEM;
@@ -193,7 +227,7 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
             ws = (uint8_t *)a.workspace;
         } else {
             void *p = nullptr;
-            st = library_scratch(P.pub.workspace_bytes, stream, &p);
+            st = library_scratch(P.pub.workspace_bytes, stream, &p, hold);
             if (st != GEMM355_OK) return st;
             ws = (uint8_t *)p;
         }
@@ -402,6 +436,18 @@ gemm355_status gemm355_conv2d_plan(const gemm355_conv_args *args, gemm355_plan_t
     return GEMM355_OK;
 }
 
+gemm355_status gemm355_conv2d_out_size(const gemm355_conv_args *args, int64_t *P, int64_t *Q)
+{
+    if (!P || !Q) return GEMM355_EINVAL;
+    gemm355_args a;
+    ConvShape cs;
+    const gemm355_status st = conv_setup(args, a, cs);
+    if (st != GEMM355_OK) return st;
+    *P = cs.P;
+    *Q = cs.Q;
+    return GEMM355_OK;
+}
+
 gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                             const void *B, int64_t ldb, void *C, int64_t ldc, gemm355_dtype dtype,
                             gemm355_layout layout, int32_t split_k, int32_t persistent,
@@ -569,7 +615,8 @@ gemm355_status gemm355_quantize(const void *x, int64_t n, int64_t batch, gemm355
     if (total > 0 && (overlap(x0, x1, q0, q1) || overlap(x0, x1, s0, s1) || overlap(q0, q1, s0, s1)))
         return GEMM355_EINVAL;
     void *scr = nullptr;
-    gemm355_status st = library_scratch((size_t)(batch * parts) * sizeof(float), stream, &scr);
+    std::unique_lock<std::mutex> hold;
+    gemm355_status st = library_scratch((size_t)(batch * parts) * sizeof(float), stream, &scr, hold);
     if (st != GEMM355_OK) return st;
     QuantParams qp;
     qp.x = x;

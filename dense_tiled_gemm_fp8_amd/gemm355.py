@@ -114,13 +114,16 @@ _lib.gemm355_conv2d.restype = ctypes.c_int
 _lib.gemm355_conv2d.argtypes = [ctypes.POINTER(gemm355_conv_args), _vp]
 _lib.gemm355_conv2d_plan.restype = ctypes.c_int
 _lib.gemm355_conv2d_plan.argtypes = [ctypes.POINTER(gemm355_conv_args), ctypes.POINTER(gemm355_plan_t)]
+_lib.gemm355_conv2d_out_size.restype = ctypes.c_int
+_lib.gemm355_conv2d_out_size.argtypes = [ctypes.POINTER(gemm355_conv_args), ctypes.POINTER(_i64),
+                                         ctypes.POINTER(_i64)]
 _lib.gemm355_status_string.restype = ctypes.c_char_p
 _lib.gemm355_status_string.argtypes = [ctypes.c_int]
 
 EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_plan", "gemm355_eta_wave",
             "gemm355_eta_pad", "gemm355_kslice", "gemm355_unit", "gemm355_num_tiles",
             "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_quantize",
-            "gemm355_conv2d", "gemm355_conv2d_plan", "gemm355_status_string")
+            "gemm355_conv2d", "gemm355_conv2d_plan", "gemm355_conv2d_out_size", "gemm355_status_string")
 
 
 class Gemm355Error(RuntimeError):
@@ -231,12 +234,6 @@ def gemm355_tile_occupancy(tile: int) -> int:
     return n.value
 
 
-def conv_out_size(H, W, R, S, pad_h=0, pad_w=0, stride_h=1, stride_w=1, dil_h=1, dil_w=1):
-    """(P, Q) of a convolution, as the library computes them."""
-    return ((H + 2 * pad_h - dil_h * (R - 1) - 1) // stride_h + 1,
-            (W + 2 * pad_w - dil_w * (S - 1) - 1) // stride_w + 1)
-
-
 def make_conv_args(N, H, W, C, K, R, S, x=None, w=None, y=None, pad_h=0, pad_w=0, stride_h=1,
                    stride_w=1, dil_h=1, dil_w=1, dtype=BF16_F32, split_k=0, persistent=-1, tile=-1,
                    cus=0, workspace=None, workspace_bytes=0) -> gemm355_conv_args:
@@ -247,6 +244,14 @@ def make_conv_args(N, H, W, C, K, R, S, x=None, w=None, y=None, pad_h=0, pad_w=0
 
 def gemm355_conv2d(args: gemm355_conv_args, stream=None) -> None:
     _check(_lib.gemm355_conv2d(ctypes.byref(args), _stream(stream)), "gemm355_conv2d")
+
+
+def gemm355_conv2d_out_size(args: gemm355_conv_args):
+    """(P, Q): the output extent the library gives this convolution."""
+    P, Q = _i64(), _i64()
+    _check(_lib.gemm355_conv2d_out_size(ctypes.byref(args) if args is not None else None, ctypes.byref(P),
+                                        ctypes.byref(Q)), "gemm355_conv2d_out_size")
+    return P.value, Q.value
 
 
 def gemm355_conv2d_plan(args: gemm355_conv_args) -> Dict[str, int]:

@@ -23,7 +23,12 @@
  *     stream).  Argument errors are reported before anything is launched;
  *     faults inside kernels surface at the caller's next synchronisation.
  *   - No entry point aborts, prints or throws; each returns a status code.
- *   - All entry points are thread-safe.
+ *   - All entry points are thread-safe.  Scratch the library owns is kept
+ *     per device and stream; a call holds that buffer from its lookup until
+ *     its last kernel is enqueued, so concurrent calls on one stream enqueue
+ *     their kernels call by call and never share partial sums.  A
+ *     caller-provided workspace belongs to the caller: calls that may run
+ *     at the same time (on different streams) need different workspaces.
  */
 #ifndef GEMM355_H
 #define GEMM355_H
@@ -256,7 +261,17 @@ GEMM355_API gemm355_status gemm355_gemm_ex(const gemm355_args *args, void *strea
 /*
  * gemm355_plan -- what gemm355_gemm_ex would do with `args` (pointers are
  * only inspected for alignment, never dereferenced).  Pure host arithmetic;
- * needs no device when args->cus > 0.
+ * needs no device when args->cus > 0.  The fields are the quantities of
+ * page "10. Tensor Cores, shapes, and tile alignment": the tile grid G and
+ * wave efficiency (section "Shape the operation", the tile-count and
+ * wave-efficiency equations), the padded sizes and padding efficiency
+ * (section "Padding efficiency"), the split-K factor and the persistent grid
+ * (section "When shape alone can't fix wave efficiency"), and the resident
+ * workgroups per compute unit b (page "Grid 24 is not headroom", section
+ * "The question I never asked": residency is the minimum over shared memory
+ * and registers).
+ * Errors: EINVAL / EALIGN / EUNSUPPORTED as gemm355_gemm_ex would return
+ * them; EHIP only when args->cus == 0 and the device query fails.
  */
 GEMM355_API gemm355_status gemm355_plan(const gemm355_args *args, gemm355_plan_t *out);
 
@@ -278,27 +293,46 @@ GEMM355_API double gemm355_eta_pad(int64_t M, int64_t N, int64_t K,
 
 /*
  * K-tile range [*begin, *end) of split-K slice i when nK K-tiles are cut into
- * s slices: begin = floor(i*nK/s), end = floor((i+1)*nK/s).
- * EINVAL unless nK >= 0, s >= 1 and 0 <= i < s.
+ * s slices: begin = floor(i*nK/s), end = floor((i+1)*nK/s).  Split-K cuts
+ * the K loop of every tile into slices whose partial sums go to a separate
+ * buffer and are combined afterwards (page "10. Tensor Cores, shapes, and
+ * tile alignment", section "When shape alone can't fix wave efficiency");
+ * the page does not say where the cuts fall, and this even partition (slice
+ * sizes differ by at most one K-tile) is the library's reading.
+ * begin and end are host pointers, written on success.
+ * EINVAL unless nK >= 0, s >= 1, 0 <= i < s and both pointers are non-NULL.
  */
 GEMM355_API gemm355_status gemm355_kslice(int64_t nK, int32_t s, int32_t i,
                               int64_t *begin, int64_t *end);
 
 /*
  * Work unit u of a plan, decoded by the same function the kernels use:
- * batch entry, tile row and column, and K-tile range.  EINVAL if u is out of
- * range.  (Host-side view of the persistent tile queue, for inspection.)
+ * batch entry, tile row and column, and K-tile range (host pointers, written
+ * on success).  The persistent grid of page "10. Tensor Cores, shapes, and
+ * tile alignment" (section "When shape alone can't fix wave efficiency")
+ * loops its workgroups over such a queue: workgroup w takes units w, w + P,
+ * w + 2P, ... of a grid of P.  Errors: those of gemm355_plan, and EINVAL if
+ * u is out of range or an output pointer is NULL.  (Host-side view of the
+ * tile queue, for inspection and tests.)
  */
 GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
                             int64_t *batch, int64_t *tile_m, int64_t *tile_n,
                             int64_t *kt_begin, int64_t *kt_end);
 
-/* Number of entries in the tile table, and one entry's parameters.
- * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2), 2 = block-scaled
- * 8-bit inputs (the MX 8-bit dtypes), 3 = block-scaled FP4 inputs, 4 =
- * block-scaled FP6 inputs; T_K counts
- * elements; b_max: resident workgroups per compute unit; op: 0 matrix
- * product, 1 convolution (gemm355_conv2d).  Null outputs are skipped. */
+/* Number of entries in the tile table, and one entry's parameters: the
+ * tile shape T_M x T_N x T_K of the tile-count and padding equations (page
+ * "10. Tensor Cores, shapes, and tile alignment", sections "Shape the
+ * operation" and "Padding efficiency") and the on-chip resources that fix
+ * how many workgroups a compute unit holds (page "Grid 24 is not headroom",
+ * section "The question I never asked").
+ * dtype_class: 0 = bf16 inputs, 1 = 8-bit inputs (E4M3 and/or E5M2), 2 =
+ * block-scaled 8-bit inputs (the MX 8-bit dtypes), 3 = block-scaled FP4
+ * inputs, 4 = block-scaled FP6 inputs; T_K counts elements; stages: LDS
+ * ring depth; waves: wavefronts per workgroup; lds_bytes: LDS per
+ * workgroup; b_max: resident workgroups per compute unit from the LDS,
+ * register and wavefront-slot limits; op: 0 matrix product, 1 convolution
+ * (gemm355_conv2d).  Outputs are host pointers; NULL ones are skipped.
+ * EINVAL if tile is not in [0, gemm355_num_tiles()). */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
                                  int32_t *T_M, int32_t *T_N, int32_t *T_K,
@@ -308,8 +342,11 @@ GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
 /* Workgroups of a tile's main-loop kernel that fit on one compute unit of
  * the current device, as the HIP runtime reports it
  * (hipOccupancyMaxActiveBlocksPerMultiprocessor at the tile's workgroup
- * size: 64 threads per wavefront).  Needs a
- * device; EHIP otherwise. */
+ * size: 64 threads per wavefront): the runtime's side of the residency
+ * arithmetic of page "Grid 24 is not headroom", section "The question I
+ * never asked", against which b_max of gemm355_tile_info is checked.
+ * *blocks_per_cu is a host pointer.  EINVAL for an unknown tile or a NULL
+ * pointer; needs a device, EHIP otherwise. */
 GEMM355_API gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu);
 
 /*
@@ -384,6 +421,15 @@ GEMM355_API gemm355_status gemm355_conv2d(const gemm355_conv_args *args, void *s
 
 /* The plan of that product (P and Q follow from the arguments). */
 GEMM355_API gemm355_status gemm355_conv2d_plan(const gemm355_conv_args *args, gemm355_plan_t *out);
+
+/* Output extent of that convolution: *P = (H + 2 pad_h - dil_h (R - 1) - 1)
+ * / stride_h + 1 and *Q likewise along W (the window positions that fit in
+ * the padded image), as gemm355_conv2d uses them to size y.  Host
+ * arithmetic only; x, w and y are not inspected.  P and Q are host
+ * pointers, written on success.  Errors: EINVAL / EUNSUPPORTED for the
+ * shape arguments exactly as gemm355_conv2d reports them, EINVAL for NULL
+ * pointers. */
+GEMM355_API gemm355_status gemm355_conv2d_out_size(const gemm355_conv_args *args, int64_t *P, int64_t *Q);
 
 /* Static description of a status code. */
 GEMM355_API const char *gemm355_status_string(gemm355_status status);

@@ -55,7 +55,7 @@ def empty_c(batch: int, M: int, N: int, out: str, fill: float = float("nan")) ->
 
 def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: int = -1,
         tile: int = -1, layout: int = g.A_ROW_B_COL, A_dev=None, B_dev=None, lda=None, ldb=None,
-        scales: bool = True, workspace=None, C=None) -> np.ndarray:
+        scales: bool = True, workspace=None, C=None, cus: int = 0) -> np.ndarray:
     """Run one (batched) product on the device in the storage convention of
     the inputs module (A row-major M x K, B column-major given as N x K)."""
     M, N, K, batch = ops.M, ops.N, ops.K, ops.batch
@@ -74,7 +74,7 @@ def run(ops: inputs.Operands, out: str = "f32", split_k: int = 0, persistent: in
     args = g.make_args(M, N, K, A=A_dev, lda=lda, B=B_dev, ldb=ldb, C=C, dtype=out_dtype(ops.fmt, out),
                        layout=layout, batch=batch, stride_a=M * K, stride_b=N * K, stride_c=M * N,
                        scale_a=sa, scale_b=sb, split_k=split_k, persistent=persistent, tile=tile,
-                       block_scale_a=bsa, block_scale_b=bsb)
+                       block_scale_a=bsa, block_scale_b=bsb, cus=cus)
     if workspace == "caller":
         p = g.gemm355_plan(args)
         if p["workspace_bytes"]:
@@ -151,3 +151,59 @@ def sample_positions(M: int, N: int, n: int, seed: int):
     rows += list(range(M - edge, M))
     cols += [N - 1] * edge
     return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+# operand formats of each input class of the tile table
+CLASS_FMTS = {0: ("bf16",), 1: ("e4m3", "e5m2", "e4m3e5m2"), 2: ("mxe4m3", "mxe5m2", "mxe4m3e5m2"),
+              3: ("mxfp4",), 4: ("mxfp6e2m3", "mxfp6e3m2")}
+
+
+def elem_formats(fmt: str):
+    """(A's, B's) element format names of a dtype name."""
+    if fmt == "bf16":
+        return "bf16", "bf16"
+    if fmt.startswith("mxfp6"):
+        return fmt[5:], fmt[5:]
+    if fmt == "mxfp4":
+        return "e2m1", "e2m1"
+    base = fmt[2:] if fmt.startswith("mx") else fmt
+    if base == "e4m3e5m2":
+        return "e4m3", "e5m2"
+    return base, base
+
+
+def exact_ops(M: int, N: int, K: int, fmt: str, seed: int, batch: int = 0, lo: int = -1, hi: int = 1,
+              scale_lo: int = 125, scale_hi: int = 129) -> inputs.Operands:
+    """Integer elements in [lo, hi] in any input format; block-scaled formats
+    get E8M0 scales in [scale_lo, scale_hi] (2^-2 .. 2^2 by default).  With
+    |products| <= 2^4 and K * 2^4 * max|a b| below 2^20, every partial sum
+    is a multiple of 2^-4 below 2^24 in magnitude, i.e. exact in binary32 in
+    any summation order."""
+    ga, gb = inputs.rng(seed), inputs.rng(seed + 1)
+    fa, fb = elem_formats(fmt)
+    nb = max(batch, 1)
+    A = np.stack([inputs.small_int_codes(ga, (M, K), fa, lo, hi) for _ in range(nb)])
+    B = np.stack([inputs.small_int_codes(gb, (N, K), fb, lo, hi) for _ in range(nb)])
+    sa = sb = None
+    if fmt.startswith("mx"):
+        sa = np.stack([ga.integers(scale_lo, scale_hi + 1, size=(M, K // 32)).astype(np.uint8)
+                       for _ in range(nb)])
+        sb = np.stack([gb.integers(scale_lo, scale_hi + 1, size=(N, K // 32)).astype(np.uint8)
+                       for _ in range(nb)])
+    if not batch:
+        A, B = A[0], B[0]
+        if sa is not None:
+            sa, sb = sa[0], sb[0]
+    return inputs.Operands(M, N, K, fmt, A, B, [1.0] * nb, [1.0] * nb, (seed, seed + 1), sa, sb)
+
+
+def split_tail_cus(args_kw: dict, limit: int = 16):
+    """The smallest planning CU count (1 .. limit) whose persistent plan for
+    these arguments splits a partial last round along K while some
+    workgroup runs more than one unit; None if there is none."""
+    for cus in range(1, limit + 1):
+        a = g.make_args(**dict(args_kw, cus=cus, persistent=1, split_k=1))
+        p = g.gemm355_plan(a)
+        if p["tail_tiles"] > 0 and p["units"] > p["grid"] and p["units"] - p["tail_tiles"] * p["tail_split"] > 0:
+            return cus
+    return None

@@ -17,6 +17,7 @@ from fractions import Fraction
 import pytest
 
 from oracle import bookkeeping as bk
+from oracle import conv as oc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -38,6 +39,28 @@ def test_header_symbols_exported(g):
     assert declared == set(g.EXPORTED)
     for name in declared:
         assert hasattr(g._lib, name), name
+
+
+def test_binding_holds_no_method_arithmetic():
+    """The Python binding only marshals arguments: no function in it does
+    arithmetic (sizes, offsets, output extents all come from the library).
+    The only binary operators allowed are %-formatting of message strings."""
+    import ast
+    path = os.path.join(ROOT, "dense_tiled_gemm_fp8_amd", "gemm355.py")
+    tree = ast.parse(open(path).read())
+    bad = []
+    for fn in [n for n in ast.walk(tree) if isinstance(n, (ast.FunctionDef, ast.AsyncFunctionDef))]:
+        for node in [n for stmt in fn.body for n in ast.walk(stmt)]:
+            if isinstance(node, ast.AugAssign):
+                bad.append((fn.name, node.lineno))
+            elif isinstance(node, ast.BinOp):
+                if isinstance(node.op, ast.Mod) and isinstance(node.left, ast.Constant) and \
+                        isinstance(node.left.value, str):
+                    continue
+                bad.append((fn.name, node.lineno))
+            elif isinstance(node, ast.UnaryOp) and isinstance(node.op, (ast.USub, ast.Invert)):
+                bad.append((fn.name, node.lineno))
+    assert not bad, "arithmetic in the binding: %s" % bad
 
 
 def test_eta_wave_bit_exact(g):
@@ -425,13 +448,14 @@ def test_conv_plan_and_argument_errors(g):
 
     p = g.gemm355_conv2d_plan(args())
     assert (p["T_M"], p["T_N"], p["T_K"]) != (0, 0, 0)
-    P, Q = g.conv_out_size(30, 30, 3, 3, 1, 1)
-    assert (P, Q) == (30, 30)
+    P, Q = g.gemm355_conv2d_out_size(args())
+    assert (P, Q) == (30, 30) == oc.out_size(30, 30, 3, 3, 1, 1, 1, 1, 1, 1)
     assert p["G"] == bk.tile_grid(4 * P * Q, 96, p["T_M"], p["T_N"])
     assert p["nK"] == bk.ceil_div(9 * 64, p["T_K"])
     assert g.gemm355_tile_info(p["tile"])["op"] == 1
     p2 = g.gemm355_conv2d_plan(args(stride_h=2, stride_w=3, dil_h=2, pad_h=0, pad_w=0))
-    P2, Q2 = g.conv_out_size(30, 30, 3, 3, 0, 0, 2, 3, 2, 1)
+    P2, Q2 = g.gemm355_conv2d_out_size(args(stride_h=2, stride_w=3, dil_h=2, pad_h=0, pad_w=0))
+    assert (P2, Q2) == oc.out_size(30, 30, 3, 3, 0, 0, 2, 3, 2, 1)
     assert p2["G"] == bk.tile_grid(4 * P2 * Q2, 96, p2["T_M"], p2["T_N"])
 
     def status(**kw):

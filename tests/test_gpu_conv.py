@@ -21,14 +21,14 @@ CONV_TILES = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)[
 def run_conv(x, w, ph=0, pw=0, sh=1, sw=1, dh=1, dw=1, out="f32", **knobs):
     N, Hh, W, C = x.shape
     K, R, S, _ = w.shape
-    P, Q = g.conv_out_size(Hh, W, R, S, ph, pw, sh, sw, dh, dw)
     xd, wd = H.dev(x), H.dev(w)
-    y = torch.full((N, P, Q, K), float("nan"), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
-                   device="cuda")
-    ws = None
-    a = g.make_conv_args(N, Hh, W, C, K, R, S, x=xd, w=wd, y=y, pad_h=ph, pad_w=pw, stride_h=sh,
+    a = g.make_conv_args(N, Hh, W, C, K, R, S, x=xd, w=wd, pad_h=ph, pad_w=pw, stride_h=sh,
                          stride_w=sw, dil_h=dh, dil_w=dw, dtype=g.BF16_BF16 if out == "bf16" else g.BF16_F32,
                          **knobs)
+    P, Q = g.gemm355_conv2d_out_size(a)
+    y = torch.full((N, P, Q, K), float("nan"), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
+                   device="cuda")
+    a.y = y.data_ptr()
     g.gemm355_conv2d(a)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
