@@ -175,12 +175,18 @@ def test_bf16_output_rounds_to_nearest_even():
         want = _bf16_rne(ref)
         ties = (np.abs(ref) > 256) & (np.abs(ref) < 512) & (np.mod(ref, 2) == 1)
         assert ties.sum() > 1000 and np.abs(ref).max() > 512
-        kw = dict(M=M, N=N, K=K, A=0x10000, B=0x100000, C=0x1000000, dtype=H.out_dtype(fmt, "bf16"))
-        tail_cus = H.split_tail_cus(kw)
-        assert tail_cus is not None
         tiles = BF16_TILES if fmt == "bf16" else E4M3_TILES
+        # the first tile with a persistent plan whose partial last round is split
+        tail = None
+        for t in tiles:
+            kw = dict(M=M, N=N, K=K, A=0x10000, B=0x100000, C=0x1000000, dtype=H.out_dtype(fmt, "bf16"), tile=t)
+            c = H.split_tail_cus(kw)
+            if c is not None:
+                tail = dict(tile=t, persistent=1, cus=c)
+                break
+        assert tail is not None
         runs = [dict(tile=t, split_k=1, persistent=0) for t in tiles]
-        runs += [dict(split_k=3), dict(split_k=7, persistent=1), dict(persistent=1, cus=tail_cus)]
+        runs += [dict(split_k=3), dict(split_k=7, persistent=1), tail]
         for kn in runs:
             H.say(fmt, "bf16 C rounding", kn)
             C = H.run(ops, out="bf16", **kn)
