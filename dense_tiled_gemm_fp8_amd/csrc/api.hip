@@ -202,7 +202,52 @@ struct ScratchReaper {
     }
 } g_reaper;
 
-gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = nullptr)
+/* Scratch of gemm355_gemm_noalloc: a fixed array in every device's memory,
+ * held from the library's load until the process ends.  Host code never
+ * passes `scratch` itself to a kernel (on the host the name denotes a
+ * stand-in, not a device address): the device address is looked up once
+ * per device, with that device current, and kept per device. */
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+struct NoAllocScratch {
+    std::mutex mu;          /* held by a call until its last enqueue */
+    void *ptr = nullptr;    /* the array's address on this device */
+};
+std::mutex g_noalloc_mu;
+std::map<int, std::unique_ptr<NoAllocScratch>> g_noalloc;
+
+gemm355_status noalloc_scratch(void **out, std::unique_lock<std::mutex> &hold)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM355_EHIP;
+    }
+    NoAllocScratch *s;
+    {
+        std::lock_guard<std::mutex> lk(g_noalloc_mu);
+        std::unique_ptr<NoAllocScratch> &slot = g_noalloc[dev];
+        if (!slot) {
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+                (void)hipGetLastError();
+                return GEMM355_EHIP;
+            }
+            slot.reset(new NoAllocScratch);
+            slot->ptr = ptr;
+        }
+        s = slot.get();
+    }
+    /* calls from several threads on one stream enqueue call by call */
+    hold = std::unique_lock<std::mutex>(s->mu);
+    *out = s->ptr;
+    return GEMM355_OK;
+}
+
+/* no_alloc: take scratch from the fixed per-device array instead of the
+ * caller's workspace or library-owned memory (nothing is allocated). */
+gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = nullptr, bool no_alloc = false)
 {
     Plan P;
     gemm355_status st = get_plan(a, P, conv);
@@ -221,7 +266,15 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
     /* held until this call's last launch is enqueued (library scratch) */
     std::unique_lock<std::mutex> hold;
     if (P.pub.workspace_bytes) {
-        if (a.workspace) {
+        if (no_alloc) {
+            /* every kernel writes the scratch it later reads (partial slots,
+             * repacked rows, regrouped scales), so nothing needs clearing */
+            if (P.pub.workspace_bytes > kNoAllocScratchBytes) return GEMM355_ETOOBIG;
+            void *p = nullptr;
+            st = noalloc_scratch(&p, hold);
+            if (st != GEMM355_OK) return st;
+            ws = (uint8_t *)p;
+        } else if (a.workspace) {
             if (a.workspace_bytes < P.pub.workspace_bytes) return GEMM355_ENOMEM;
             if (((uintptr_t)a.workspace & 255u) != 0) return GEMM355_EALIGN;
             ws = (uint8_t *)a.workspace;
@@ -479,6 +532,13 @@ gemm355_status gemm355_gemm_ex(const gemm355_args *args, void *stream)
     return run(*args, stream);
 }
 
+gemm355_status gemm355_gemm_noalloc(const gemm355_args *args, void *stream)
+{
+    if (!args) return GEMM355_EINVAL;
+    if (args->workspace || args->workspace_bytes) return GEMM355_EINVAL;
+    return run(*args, stream, nullptr, true);
+}
+
 gemm355_status gemm355_plan(const gemm355_args *args, gemm355_plan_t *out)
 {
     if (!args || !out) return GEMM355_EINVAL;
@@ -642,6 +702,7 @@ const char *gemm355_status_string(gemm355_status status)
     case GEMM355_EUNSUPPORTED: return "unsupported size";
     case GEMM355_ENOMEM: return "workspace too small or allocation failed";
     case GEMM355_EHIP: return "HIP runtime error";
+    case GEMM355_ETOOBIG: return "needs more scratch than the allocation-free entry point's fixed buffer";
     default: return "unknown status";
     }
 }

@@ -22,7 +22,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # status codes
-OK, EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP = range(6)
+OK, EINVAL, EALIGN, EUNSUPPORTED, ENOMEM, EHIP, ETOOBIG = range(7)
 # dtypes (input -> output)
 (BF16_F32, BF16_BF16, E4M3_F32, E4M3_BF16, E5M2_F32, E5M2_BF16, E4M3_E5M2_F32,
  E4M3_E5M2_BF16, MXE4M3_F32, MXE4M3_BF16, MXE5M2_F32, MXE5M2_BF16, MXE4M3_E5M2_F32,
@@ -92,6 +92,8 @@ _lib.gemm355_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                               ctypes.c_int, ctypes.c_int, _i32, _i32, _vp]
 _lib.gemm355_gemm_ex.restype = ctypes.c_int
 _lib.gemm355_gemm_ex.argtypes = [ctypes.POINTER(gemm355_args), _vp]
+_lib.gemm355_gemm_noalloc.restype = ctypes.c_int
+_lib.gemm355_gemm_noalloc.argtypes = [ctypes.POINTER(gemm355_args), _vp]
 _lib.gemm355_plan.restype = ctypes.c_int
 _lib.gemm355_plan.argtypes = [ctypes.POINTER(gemm355_args), ctypes.POINTER(gemm355_plan_t)]
 _lib.gemm355_eta_wave.restype = _f64
@@ -120,7 +122,8 @@ _lib.gemm355_conv2d_out_size.argtypes = [ctypes.POINTER(gemm355_conv_args), ctyp
 _lib.gemm355_status_string.restype = ctypes.c_char_p
 _lib.gemm355_status_string.argtypes = [ctypes.c_int]
 
-EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_plan", "gemm355_eta_wave",
+EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_gemm_noalloc",
+            "gemm355_plan", "gemm355_eta_wave",
             "gemm355_eta_pad", "gemm355_kslice", "gemm355_unit", "gemm355_num_tiles",
             "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_quantize",
             "gemm355_conv2d", "gemm355_conv2d_plan", "gemm355_conv2d_out_size", "gemm355_status_string")
@@ -188,6 +191,10 @@ def make_args(M, N, K, A=None, lda=None, B=None, ldb=None, C=None, ldc=None, dty
 
 def gemm355_gemm_ex(args: gemm355_args, stream=None) -> None:
     _check(_lib.gemm355_gemm_ex(ctypes.byref(args), _stream(stream)), "gemm355_gemm_ex")
+
+
+def gemm355_gemm_noalloc(args: gemm355_args, stream=None) -> None:
+    _check(_lib.gemm355_gemm_noalloc(ctypes.byref(args), _stream(stream)), "gemm355_gemm_noalloc")
 
 
 def gemm355_plan(args: gemm355_args) -> Dict[str, int]:

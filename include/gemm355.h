@@ -53,8 +53,10 @@ typedef enum gemm355_status {
                                   MX FP4 / FP6 call outside its limits */
     GEMM355_ENOMEM = 4,        /* caller workspace smaller than the plan's
                                   workspace_bytes, or allocation failed */
-    GEMM355_EHIP = 5           /* a HIP runtime call failed (no device,
+    GEMM355_EHIP = 5,          /* a HIP runtime call failed (no device,
                                   launch failure) */
+    GEMM355_ETOOBIG = 6        /* gemm355_gemm_noalloc: the plan needs more
+                                  scratch than its fixed per-device buffer */
 } gemm355_status;
 
 /* Element types, input -> output.  The two 8-bit formats are the FP8 pair
@@ -257,6 +259,29 @@ GEMM355_API gemm355_status gemm355_gemm(int64_t M, int64_t N, int64_t K,
  * them to the scaled matrix instruction.
  */
 GEMM355_API gemm355_status gemm355_gemm_ex(const gemm355_args *args, void *stream);
+
+/*
+ * gemm355_gemm_noalloc -- gemm355_gemm_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): it calls no hipMalloc, hipFree or other
+ * allocating routine.  Same arguments, plan, kernels and results as
+ * gemm355_gemm_ex, except that the scratch (split-K partial sums, repacked
+ * operands, regrouped block scales; plan.workspace_bytes) comes from a
+ * fixed array of 64 MiB (67,108,864 bytes) in each device's memory,
+ * reserved when the library is loaded and held until the process ends;
+ * its device address is looked up on the first call on each device.
+ *   args->workspace must be NULL and workspace_bytes 0 (EINVAL otherwise).
+ *   ETOOBIG if plan.workspace_bytes exceeds the fixed size (nothing is
+ *   launched; a smaller split_k or another tile brings the plan under it).
+ * Every call on one device uses that device's one array, and a call leaves
+ * its contents behind (nothing in it needs to start at zero: every kernel
+ * writes the scratch it later reads).  Calls that overlap in time on one
+ * device race on the array and may corrupt each other's results: calls on
+ * different streams must be ordered by the caller.  Calls on one stream,
+ * from any number of threads, enqueue call by call and are safe.
+ * Errors otherwise as gemm355_gemm_ex.
+ */
+GEMM355_API gemm355_status gemm355_gemm_noalloc(const gemm355_args *args, void *stream);
 
 /*
  * gemm355_plan -- what gemm355_gemm_ex would do with `args` (pointers are

@@ -63,6 +63,23 @@ def test_binding_holds_no_method_arithmetic():
     assert not bad, "arithmetic in the binding: %s" % bad
 
 
+def test_noalloc_host_checks(g):
+    """gemm355_gemm_noalloc refuses a caller workspace (EINVAL) and a plan
+    whose scratch exceeds its fixed 64 MiB array (ETOOBIG) before any device
+    work."""
+    base = dict(A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
+    big = g.make_args(4096, 4096, 4096, split_k=8, tile=0, **base)
+    assert g.gemm355_plan(big)["workspace_bytes"] == 256 * 8 * 256 * 256 * 4
+    with pytest.raises(g.Gemm355Error) as e:
+        g.gemm355_gemm_noalloc(big, stream=0)
+    assert e.value.status == g.ETOOBIG
+    with pytest.raises(g.Gemm355Error) as e:
+        g.gemm355_gemm_noalloc(g.make_args(64, 64, 64, workspace=0x300000000000, workspace_bytes=1 << 20,
+                                           **base), stream=0)
+    assert e.value.status == g.EINVAL
+    assert "fixed buffer" in g.gemm355_status_string(g.ETOOBIG)
+
+
 def test_eta_wave_bit_exact(g):
     rnd = random.Random(0)
     cases = [(24, 148, 1), (12, 148, 1), (256, 256, 1), (272, 256, 1), (1, 256, 1), (752, 256, 4)]
