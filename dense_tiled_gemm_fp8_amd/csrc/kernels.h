@@ -25,6 +25,9 @@ struct GemmParams {
     const float *scale_a, *scale_b;
     int32_t M, N, Kb;             /* Kb: K in bytes (multiple of 16)        */
     int32_t out_bf16;
+    int32_t c_vec;                /* 1: C rows can take 16-byte stores (base,
+                                     row pitch and batch stride multiples
+                                     of 16 bytes)                           */
     uint64_t *stamps;             /* per-unit start/end clock or null       */
     /* block scales (MX tiles), regrouped: dword [batch][K-tile][row] holds
      * a row's four E8M0 scales of one K-tile of 128 values */

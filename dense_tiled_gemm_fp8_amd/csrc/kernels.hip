@@ -35,6 +35,7 @@
 namespace g355 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -62,6 +63,13 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base)
     return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
                  __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF),
                  (int)kNumRecords, 0x00020000};
+}
+
+/* The lane's index in its wavefront, counted from the execution mask
+ * (every lane active): needs no register held since the kernel's start. */
+__device__ __forceinline__ int lane_id()
+{
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
 /* 32-bit LDS address of a __shared__ object. */
@@ -251,33 +259,37 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     /* this wavefront's index among the CW copying ones (SPREAD 3: the
      * producers NW .. NW+3) */
     const bool producer = SPREAD == 3 && wave >= NW;
     const int cw = SPREAD == 3 ? wave - NW : wave;
-    const int drow = lane / CPR;
-    /* Copy d of a stage part is copy group d * CW + cw; the lane's row is
-     * r = (d * CW + cw) * ROWS_PER_DMA + drow, and ROWS_PER_DMA = 4 RPL,
-     * so (r / RPL) % CPR = (4 (d CW + cw) + drow / RPL) % CPR: with
-     * 4 CW a multiple of CPR it is the same for every d, otherwise (CPR = 8,
-     * CW odd) it alternates with the parity of d.  lchunk[d & 1] is the
-     * logical chunk the lane fetches. */
     constexpr bool TWO = (4 * CW) % CPR != 0;
-    int lchunk[2];
-    lchunk[0] = (lane % CPR) ^ ((4 * cw + drow / RPL) % CPR);
-    lchunk[1] = (lane % CPR) ^ ((4 * (CW + cw) + drow / RPL) % CPR);
-    /* fragment lanes: lane l reads row l % MI of the block and K-chunk
-     * group l / MI of the step */
-    const int frow = lane % MI, hi = lane / MI, sw = (frow / RPL) % CPR;
     const uint32_t smem_base = lds_addr(smem);
 
     int32_t first = blockIdx.x;
     if (p.s.xcd_remap) first = xcd_remap(first, p.s.grid);
 
     for (int32_t u = first; u < p.s.units; u += p.s.grid) {
+        /* Lane-derived addresses are formed per unit from a lane index the
+         * compiler cannot see through: otherwise it hoists them out of the
+         * persistent loop and holds (or spills) them across every unit. */
+        int lane_u = lane_id();
+        asm volatile("" : "+v"(lane_u));
+        const int drow = lane_u / CPR;
+        /* Copy d of a stage part is copy group d * CW + cw; the lane's row
+         * is r = (d * CW + cw) * ROWS_PER_DMA + drow, and ROWS_PER_DMA =
+         * 4 RPL, so (r / RPL) % CPR = (4 (d CW + cw) + drow / RPL) % CPR:
+         * with 4 CW a multiple of CPR it is the same for every d, otherwise
+         * (CPR = 8, CW odd) it alternates with the parity of d.
+         * lchunk[d & 1] is the logical chunk the lane fetches. */
+        int lchunk[2];
+        lchunk[0] = (lane_u % CPR) ^ ((4 * cw + drow / RPL) % CPR);
+        lchunk[1] = (lane_u % CPR) ^ ((4 * (CW + cw) + drow / RPL) % CPR);
+        /* fragment lanes: lane l reads row l % MI of the block and K-chunk
+         * group l / MI of the step */
+        const int frow = lane_u % MI, hi = lane_u / MI, sw = (frow / RPL) % CPR;
         uint64_t stamp0 = 0, clk0 = 0;
         if (p.stamps) {
             stamp0 = __builtin_amdgcn_s_memrealtime();
@@ -338,7 +350,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 const int g = q * NW + wave;
                 const int w = g / G1, g1 = g % G1;
                 const bool in_a = g1 < TM / 64;
-                const int r = (in_a ? g1 : g1 - TM / 64) * 64 + lane;
+                const int r = (in_a ? g1 : g1 - TM / 64) * 64 + lane_u;
                 const uint32_t plane = (uint32_t)(in_a ? p.ktp_a : p.ktp_b);
                 srs[q] = rsrc_words(in_a ? sa0 : sb0);
                 soff[q] = (in_a ? m0 + r < p.M : n0 + r < p.N) ? (uint32_t)(r * 4) + w * plane : kOOB;
@@ -772,90 +784,186 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * column l % 32, register 4 g + r holds row 8 g + 4 (l / 32) + r; of a
          * 16 x 16 block: lane l holds column l % 16, register r holds row
          * 4 (l / 16) + r.
-         * Stores go through a buffer resource based at the tile's corner: the
-         * lane's column and row group in the VGPR offset, the register's row
-         * in the scalar offset; elements outside M x N get VGPR offset kOOB
-         * and are dropped.  The lane index is re-materialised here so the
-         * compiler cannot hoist the epilogue's addresses above the main loop
-         * and hold them in registers across it. */
-        int lv = threadIdx.x;
-        asm volatile("" : "+v"(lv));
-        if (!producer) {
-            const int el = lv & 63, ecol = el % MI, ehi = el / MI;
-            /* row of accumulator register e relative to the lane's first row */
-            auto erow = [](int e) __attribute__((always_inline)) { return MI == 32 ? (e >> 2) * 8 + (e & 3) : e; };
-            if (un.slot >= 0) {
-                /* partial slot: the tile's positions inside M x N only (the
-                 * combine pass reads no others) */
-                const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (int64_t)un.slot * (TM * TN));
-                const int32_t mrem = p.M - m0, nrem = p.N - n0;
+         * Stores go through a buffer resource based at the tile's corner.
+         * The lane index is re-materialised here so the compiler cannot
+         * hoist the epilogue's addresses above the main loop and hold them
+         * in registers across it. */
+        int el = lane_id();
+        asm volatile("" : "+v"(el));
+        const int ecol = el % MI, ehi = el / MI;
+        /* row of accumulator register e relative to the lane's first row */
+        auto erow = [](int e) __attribute__((always_inline)) { return MI == 32 ? (e >> 2) * 8 + (e & 3) : e; };
+        const int32_t mrem = p.M - m0, nrem = p.N - n0;
+
+        /* Staged epilogue: once the ring is idle, each MFMA wavefront writes
+         * its WTM x WTN block of results (alpha applied, binary32) into its
+         * own share of the LDS, FMP block rows per pass, then reads it back
+         * as row segments and stores 16 bytes per lane (4 fp32 results, or 8
+         * results rounded to bf16) instead of one 2- or 4-byte store per
+         * result.  One write sequence serves both output types, so each
+         * accumulator is read once.  Staged rows are WTN fp32 (CW 16-byte
+         * chunks); chunk c of staged row r sits at position
+         * c ^ ((CB (r / 4)) mod CW), CB the chunks one MFMA block row spans,
+         * so that the 64 / MI row groups one write instruction covers (rows
+         * 4 apart) fall on different banks.  Rows past M and segments past N
+         * are not stored.  The columns of a segment that straddles N, and
+         * every result when C's rows are not 16-byte aligned (vec false),
+         * are stored element by element in a second, rolled loop. */
+        constexpr int WAVE_LDS = STAGES * STAGE_BYTES / NW;
+        constexpr int FMP = [] {
+            int f = FM;
+            while (f > 0 && (FM % f != 0 || f * MI * WTN * 4 > WAVE_LDS)) --f;
+            return f;
+        }();
+        static_assert(FMP > 0, "a wave's share of the LDS holds one block row of fp32 results");
+        constexpr int CWB = WTN * 4, CW = CWB / 16, CB = MI / 4;
+        constexpr int PR = FMP * MI;
+        static_assert((CW & (CW - 1)) == 0 && CW >= 2, "staged rows: a power of two of 16-byte chunks");
+        auto swz = [](int r) __attribute__((always_inline)) { return (CB * (r >> 2)) & (CW - 1); };
+        /* output kind: 0 partial slot (fp32, pitch TN), 1 fp32 C, 2 bf16 C.
+         * Staged: bf16 C, and fp32 C from 16 x 16 blocks (a store of one
+         * register then covers only 64 bytes of each of 4 rows) when C's
+         * rows are 16-byte aligned.  Direct fp32 stores from the
+         * accumulators: partial slots (a split tail's slots often hold a few
+         * valid rows), fp32 C from 32 x 32 blocks, whose stores already
+         * cover 128 contiguous bytes of each of 2 rows, and fp32 C whose rows
+         * are not 16-byte aligned. */
+        const int kind = un.slot >= 0 ? 0 : (p.out_bf16 ? 2 : 1);
+        const bool use_staged = kind == 2 || (kind == 1 && MI == 16 && p.c_vec);
+        if (!producer && !use_staged) {
+            const float alpha = kind == 0 ? 1.0f : unit_alpha(p, un.batch);
+            const __amdgpu_buffer_rsrc_t rc =
+                kind == 0 ? make_rsrc(p.ws + (int64_t)un.slot * (TM * TN))
+                          : make_rsrc((const uint8_t *)p.C +
+                                      ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
+            const int32_t ldcb = kind == 0 ? TN * 4 : (int32_t)p.ldc * 4;
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = wn * WTN + j * MI + ecol;
+                    const int row0 = wm * WTM + i * MI + ehi * 4;
+                    const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
+#pragma unroll
+                    for (int e = 0; e < ACC_N; ++e) {
+                        /* copy the element out first: a bit_cast applied to
+                         * a vector subscript directly was lowered to element
+                         * 0 for every e */
+                        const float v = alpha * acc[i][j][e];
+                        const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, ok ? voff : kOOB,
+                                                              erow(e) * ldcb, 0);
+                    }
+                    /* one block at a time keeps the epilogue's registers few */
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+        if (use_staged) {
+            /* the ring is idle: every wave's copies (those of K-tiles past
+             * the range included) have landed and its fragment reads are done */
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        if (!producer && use_staged) {
+            uint8_t *region = smem + wave * WAVE_LDS;
+            const int os = kind == 2 ? 2 : 4;
+            const float alpha = unit_alpha(p, un.batch);
+            const __amdgpu_buffer_rsrc_t rc =
+                make_rsrc((const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * os);
+            const int32_t ldcb = (int32_t)p.ldc * os;
+            const bool vec = p.c_vec != 0;
+            /* output elements per 16-byte segment */
+            const int epc = 16 / os;
+            /* this wave's columns end inside a segment of C */
+            const int ncol = nrem - wn * WTN;
+            const bool edge = ncol > 0 && ncol < WTN && ncol % epc != 0;
+#pragma unroll
+            for (int ps = 0; ps < FM / FMP; ++ps) {
+#pragma unroll
+                for (int ii = 0; ii < FMP; ++ii)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const int col = wn * WTN + j * MI + ecol;
-                        const int row0 = wm * WTM + i * MI + ehi * 4;
-                        const uint32_t voff = (uint32_t)((row0 * TN + col) * 4);
 #pragma unroll
                         for (int e = 0; e < ACC_N; ++e) {
-                            /* copy the element out first: a bit_cast applied to
-                             * a vector subscript directly was lowered to element
-                             * 0 for every e */
-                            const float v = acc[i][j][e];
-                            const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
-                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, ok ? voff : kOOB,
-                                                                  erow(e) * TN * 4, 0);
+                            const int r = ii * MI + ehi * 4 + erow(e), c = j * MI + ecol;
+                            *(float *)(region + r * CWB + ((((c * 4) >> 4) ^ swz(r)) << 4) + ((c * 4) & 15)) =
+                                alpha * acc[ps * FMP + ii][j][e];
                         }
                         /* one block at a time keeps the epilogue's registers few */
                         __builtin_amdgcn_sched_barrier(0);
                     }
-            } else {
-                const float alpha = unit_alpha(p, un.batch);
-                const int32_t mrem = p.M - m0, nrem = p.N - n0;
-                if (p.out_bf16) {
-                    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
-                        (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 2);
-                    const int32_t ldcb = (int32_t)p.ldc * 2;
+                if (vec) {
+                    if (kind == 2) {
+                        /* segment q: staged row q / (CW/2), bf16 columns
+                         * 8 (q % (CW/2)) .. + 7 from fp32 chunks 2c, 2c + 1 */
+                        constexpr int NSEG = PR * CW / 2, IT = (NSEG + 63) / 64;
 #pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j) {
-                            const int col = wn * WTN + j * MI + ecol;
-                            const int row0 = wm * WTM + i * MI + ehi * 4;
-                            const uint32_t voff = (uint32_t)(row0 * ldcb + col * 2);
-#pragma unroll
-                            for (int e = 0; e < ACC_N; ++e) {
-                                const int dr = erow(e);
-                                const bool ok = (row0 + dr < mrem) && (col < nrem);
-                                const float v = alpha * acc[i][j][e];
-                                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc,
-                                                                      ok ? voff : kOOB, dr * ldcb, 0);
+                        for (int it = 0; it < IT; ++it) {
+                            const int q = it * 64 + el;
+                            if (NSEG % 64 == 0 || q < NSEG) {
+                                const int r = q / (CW / 2), c = q % (CW / 2);
+                                const f32x4 lo = *(const f32x4 *)(region + r * CWB + (((2 * c) ^ swz(r)) << 4));
+                                const f32x4 hi = *(const f32x4 *)(region + r * CWB + (((2 * c + 1) ^ swz(r)) << 4));
+                                const int grow = wm * WTM + ps * PR + r, gcol = wn * WTN + 8 * c;
+                                const bool full = grow < mrem && gcol + 8 <= nrem;
+                                __attribute__((ext_vector_type(4))) uint32_t d;
+                                d[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[0], (__bf16)lo[1]});
+                                d[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[2], (__bf16)lo[3]});
+                                d[2] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi[0], (__bf16)hi[1]});
+                                d[3] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi[2], (__bf16)hi[3]});
+                                __builtin_amdgcn_raw_buffer_store_b128(d, rc, full ? (uint32_t)(grow * ldcb + gcol * 2) : kOOB,
+                                                                       0, 0);
                             }
                             __builtin_amdgcn_sched_barrier(0);
                         }
-                } else {
-                    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
-                        (const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
-                    const int32_t ldcb = (int32_t)p.ldc * 4;
+                    } else {
+                        constexpr int NSEG = PR * CW, IT = (NSEG + 63) / 64;
 #pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j) {
-                            const int col = wn * WTN + j * MI + ecol;
-                            const int row0 = wm * WTM + i * MI + ehi * 4;
-                            const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
-#pragma unroll
-                            for (int e = 0; e < ACC_N; ++e) {
-                                const int dr = erow(e);
-                                const bool ok = (row0 + dr < mrem) && (col < nrem);
-                                const float v = alpha * acc[i][j][e];
-                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc,
-                                                                      ok ? voff : kOOB, dr * ldcb, 0);
+                        for (int it = 0; it < IT; ++it) {
+                            const int q = it * 64 + el;
+                            if (NSEG % 64 == 0 || q < NSEG) {
+                                const int r = q / CW, c = q % CW;
+                                const i32x4 d = *(const i32x4 *)(region + r * CWB + ((c ^ swz(r)) << 4));
+                                const int grow = wm * WTM + ps * PR + r, gcol = wn * WTN + 4 * c;
+                                const bool full = grow < mrem && gcol + 4 <= nrem;
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, d), rc,
+                                    full ? (uint32_t)(grow * ldcb + gcol * 4) : kOOB, 0, 0);
                             }
                             __builtin_amdgcn_sched_barrier(0);
                         }
+                    }
+                }
+                if (!vec || edge) {
+                    /* element by element, 64 consecutive columns of a row
+                     * per store instruction: every result when C's rows are
+                     * not 16-byte aligned, else the columns of the segment
+                     * that straddles N (those past the last whole segment) */
+                    const int c0 = vec ? ncol - ncol % epc : 0, cn = vec ? ncol % epc : WTN;
+                    for (int t = el; t < PR * cn; t += 64) {
+                        const int r = t / cn, col = c0 + t % cn;
+                        const int grow = wm * WTM + ps * PR + r, gcol = wn * WTN + col;
+                        if (grow < mrem && gcol < nrem) {
+                            const float v = *(const float *)(region + r * CWB + ((((col * 4) >> 4) ^ swz(r)) << 4) +
+                                                             ((col * 4) & 15));
+                            const uint32_t voff = (uint32_t)(grow * ldcb + gcol * os);
+                            if (os == 2)
+                                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc, voff,
+                                                                      0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, voff, 0, 0);
+                        }
+                    }
                 }
             }
+        }
+        if (use_staged) {
+            /* every wave has read its staged results back before the next
+             * unit's copies refill the ring */
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
         if (p.stamps) {
             /* every wave's stores of this unit have completed */
@@ -863,7 +971,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             __builtin_amdgcn_s_barrier();
             const uint64_t stamp1 = __builtin_amdgcn_s_memrealtime();
             const uint64_t clk1 = __builtin_amdgcn_s_memtime();
-            if (threadIdx.x == 0) {
+            if (wave == 0 && lane_id() == 0) {
                 uint64_t *st = p.stamps + 4 * (int64_t)u;
                 st[0] = stamp0;
                 st[1] = stamp1;
