@@ -12,9 +12,11 @@ shader clock takes some tens of milliseconds of load to reach its
 TFLOP/s of useful work 2MNK per step (section "Shape the operation" of page
 "10. Tensor Cores, shapes, and tile alignment"), the roofline of the main
 kernel (achieved vs the dense bf16 MFMA peak, timed with HIP events on the
-launch stream), the CPU oracle timed on a bounded sample, and a per-workload
-detail list (every named workload, each timed the same way, HBM-bound shapes
-rotating input copies so they cannot sit in the 256 MB last-level cache).
+launch stream; also the median and minimum of per-call kernel times), the
+CPU oracle timed on a bounded sample, and a per-workload detail list (every
+named workload, each timed the same way, HBM-bound shapes rotating input
+copies so they cannot sit in the 256 MB last-level cache, each with the
+oracle timed on a bounded sample of it).
 """
 from __future__ import annotations
 
@@ -217,6 +219,23 @@ def time_case(case, torch, steps, warmup, settle_s=0.0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, e0.elapsed_time(e1) * 1e-3
+
+
+def per_call_times(case, torch, calls):
+    """After the timed region: `calls` back-to-back calls, each bracketed by
+    its own HIP event pair on the launch stream; median and min of the
+    per-call durations (events only, no host synchronisation in between)."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        case.step(sp)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    return {"calls": calls, "median_us": round(us[len(us) // 2], 3), "min_us": round(us[0], 3),
+            "max_us": round(us[-1], 3)}
 
 
 def sample_smi():
@@ -432,6 +451,38 @@ def conv_layers(torch, g, inputs, args):
     return out
 
 
+def oracle_sample(ops, budget_s=2.0):
+    """The oracle (as it stands) on a bounded sample of one workload: the
+    first R rows of A (R from a 16-row probe, about budget_s seconds) against
+    all of B, of the first batch entry.  Returns the sample's wall seconds,
+    its oracle GFLOP/s and the full workload's time at that rate."""
+    from oracle import reference as oracle
+    M, N, K = ops.M, ops.N, ops.K
+    A = ops.A[0] if ops.A.ndim == 3 else ops.A
+    B = ops.B[0] if ops.B.ndim == 3 else ops.B
+    kw = {} if ops.fmt == "bf16" else {"fmt_a": ops.fmt_a, "fmt_b": ops.fmt_b}
+    # two probes separate the fixed cost (decoding all of B) from the per-row cost
+    times = []
+    probes = (min(M, 8), min(M, 24))
+    for r in probes:
+        t0 = time.perf_counter()
+        oracle.gemm(r, N, K, A[:r].reshape(-1), K, B.reshape(-1), K, **kw)
+        times.append(time.perf_counter() - t0)
+    per_row = max((times[1] - times[0]) / max(probes[1] - probes[0], 1), 1e-7)
+    fixed = max(times[0] - probes[0] * per_row, 0.0)
+    rows = int(min(M, max(probes[1], budget_s / per_row)))
+    t0 = time.perf_counter()
+    oracle.gemm(rows, N, K, A[:rows].reshape(-1), K, B.reshape(-1), K, **kw)
+    t = time.perf_counter() - t0
+    gflops = 2.0 * rows * N * K / t / 1e9
+    per_row = max((t - fixed) / rows, 1e-9)
+    full = ops.batch * (fixed + per_row * M)
+    return {"seconds": round(t, 3), "gflops": round(gflops, 2), "cores": oracle.threads(),
+            "sample": "rows 0..%d of %s (binary64 triple loop with W, decode of all of B included)" % (
+                rows - 1, "batch entry 0" if ops.batch > 1 else "the product"),
+            "full_s_estimate": round(full, 2)}
+
+
 def cpu_baseline(torch, budget_s=15.0):
     """The oracle (as it stands) on a bounded sample of the headline product:
     the first R rows of A against all of B, R sized from a short probe to
@@ -512,6 +563,8 @@ def main():
     kern_avg = ev / args.steps
     achieved = head.flops / kern_avg / 1e12
     log("bench: %.3f ms/step wall, kernel avg %.2f us, %.1f TFLOP/s" % (ms_per_step, kern_avg * 1e6, achieved))
+    per_call = per_call_times(head, torch, max(args.steps, 20))
+    log("bench: per-call kernel us median %.2f min %.2f" % (per_call["median_us"], per_call["min_us"]))
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -552,6 +605,8 @@ def main():
                     "eta_pad": [p["eta_pad_num"], p["eta_pad_den"]],
                     "eta_sched": [p["eta_sched_num"], p["eta_sched_den"]],
                 })
+                if not args.no_cpu_baseline:
+                    detail[-1]["cpu_oracle"] = oracle_sample(c.ops)
                 me = c.measured_eta(torch)
                 detail[-1]["eta_measured"] = None if me is None else round(me["eta"], 4)
                 detail[-1]["sclk_mhz"] = None if me is None else round(me["sclk_mhz"], 0)
@@ -588,6 +643,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": traffic, "kernel_us": round(kern_avg * 1e6, 3)},
+        "per_call_kernel_us": per_call,
         "cpu_baseline": cpu,
         "detail": detail,
     }
