@@ -801,25 +801,24 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * as row segments and stores 16 bytes per lane (4 fp32 results, or 8
          * results rounded to bf16) instead of one 2- or 4-byte store per
          * result.  One write sequence serves both output types, so each
-         * accumulator is read once.  Staged rows are WTN fp32 (CW 16-byte
-         * chunks); chunk c of staged row r sits at position
-         * c ^ ((CB (r / 4)) mod CW), CB the chunks one MFMA block row spans,
-         * so that the 64 / MI row groups one write instruction covers (rows
-         * 4 apart) fall on different banks.  Rows past M and segments past N
-         * are not stored.  The columns of a segment that straddles N, and
-         * every result when C's rows are not 16-byte aligned (vec false),
-         * are stored element by element in a second, rolled loop. */
+         * accumulator is read once.  A staged row is WTN fp32 plus 16 bytes
+         * of padding (CWB bytes): the 64 / MI row groups one write
+         * instruction covers (rows 4 apart) then start 16 banks apart, and
+         * every staged address is the lane's base plus a constant.  Rows
+         * past M and segments past N are not stored.  The columns of a
+         * segment that straddles N, and every result when C's rows are not
+         * 16-byte aligned (vec false), are stored element by element in a
+         * second, rolled loop. */
         constexpr int WAVE_LDS = STAGES * STAGE_BYTES / NW;
+        /* (no padding where a wave's share holds just one unpadded block row) */
+        constexpr int CWB = WTN * 4 + (MI * (WTN * 4 + 16) <= WAVE_LDS ? 16 : 0), CW = WTN / 4;
         constexpr int FMP = [] {
             int f = FM;
-            while (f > 0 && (FM % f != 0 || f * MI * WTN * 4 > WAVE_LDS)) --f;
+            while (f > 0 && (FM % f != 0 || f * MI * CWB > WAVE_LDS)) --f;
             return f;
         }();
         static_assert(FMP > 0, "a wave's share of the LDS holds one block row of fp32 results");
-        constexpr int CWB = WTN * 4, CW = CWB / 16, CB = MI / 4;
         constexpr int PR = FMP * MI;
-        static_assert((CW & (CW - 1)) == 0 && CW >= 2, "staged rows: a power of two of 16-byte chunks");
-        auto swz = [](int r) __attribute__((always_inline)) { return (CB * (r >> 2)) & (CW - 1); };
         /* output kind: 0 partial slot (fp32, pitch TN), 1 fp32 C, 2 bf16 C.
          * Staged: bf16 C, and fp32 C from 16 x 16 blocks (a store of one
          * register then covers only 64 bytes of each of 4 rows) when C's
@@ -830,13 +829,36 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * are not 16-byte aligned. */
         const int kind = un.slot >= 0 ? 0 : (p.out_bf16 ? 2 : 1);
         const bool use_staged = kind == 2 || (kind == 1 && MI == 16 && p.c_vec);
-        if (!producer && !use_staged) {
-            const float alpha = kind == 0 ? 1.0f : unit_alpha(p, un.batch);
+        if (!producer && kind == 0) {
+            /* partial slot: the tile's positions inside M x N only (the
+             * combine pass reads no others) */
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (int64_t)un.slot * (TM * TN));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = wn * WTN + j * MI + ecol;
+                    const int row0 = wm * WTM + i * MI + ehi * 4;
+                    const uint32_t voff = (uint32_t)((row0 * TN + col) * 4);
+#pragma unroll
+                    for (int e = 0; e < ACC_N; ++e) {
+                        /* copy the element out first: a bit_cast applied to
+                         * a vector subscript directly was lowered to element
+                         * 0 for every e */
+                        const float v = acc[i][j][e];
+                        const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rw, ok ? voff : kOOB,
+                                                              erow(e) * TN * 4, 0);
+                    }
+                    /* one block at a time keeps the epilogue's registers few */
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        } else if (!producer && !use_staged) {
+            /* fp32 C straight from the accumulators */
+            const float alpha = unit_alpha(p, un.batch);
             const __amdgpu_buffer_rsrc_t rc =
-                kind == 0 ? make_rsrc(p.ws + (int64_t)un.slot * (TM * TN))
-                          : make_rsrc((const uint8_t *)p.C +
-                                      ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
-            const int32_t ldcb = kind == 0 ? TN * 4 : (int32_t)p.ldc * 4;
+                make_rsrc((const uint8_t *)p.C + ((int64_t)un.batch * p.stride_c + (int64_t)m0 * p.ldc + n0) * 4);
+            const int32_t ldcb = (int32_t)p.ldc * 4;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -846,15 +868,12 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     const uint32_t voff = (uint32_t)(row0 * ldcb + col * 4);
 #pragma unroll
                     for (int e = 0; e < ACC_N; ++e) {
-                        /* copy the element out first: a bit_cast applied to
-                         * a vector subscript directly was lowered to element
-                         * 0 for every e */
+                        const int dr = erow(e);
+                        const bool ok = (row0 + dr < mrem) && (col < nrem);
                         const float v = alpha * acc[i][j][e];
-                        const bool ok = (row0 + erow(e) < mrem) && (col < nrem);
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, ok ? voff : kOOB,
-                                                              erow(e) * ldcb, 0);
+                                                              dr * ldcb, 0);
                     }
-                    /* one block at a time keeps the epilogue's registers few */
                     __builtin_amdgcn_sched_barrier(0);
                 }
         }
@@ -867,6 +886,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         }
         if (!producer && use_staged) {
             uint8_t *region = smem + wave * WAVE_LDS;
+            /* the lane's staged element of register 0 of block (0, 0) */
+            uint8_t *lbase = region + ehi * 4 * CWB + ecol * 4;
             const int os = kind == 2 ? 2 : 4;
             const float alpha = unit_alpha(p, un.batch);
             const __amdgpu_buffer_rsrc_t rc =
@@ -885,11 +906,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
 #pragma unroll
-                        for (int e = 0; e < ACC_N; ++e) {
-                            const int r = ii * MI + ehi * 4 + erow(e), c = j * MI + ecol;
-                            *(float *)(region + r * CWB + ((((c * 4) >> 4) ^ swz(r)) << 4) + ((c * 4) & 15)) =
-                                alpha * acc[ps * FMP + ii][j][e];
-                        }
+                        for (int e = 0; e < ACC_N; ++e)
+                            *(float *)(lbase + (ii * MI + erow(e)) * CWB + j * MI * 4) = alpha * acc[ps * FMP + ii][j][e];
                         /* one block at a time keeps the epilogue's registers few */
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -903,8 +921,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                             const int q = it * 64 + el;
                             if (NSEG % 64 == 0 || q < NSEG) {
                                 const int r = q / (CW / 2), c = q % (CW / 2);
-                                const f32x4 lo = *(const f32x4 *)(region + r * CWB + (((2 * c) ^ swz(r)) << 4));
-                                const f32x4 hi = *(const f32x4 *)(region + r * CWB + (((2 * c + 1) ^ swz(r)) << 4));
+                                const f32x4 lo = *(const f32x4 *)(region + r * CWB + 32 * c);
+                                const f32x4 hi = *(const f32x4 *)(region + r * CWB + 32 * c + 16);
                                 const int grow = wm * WTM + ps * PR + r, gcol = wn * WTN + 8 * c;
                                 const bool full = grow < mrem && gcol + 8 <= nrem;
                                 __attribute__((ext_vector_type(4))) uint32_t d;
@@ -924,7 +942,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                             const int q = it * 64 + el;
                             if (NSEG % 64 == 0 || q < NSEG) {
                                 const int r = q / CW, c = q % CW;
-                                const i32x4 d = *(const i32x4 *)(region + r * CWB + ((c ^ swz(r)) << 4));
+                                const i32x4 d = *(const i32x4 *)(region + r * CWB + 16 * c);
                                 const int grow = wm * WTM + ps * PR + r, gcol = wn * WTN + 4 * c;
                                 const bool full = grow < mrem && gcol + 4 <= nrem;
                                 __builtin_amdgcn_raw_buffer_store_b128(
@@ -945,8 +963,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                         const int r = t / cn, col = c0 + t % cn;
                         const int grow = wm * WTM + ps * PR + r, gcol = wn * WTN + col;
                         if (grow < mrem && gcol < nrem) {
-                            const float v = *(const float *)(region + r * CWB + ((((col * 4) >> 4) ^ swz(r)) << 4) +
-                                                             ((col * 4) & 15));
+                            const float v = *(const float *)(region + r * CWB + col * 4);
                             const uint32_t voff = (uint32_t)(grow * ldcb + gcol * os);
                             if (os == 2)
                                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc, voff,

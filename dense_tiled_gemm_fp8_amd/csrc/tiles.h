@@ -90,7 +90,7 @@ constexpr TileCfg kTiles[] = {
     /* small tiles with deep rings for streaming (small M, N, long K) */
     {0, 64, 64, 64, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.10f, 0.10f, 0.10f, 0.10f}, 1.56f},
     {0, 64, 64, 64, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.10f, 0.17f, 0.17f, 0.17f}, 2.48f},
-    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.32f, 0.32f, 0.32f, 0.32f}, 1.20f},
+    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.32f, 0.32f, 0.32f, 0.32f}, 1.40f},
     {1, 64, 64, 128, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.12f, 0.12f, 0.12f, 0.12f}, 1.50f},
     {1, 64, 64, 128, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.12f, 0.20f, 0.20f, 0.20f}, 1.68f},
     {1, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.35f, 0.35f, 0.35f, 0.35f}, 1.34f},
