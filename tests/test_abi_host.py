@@ -427,6 +427,10 @@ def test_main_loop_uses_mfma(g, tmp_path):
             assert all(("blgp:1" in l) == (fmt >= 1) for l in lines), name
         else:
             assert fmt == 0
+        # no register spills anywhere in the kernel (a spill reloaded in the
+        # main loop or prologue costs far more than the instructions it saves)
+        m = re.search(r"; ScratchSize: (\d+)", body)
+        assert m and int(m.group(1)) == 0, (name, m and m.group(1))
 
 
 def test_struct_layout_matches_header(g, tmp_path):
