@@ -340,6 +340,7 @@ gemm355_status run(const gemm355_args &a, void *stream, const ConvShape *conv = 
     gp.M = (int32_t)a.M;
     gp.N = (int32_t)a.N;
     gp.Kb = P.Kb;
+    gp.Kv = P.Kv;
     gp.out_bf16 = P.out_esize == 2 ? 1 : 0;
     gp.c_vec = ((uintptr_t)a.C % 16 == 0) && (a.ldc * P.out_esize) % 16 == 0 &&
                (a.batch <= 1 || (a.stride_c * P.out_esize) % 16 == 0);

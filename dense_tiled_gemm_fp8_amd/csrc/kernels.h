@@ -23,7 +23,11 @@ struct GemmParams {
     int64_t stride_a, stride_b;   /* bytes between batch entries            */
     int64_t ldc, stride_c;        /* elements of C                          */
     const float *scale_a, *scale_b;
-    int32_t M, N, Kb;             /* Kb: K in bytes (multiple of 16)        */
+    int32_t M, N, Kb;             /* Kb: K in bytes rounded up to 16        */
+    int32_t Kv;                   /* K in bytes when rows are read in place
+                                     and K is not a whole number of 16-byte
+                                     chunks (the bytes of the last chunk past
+                                     Kv are cleared in LDS); else 0          */
     int32_t out_bf16;
     int32_t c_vec;                /* 1: C rows can take 16-byte stores (base,
                                      row pitch and batch stride multiples

@@ -435,6 +435,39 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 dma4(srs[q], smem_base + so + sdst[q], kv.tile ? soff[q] + (kb / KTB) * stp[q] : kOOB);
             }
         };
+        /* Rows read in place whose K ends inside a 16-byte chunk: the chunk
+         * also brought the next bytes of memory (the next row's first
+         * elements, or whatever follows the operand).  Once the copies of
+         * iteration i (in the stage at so) have landed, each lane that
+         * fetched such a chunk clears its bytes past K in LDS, before the
+         * barrier that shows the stage to the other waves.  Only copy
+         * schedules 0 and 4 (tile and prologue waits below) take this path. */
+        auto zero_tail = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
+            if constexpr (!FP6 && !MX && !CONV && (SPREAD == 0 || SPREAD == 4)) {
+                const int32_t kb = ktile(i) * KTB;
+                if (p.Kv > 0 && i < nkt && kb + KTB > p.Kv) {
+                    unroll<A_LOADS + B_LOADS>([&](auto dc) __attribute__((always_inline)) {
+                        constexpr int d = decltype(dc)::value;
+                        constexpr int di = d < A_LOADS ? d : d - A_LOADS;
+                        const int32_t v = p.Kv - (kb + lchunk[TWO ? di & 1 : 0] * 16);
+                        if (v > 0 && v < 16) {
+                            constexpr int DOFF = d < A_LOADS ? d * CW * 1024 : A_BYTES + (d - A_LOADS) * CW * 1024;
+                            i32x4 *c = (i32x4 *)(smem + so + DOFF + cw * 1024 + lane_u * 16);
+                            i32x4 w = *c;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int32_t vb = v - 4 * j;
+                                const uint32_t keep = vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+                                w[j] = (int)((uint32_t)w[j] & keep);
+                            }
+                            *c = w;
+                        }
+                    });
+                    /* the cleared bytes are in LDS before the barrier */
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
+            }
+        };
         auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
             const KV kv = kvalid(i);
             const uint32_t kb = (uint32_t)ktile(i) * KTB;
@@ -687,6 +720,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
              * 3: the producers have waited for it before this barrier) */
             if constexpr (SPREAD != 3)
                 wait_vmcnt<SP1 ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
+            /* K-tile kt+1 (stage nso) has landed */
+            zero_tail(nso, kt + 1);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             if constexpr (SP1) {
@@ -737,6 +772,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     copy_tile(st * STAGE_BYTES, kt + st);
                 });
                 wait_vmcnt<(PRE - 1) * LOADS>();
+                zero_tail(0u, kt);
             }
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");

@@ -18,6 +18,8 @@ struct Plan {
     int32_t esize;              /* input element bytes (2 bf16, 1 8-bit)    */
     int32_t out_esize;          /* 4 fp32, 2 bf16                           */
     int32_t Kb;                 /* K bytes seen by the main loop            */
+    int32_t Kv;                 /* K bytes when an operand is read in place
+                                   and K ends inside a 16-byte chunk; else 0 */
     int32_t pack_a, pack_b;
     /* operand views the main loop reads (bytes) */
     int64_t lda_b, ldb_b, stride_a_b, stride_b_b;

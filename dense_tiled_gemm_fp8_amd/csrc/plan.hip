@@ -392,16 +392,27 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
         if (pst != GEMM355_OK) return pst;
     }
 
-    /* Operand views of the main loop: K-contiguous rows, 16-byte aligned
-     * rows and starts, K a whole number of 16-byte chunks; otherwise the
-     * operand is repacked (zero-filled to a whole number of K-tiles). */
+    /* Operand views of the main loop: K-contiguous rows.  bf16 and 8-bit
+     * rows are read in place whatever their alignment (16-byte buffer
+     * loads take any byte address); if K ends inside a 16-byte chunk, the
+     * copy schedules that clear the chunk's bytes past K in LDS (0 and 4)
+     * are the only candidates.  Other operands (the transposed layouts;
+     * block-scaled rows that are not 16-byte aligned or do not end on a
+     * chunk) are repacked, zero-filled to a whole number of K-tiles. */
     auto bytes_of = [ebits](int64_t elems) { return elems * ebits / 8; };
     const int64_t kbytes = bytes_of(K);
     const int64_t packed_ld = cdiv(std::max<int64_t>(kbytes, 1), 128) * 128;
-    P.pack_a = !a_row || misaligned16(a.A) || bytes_of(a.lda) % 16 || kbytes % 16 ||
-               (batch > 1 && bytes_of(a.stride_a) % 16);
-    P.pack_b = !b_col || misaligned16(a.B) || bytes_of(a.ldb) % 16 || kbytes % 16 ||
-               (batch > 1 && bytes_of(a.stride_b) % 16);
+    const bool in_place = (dclass == 0 || dclass == 1) && !conv;
+    const bool ktail = kbytes % 16 != 0;
+    const bool tail_tile_ok = a.tile < 0 || kTiles[a.tile].spread == 0 || kTiles[a.tile].spread == 4;
+    auto needs_pack = [&](bool kcontig, const void *ptr, int64_t ld, int64_t stride) {
+        if (!kcontig) return true;
+        const bool mis = misaligned16(ptr) || bytes_of(ld) % 16 || (batch > 1 && bytes_of(stride) % 16);
+        if (!in_place) return mis || ktail;
+        return ktail && !tail_tile_ok;
+    };
+    P.pack_a = needs_pack(a_row, a.A, a.lda, a.stride_a);
+    P.pack_b = needs_pack(b_col, a.B, a.ldb, a.stride_b);
     /* the repack passes move whole bytes per element */
     if ((fp4 || fp6) && (P.pack_a || P.pack_b)) return GEMM355_EUNSUPPORTED;
     if (conv) {
@@ -427,6 +438,10 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
         P.stride_b_b = bytes_of(a.stride_b);
     }
     P.Kb = (int32_t)std::min<int64_t>(cdiv(kbytes, 16) * 16, kMaxDim);
+    /* an operand read in place whose K ends inside a chunk: its bytes past
+     * K are cleared in LDS, and only tiles with that clearing are planned */
+    const bool tail_in_place = ktail && (!P.pack_a || !P.pack_b);
+    P.Kv = tail_in_place ? (int32_t)std::min<int64_t>(kbytes, kMaxDim) : 0;
     P.pub.repack = (P.pack_a ? 1 : 0) | (P.pack_b ? 2 : 0);
     if (256 * P.lda_b > kMaxOffset || 256 * P.ldb_b > kMaxOffset) return GEMM355_EUNSUPPORTED;
     if (256 * a.ldc * out_esize > kMaxOffset) return GEMM355_EUNSUPPORTED;
@@ -437,6 +452,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
         const TileCfg &cfg = kTiles[t];
         if (cfg.dtype_class != dclass || cfg.op != want_op) continue;
         if (a.tile >= 0 && a.tile != t) continue;
+        if (P.Kv && cfg.spread != 0 && cfg.spread != 4) continue;
         Cand base;
         base.tile = t;
         base.tiles_m = cdiv(std::max<int64_t>(M, 1), cfg.TM);

@@ -236,6 +236,40 @@ def test_all_layouts(fmt, K):
     assert np.array_equal(C1, C2.T)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_rows_in_place_misaligned_with_nan_padding(fmt):
+    """K-contiguous rows read in place: the operands start one element past
+    a 16-byte boundary, rows are lda = K + 3 and ldb = K + 5 elements apart
+    (no row 16-byte aligned), K = 77 ends inside a 16-byte chunk, and every
+    element outside the matrices (the row padding and what follows the last
+    row) is a NaN code.  The bytes of the last chunk past K must be cleared
+    before the product, so exact-integer results are the oracle's bits
+    through every tile that reads rows in place, split-K and the persistent
+    grid included."""
+    M, N, K = 130, 200, 77
+    lda, ldb = K + 3, K + 5
+    ops = int_ops(M, N, K, fmt, 53)
+    nan = np.uint16(0x7FC0) if fmt == "bf16" else np.uint8(0x7F)
+    dt = np.uint16 if fmt == "bf16" else np.uint8
+
+    def padded(codes, rows, ld):
+        buf = np.full(1 + rows * ld + 64, nan, dtype=dt)
+        buf[1:1 + rows * ld].reshape(rows, ld)[:, :K] = codes
+        return H.dev(buf)
+
+    Abuf, Bbuf = padded(ops.A, M, lda), padded(ops.B, N, ldb)
+    ref, _ = H.oracle_full(ops, alpha=1.0)
+    tiles = [t for t in (BF16_TILES if fmt == "bf16" else E4M3_TILES)
+             if g.gemm355_plan(g.make_args(M, N, K, A=Abuf[1:], lda=lda, B=Bbuf[1:], ldb=ldb,
+                                           C=0x200000000000, dtype=H.out_dtype(fmt, "f32"), tile=t))["repack"] == 0]
+    assert len(tiles) >= 5
+    for tile in [-1] + tiles:
+        for knobs in (dict(split_k=1, persistent=0), dict(split_k=3), dict(persistent=1)):
+            H.say(fmt, "in place, NaN padding, tile", tile, knobs)
+            C = H.run(ops, out="f32", tile=tile, A_dev=Abuf[1:], B_dev=Bbuf[1:], lda=lda, ldb=ldb, **knobs)
+            assert np.array_equal(C, ref), (fmt, tile, knobs)
+
+
 def test_persistent_on_off_bit_identical():
     """Same tile and the same uniform split: the persistent loop only changes
     which workgroup runs a unit, so results are bit-identical."""
