@@ -151,7 +151,7 @@ class Case:
         p = self.plan
         if not p["units"]:
             return None
-        stamps = torch.zeros(4 * p["units"], dtype=torch.int64, device="cuda")
+        stamps = torch.zeros(6 * p["units"], dtype=torch.int64, device="cuda")
         a = self.args[0]
         a.unit_stamps = stamps.data_ptr()
         try:
@@ -159,7 +159,7 @@ class Case:
             torch.cuda.synchronize()
         finally:
             a.unit_stamps = None
-        st = stamps.view(-1, 4).cpu().numpy().astype("float64")
+        st = stamps.view(-1, 6).cpu().numpy().astype("float64")
         span = st[:, 1].max() - st[:, 0].min()
         busy_rt = (st[:, 1] - st[:, 0]).sum()
         cycles = (st[:, 3] - st[:, 2]).sum()
@@ -168,9 +168,15 @@ class Case:
         # dense MFMA FLOPs per clock of one compute unit, shared by b groups
         per_clk = (4096.0 if self.fmt == "bf16" else 8192.0) / p["b"]
         ideal = 2.0 * p["T_M"] * p["T_N"] * p["T_K"] * p["G"] * p["nK"] / per_clk
+        n = float(len(st))
         return {"eta": float(busy_rt / (p["S"] * p["b"] * span)),
                 "sclk_mhz": float(100.0 * cycles / busy_rt),
-                "mfma_cycle_eff": float(ideal / cycles)}
+                "mfma_cycle_eff": float(ideal / cycles),
+                # mean shader cycles per unit: main loop (prologue included),
+                # epilogue until its stores are issued, and their completion
+                "unit_cycles": {"loop": round(float((st[:, 4] - st[:, 2]).sum()) / n),
+                                "epilogue": round(float((st[:, 5] - st[:, 4]).sum()) / n),
+                                "store_drain": round(float((st[:, 3] - st[:, 5]).sum()) / n)}}
 
     def step(self, stream):
         a = self.args[self.i % self.copies]
@@ -611,6 +617,7 @@ def main():
                 detail[-1]["eta_measured"] = None if me is None else round(me["eta"], 4)
                 detail[-1]["sclk_mhz"] = None if me is None else round(me["sclk_mhz"], 0)
                 detail[-1]["mfma_cycle_eff"] = None if me is None else round(me["mfma_cycle_eff"], 4)
+                detail[-1]["unit_cycles"] = None if me is None else me["unit_cycles"]
                 if c is not head:
                     del c
                     torch.cuda.empty_cache()

@@ -824,6 +824,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * The lane index is re-materialised here so the compiler cannot
          * hoist the epilogue's addresses above the main loop and hold them
          * in registers across it. */
+        /* per-unit clock hook: wave 0's main loop ends here */
+        const uint64_t clk_loop = p.stamps ? __builtin_amdgcn_s_memtime() : 0;
         int el = lane_id();
         asm volatile("" : "+v"(el));
         const int ecol = el % MI, ehi = el / MI;
@@ -1019,17 +1021,21 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             asm volatile("" ::: "memory");
         }
         if (p.stamps) {
+            /* wave 0 has issued its epilogue's stores */
+            const uint64_t clk_epi = __builtin_amdgcn_s_memtime();
             /* every wave's stores of this unit have completed */
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             const uint64_t stamp1 = __builtin_amdgcn_s_memrealtime();
             const uint64_t clk1 = __builtin_amdgcn_s_memtime();
             if (wave == 0 && lane_id() == 0) {
-                uint64_t *st = p.stamps + 4 * (int64_t)u;
+                uint64_t *st = p.stamps + 6 * (int64_t)u;
                 st[0] = stamp0;
                 st[1] = stamp1;
                 st[2] = clk0;
                 st[3] = clk1;
+                st[4] = clk_loop;
+                st[5] = clk_epi;
             }
         }
     }
@@ -1065,6 +1071,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
      * not read here */
     const bool live = e4 < tile_f4 && m0 + (int32_t)(e4 * 4 / r.TN) < r.M && n0 + (int32_t)(e4 * 4 % r.TN) < r.N;
     const int32_t s_lo = (int32_t)((int64_t)g * nsl / SG), s_hi = (int32_t)((int64_t)(g + 1) * nsl / SG);
+    /* the scales are fetched while the slices load */
+    float alpha = 1.0f;
+    if (r.scale_a) alpha *= r.scale_a[un.batch];
+    if (r.scale_b) alpha *= r.scale_b[un.batch];
     f32x4 sum = f32x4{};
     if (live) {
         const f32x4 *src = (const f32x4 *)(r.ws + (int64_t)q * nsl * r.TM * r.TN) + e4;
@@ -1082,11 +1092,23 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
     part[threadIdx.x] = sum;
     __syncthreads();
     if (g != 0 || !live) return;
-    for (int32_t h = 1; h < SG; ++h) sum += part[h * P + pos];
-
-    float alpha = 1.0f;
-    if (r.scale_a) alpha *= r.scale_a[un.batch];
-    if (r.scale_b) alpha *= r.scale_b[un.batch];
+    /* the group sums in ascending order, read seven or eight at a time (SG
+     * is a power of two): groups 1 .. 7, then 8 .. 15, ... */
+    if (SG >= 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) v[j] = part[j * P + pos];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) sum += v[j];
+        for (int32_t h = 8; h < SG; h += 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = part[(h + j) * P + pos];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sum += v[j];
+        }
+    } else {
+        for (int32_t h = 1; h < SG; ++h) sum += part[h * P + pos];
+    }
     const int64_t e = e4 * 4;
     const int32_t row = m0 + (int32_t)(e / r.TN);
     const int32_t col0 = n0 + (int32_t)(e % r.TN);

@@ -156,15 +156,18 @@ typedef struct gemm355_args {
                                  repacked operands, 256-byte aligned
                                  (EALIGN otherwise); NULL: library-owned  */
     size_t workspace_bytes;   /* size of `workspace`                      */
-    uint64_t *unit_stamps;    /* device uint64 [4 * plan.units] or NULL.
+    uint64_t *unit_stamps;    /* device uint64 [6 * plan.units] or NULL.
                                  When set, work unit u records the device
                                  real-time clock (100 MHz) when its
-                                 workgroup starts it at [4u] and after its
-                                 stores have completed at [4u + 1], and the
+                                 workgroup starts it at [6u] and after its
+                                 stores have completed at [6u + 1], and the
                                  shader clock counter (cycles) at the same
-                                 two points at [4u + 2] and [4u + 3], for
+                                 two points at [6u + 2] and [6u + 3], when
+                                 its first wavefront leaves the main loop
+                                 at [6u + 4] and when that wavefront has
+                                 issued its output stores at [6u + 5], for
                                  measuring how evenly the units fill the
-                                 device and how many cycles a unit takes.
+                                 device and where a unit's cycles go.
                                  8-byte aligned (EALIGN).                  */
     /* Block scales of the MX dtypes (NULL otherwise, else EINVAL): E8M0
      * bytes, dense, block_scale_a[g][i][k / 32] for row i of A and

@@ -475,8 +475,9 @@ def test_workload_e4m3_batch64():
 
 def test_unit_stamps_cover_every_unit():
     """The per-unit clock hook: every unit of a persistent split schedule
-    records start <= end, the product is unchanged by recording, and the
-    busy fraction the stamps give lies in (0, 1]."""
+    records start <= loop end <= stores issued <= end, the product is
+    unchanged by recording, and the busy fraction the stamps give lies in
+    (0, 1]."""
     M, N, K = 1500, 1300, 2048
     ops = ops_from(M, N, K, "bf16", 37, dist="normal")
     A, B = H.dev(ops.A), H.dev(ops.B)
@@ -488,15 +489,17 @@ def test_unit_stamps_cover_every_unit():
         p = g.gemm355_plan(args)
         H.say("stamps tile", tile, "split", split, "persistent", pers, "units", p["units"], "grid", p["grid"])
         g.gemm355_gemm_ex(args)
-        stamps = torch.zeros(4 * p["units"], dtype=torch.int64, device="cuda")
+        stamps = torch.zeros(6 * p["units"], dtype=torch.int64, device="cuda")
         args2 = g.make_args(M, N, K, A=A, B=B, C=C1, dtype=g.BF16_F32, tile=tile, split_k=split,
                             persistent=pers, unit_stamps=stamps)
         g.gemm355_gemm_ex(args2)
         torch.cuda.synchronize()
         assert torch.equal(C0, C1)
-        st = stamps.view(-1, 4).cpu().numpy()
+        st = stamps.view(-1, 6).cpu().numpy()
         assert (st[:, 0] > 0).all() and (st[:, 1] >= st[:, 0]).all()
         assert (st[:, 3] > st[:, 2]).all()
+        # start <= main loop done <= stores issued <= stores complete (shader clock)
+        assert (st[:, 4] >= st[:, 2]).all() and (st[:, 5] >= st[:, 4]).all() and (st[:, 3] >= st[:, 5]).all()
         # shader cycles per real-time tick (100 MHz): a clock between 0.3 and 3 GHz
         mhz = 100.0 * float((st[:, 3] - st[:, 2]).sum()) / max(float((st[:, 1] - st[:, 0]).sum()), 1.0)
         H.say("  shader clock from the stamps (MHz)", mhz)
