@@ -85,12 +85,21 @@ def parse():
 
 
 def copy_reference(nbytes: int) -> None:
+    """A plain device-to-device copy, 5 times: the reference kernel for
+    scaling the HBM byte counters, and the stream rate a simple kernel
+    reaches (each copy reads and writes nbytes)."""
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(5):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 5
+    print(json.dumps({"copy_bytes": nbytes, "us_per_copy": round(us, 2),
+                      "read_plus_write_tb_s": round(2 * nbytes / (us * 1e-6) / 1e12, 3)}), flush=True)
     log("copy reference: 5 x %d bytes" % nbytes)
 
 
