@@ -45,6 +45,13 @@ constexpr double kPeakFp8PerCu = 5033.2e12 / 256.0;
 constexpr double kPeakFp4PerCu = 10066.3e12 / 256.0;
 constexpr double kHbmBytesPerSec = 5.0e12;            /* sustained, planning only */
 constexpr double kExtraPassSec = 4.0e-6;              /* one launch: main, combine or repack */
+/* Rows that are not 16-byte aligned and read in place turn every copy of a
+ * row (once per tile column of the product, or row for B) into unaligned
+ * accesses over two lines.  From this dense-MFMA time at peak up, one
+ * repack pass costs less than those re-reads (bf16 and E4M3 products from
+ * 2500 x 2500 x 2501 up ran 15-31 % faster repacked; at 2000 x 2000 x 2001
+ * and below, reading in place was as fast or faster). */
+constexpr double kRepackMisalignedSec = 10.0e-6;
 constexpr double kCopyBytesPerSecPerCu = 100.0e9;     /* L2 -> LDS copies per compute unit */
 constexpr double kUnitSec = 3.0e-6;                   /* per unit run in turn on one slot: pipeline
                                                          fill and epilogue */
@@ -393,22 +400,28 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
     }
 
     /* Operand views of the main loop: K-contiguous rows.  bf16 and 8-bit
-     * rows are read in place whatever their alignment (16-byte buffer
-     * loads take any byte address); if K ends inside a 16-byte chunk, the
-     * copy schedules that clear the chunk's bytes past K in LDS (0 and 4)
-     * are the only candidates.  Other operands (the transposed layouts;
-     * block-scaled rows that are not 16-byte aligned or do not end on a
-     * chunk) are repacked, zero-filled to a whole number of K-tiles. */
+     * rows are read in place (16-byte buffer loads take any byte address),
+     * except rows that are not 16-byte aligned in products large enough
+     * for a repack pass to pay (kRepackMisalignedSec); if K ends inside a
+     * 16-byte chunk, the copy schedules that clear the chunk's bytes past K
+     * in LDS (0 and 4) are the only candidates.  Other operands (the
+     * transposed layouts; block-scaled rows that are not 16-byte aligned or
+     * do not end on a chunk) are repacked, zero-filled to a whole number of
+     * K-tiles. */
     auto bytes_of = [ebits](int64_t elems) { return elems * ebits / 8; };
     const int64_t kbytes = bytes_of(K);
     const int64_t packed_ld = cdiv(std::max<int64_t>(kbytes, 1), 128) * 128;
     const bool in_place = (dclass == 0 || dclass == 1) && !conv;
     const bool ktail = kbytes % 16 != 0;
     const bool tail_tile_ok = a.tile < 0 || kTiles[a.tile].spread == 0 || kTiles[a.tile].spread == 4;
+    const double peak_cu = fp4 || fp6 ? kPeakFp4PerCu : dclass ? kPeakFp8PerCu : kPeakBf16PerCu;
+    const bool repack_misaligned =
+        2.0 * (double)M * (double)N * (double)K * (double)batch / (peak_cu * S) >= kRepackMisalignedSec;
     auto needs_pack = [&](bool kcontig, const void *ptr, int64_t ld, int64_t stride) {
         if (!kcontig) return true;
         const bool mis = misaligned16(ptr) || bytes_of(ld) % 16 || (batch > 1 && bytes_of(stride) % 16);
         if (!in_place) return mis || ktail;
+        if (mis && repack_misaligned) return true;
         return ktail && !tail_tile_ok;
     };
     P.pack_a = needs_pack(a_row, a.A, a.lda, a.stride_a);

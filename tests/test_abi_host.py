@@ -264,15 +264,25 @@ def test_plan_fits_short_k_and_narrow_shapes(g):
 
 
 def test_repack_decisions(g):
-    """K-contiguous bf16 / 8-bit rows are read in place at any alignment
-    (K ending inside a 16-byte chunk plans only tiles that clear the
-    chunk's bytes past K); the transposed layouts are repacked, and so are
-    block-scaled rows that are not 16-byte aligned, and in-place rows with
-    a K tail under a forced tile without the clearing."""
+    """K-contiguous bf16 / 8-bit rows are read in place (K ending inside a
+    16-byte chunk plans only tiles that clear the chunk's bytes past K),
+    except rows that are not 16-byte aligned in products whose dense-MFMA
+    time at peak reaches 10 us; the transposed layouts are repacked, and so
+    are block-scaled rows that are not 16-byte aligned, and in-place rows
+    with a K tail under a forced tile without the clearing."""
     base = dict(A=0x10000, B=0x1000000000, C=0x200000000000, cus=256)
     p = g.gemm355_plan(g.make_args(1000, 3000, 777, **base))       # rows 2-byte aligned, K tail
     assert p["repack"] == 0 and g.gemm355_tile_info(p["tile"])["stages"] >= 2
     assert g.gemm355_plan(g.make_args(1000, 3000, 776, **base))["repack"] == 0
+    # misaligned rows around the threshold: 2 M N K / 2516.6 TFLOP/s = 10 us at M N K = 12.58e9
+    assert g.gemm355_plan(g.make_args(2000, 2000, 2001, **base))["repack"] == 0      # 8.0e9
+    assert g.gemm355_plan(g.make_args(2500, 2500, 2501, **base))["repack"] == 3      # 15.6e9
+    assert g.gemm355_plan(g.make_args(2500, 2500, 2504, **base))["repack"] == 0      # rows 16-byte aligned
+    assert g.gemm355_plan(g.make_args(2500, 2500, 2504, lda=2505, **base))["repack"] == 1
+    assert g.gemm355_plan(g.make_args(2500, 2500, 2501, dtype=g.E4M3_F32, **base))["repack"] == 0  # fp8 peak twice
+    assert g.gemm355_plan(g.make_args(3200, 3200, 3201, dtype=g.E4M3_F32, **base))["repack"] == 3
+    # on 64 compute units the same product takes four times as long at peak
+    assert g.gemm355_plan(g.make_args(2000, 2000, 2001, **dict(base, cus=64)))["repack"] == 3
     assert g.gemm355_plan(g.make_args(64, 64, 64, layout=g.A_COL_B_COL, **base))["repack"] == 1
     assert g.gemm355_plan(g.make_args(64, 64, 64, layout=g.A_ROW_B_ROW, **base))["repack"] == 2
     b2 = dict(base, A=0x10002)

@@ -270,6 +270,35 @@ def test_rows_in_place_misaligned_with_nan_padding(fmt):
             assert np.array_equal(C, ref), (fmt, tile, knobs)
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("bf16", 2600, 2500, 2001), ("e4m3", 3200, 3200, 3201)])
+def test_rows_misaligned_repacked_large(fmt, M, N, K):
+    """Rows that are not 16-byte aligned in a product large enough for the
+    planner to repack them (dense-MFMA time at peak of 10 us or more): the
+    operands start one element past a 16-byte boundary, rows are K + 3 and
+    K + 5 elements apart, K ends inside a 16-byte chunk and every element
+    outside the matrices is a NaN code.  The repack pass must copy exactly
+    the K elements of each row and zero the rest of its padded row, so
+    exact-integer results are the oracle's bits."""
+    lda, ldb = K + 3, K + 5
+    ops = int_ops(M, N, K, fmt, 57, lo=-1, hi=1)
+    nan = np.uint16(0x7FC0) if fmt == "bf16" else np.uint8(0x7F)
+    dt = np.uint16 if fmt == "bf16" else np.uint8
+
+    def padded(codes, rows, ld):
+        buf = np.full(1 + rows * ld + 64, nan, dtype=dt)
+        buf[1:1 + rows * ld].reshape(rows, ld)[:, :K] = codes
+        return H.dev(buf)
+
+    Abuf, Bbuf = padded(ops.A, M, lda), padded(ops.B, N, ldb)
+    p = g.gemm355_plan(g.make_args(M, N, K, A=Abuf[1:], lda=lda, B=Bbuf[1:], ldb=ldb, C=0x200000000000,
+                                   dtype=H.out_dtype(fmt, "f32")))
+    H.say(fmt, M, N, K, "misaligned rows: repack", p["repack"], "tile", p["tile"])
+    assert p["repack"] == 3
+    ref, _ = H.oracle_full(ops, alpha=1.0)
+    C = H.run(ops, out="f32", A_dev=Abuf[1:], B_dev=Bbuf[1:], lda=lda, ldb=ldb)
+    assert np.array_equal(C, ref)
+
+
 def test_persistent_on_off_bit_identical():
     """Same tile and the same uniform split: the persistent loop only changes
     which workgroup runs a unit, so results are bit-identical."""
