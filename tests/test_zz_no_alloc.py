@@ -83,3 +83,44 @@ def test_no_alloc_rejects_workspace_and_oversized_plans():
     assert e.value.status == g.ETOOBIG
     torch.cuda.synchronize()
     assert torch.isnan(C).all() and torch.isnan(Cb).all()   # nothing was launched
+
+
+def test_no_alloc_replays_in_a_captured_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture.  A product that uses the fixed array twice over (A repacked
+    into it, then a 4-way split whose partial sums it holds and a combine
+    pass) is captured once and replayed three times, with an eager call of
+    another shape on the same array before each replay; every replay's C
+    equals the eager call's bit for bit.  The library records no memset and
+    makes no allocation while captured."""
+    M, N, K = 300, 200, 3000
+    ops = inputs.make_operands(M, N, K, "bf16", "normal", 67, 68)
+    At = H.dev(np.ascontiguousarray(ops.A.T))
+    B = H.dev(ops.B)
+    kn = dict(layout=g.A_COL_B_COL, split_k=4)
+    C_e = H.empty_c(1, M, N, "f32")
+    C_g = H.empty_c(1, M, N, "f32")
+    a_e = g.make_args(M, N, K, A=At, lda=M, B=B, C=C_e, **kn)
+    a_g = g.make_args(M, N, K, A=At, lda=M, B=B, C=C_g, **kn)
+    p = g.gemm355_plan(a_g)
+    assert p["repack"] == 1 and p["split"] == 4
+    # the first call on the device looks up the array's address: before the capture
+    g.gemm355_gemm_noalloc(a_e)
+    torch.cuda.synchronize()
+    other = inputs.make_operands(190, 130, 640, "bf16", "normal", 69, 70)
+    C_o = H.empty_c(1, 190, 130, "f32")
+    a_o = g.make_args(190, 130, 640, A=H.dev(other.A), B=H.dev(other.B), C=C_o, split_k=3)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        g.gemm355_gemm_noalloc(a_g, torch.cuda.current_stream().cuda_stream)
+    for r in range(3):
+        C_g.fill_(float("nan"))
+        g.gemm355_gemm_noalloc(a_o)
+        torch.cuda.synchronize()
+        H.say("graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C_g, C_e), r
+    C_ref, W = H.oracle_full(ops)
+    H.check(C_g.double().cpu().numpy(), C_ref, W, "bf16", "captured graph")
