@@ -1135,16 +1135,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams r)
  * [0, nb0) work on the first, the rest on the second.
  *
  * pack_rows (K-contiguous source whose rows are misaligned or whose K is
- * not a whole number of 16-byte chunks): one wavefront per row.  The row
- * is read through a buffer resource based at the 16-byte boundary at or
- * below the row's first byte and ending at the 16-byte boundary at or above
- * its last byte, so every 16-byte block read lies in a block that holds a
- * byte of the row (never past the allocation) and blocks beyond read as
- * zero.  Output chunk c is bytes [sh + 16c, sh + 16c + 16) of that window
- * (sh = the row's offset from the boundary): two aligned 16-byte loads and
- * a byte funnel shift.  A lane takes chunks lane + 64i and issues the loads
- * of four of them before the first store.  Bytes at or beyond K are
- * cleared.
+ * not a whole number of 16-byte chunks): one lane per 16-byte chunk of the
+ * padded output, the chunks of consecutive rows numbered consecutively
+ * (row r, chunk c is chunk r * cpr + c), 256 per workgroup, a workgroup
+ * within one batch entry.  A chunk wholly inside the row is one 16-byte
+ * load at its own byte offset (buffer loads take any byte address); the
+ * chunk that holds the row's last n < 16 bytes loads the row's last 16
+ * bytes instead (never past the row) and shifts them down by 16 - n; rows
+ * shorter than 16 bytes are read element by element.  Bytes at or beyond
+ * K are zero.
  */
 __device__ __forceinline__ i32x4 pack_chunk(const i32x4 lo, const i32x4 hi, uint32_t q, uint32_t rb, uint32_t valid)
 {
@@ -1173,45 +1172,45 @@ __device__ __forceinline__ i32x4 pack_chunk(const i32x4 lo, const i32x4 hi, uint
 
 __device__ __forceinline__ void pack_rows(const PackParams &pk, int64_t blk)
 {
-    constexpr int NC = 4; /* chunks per lane per round */
-    const int64_t row_id = blk * 4 + (threadIdx.x >> 6);
-    if (row_id >= (int64_t)pk.batch * pk.rows) return;
-    const int lane = threadIdx.x & 63;
-    const int64_t g = row_id / pk.rows, r = row_id - g * pk.rows;
-    const uint8_t *row = (const uint8_t *)pk.src + (g * pk.stride + r * pk.ld) * pk.esize;
+    const int64_t cpr = pk.ldd_bytes / 16;
+    const int64_t per_entry = (int64_t)pk.rows * cpr;
+    const int64_t bpe = (per_entry + 255) / 256;
+    const int64_t g = blk / bpe;
+    /* the workgroup's first chunk and its row r0 (within batch entry g) */
+    const int64_t q0 = (blk - g * bpe) * 256;
+    const int64_t r0 = q0 / cpr;
+    if (q0 + (int64_t)threadIdx.x >= per_entry) return;
+    const uint32_t ql = (uint32_t)(q0 - r0 * cpr) + threadIdx.x;
+    const uint32_t dr = ql / (uint32_t)cpr, c = ql - dr * (uint32_t)cpr;
+    const int64_t r = r0 + dr;
+    const int64_t ld_bytes = pk.ld * pk.esize;
+    const uint8_t *entry = (const uint8_t *)pk.src + g * pk.stride * pk.esize;
     const uint32_t kbytes = (uint32_t)pk.K * (uint32_t)pk.esize;
-    const uintptr_t ra = (uintptr_t)row;
-    const uint32_t sh = (uint32_t)(ra & 15u);
-    const uint8_t *base = (const uint8_t *)(ra - sh);
-    const uint32_t nrec = (sh + kbytes + 15u) & ~15u;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, (int)nrec, 0x00020000);
-    uint8_t *drow = pk.dst + g * pk.dst_stride_bytes + r * pk.ldd_bytes;
-    const uint32_t q = sh >> 2, rb = sh & 3u;
-    const uint32_t chunks = (uint32_t)(pk.ldd_bytes / 16);
-    for (uint32_t c0 = (uint32_t)lane; c0 < chunks; c0 += 64 * NC) {
-        i32x4 lo[NC], hi[NC];
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            /* only chunks holding bytes of the row are read (a wave whose
-             * lanes are all past them issues nothing) */
-            const uint32_t off = (c0 + 64u * i) * 16u;
-            lo[i] = i32x4{0, 0, 0, 0};
-            hi[i] = i32x4{0, 0, 0, 0};
-            if (off < kbytes) {
-                lo[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-                hi[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
-            }
+    const uint32_t off = c * 16u;
+    /* a buffer resource based at row r0 serves the whole workgroup while
+     * the rows it spans (256 / cpr + 2 at most) stay within 31-bit offsets;
+     * otherwise (short rows far apart) bytes are read one by one */
+    const bool near = (256 / cpr + 2) * ld_bytes < ((int64_t)1 << 31);
+    i32x4 out = i32x4{0, 0, 0, 0};
+    if (near && kbytes >= 16u) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(entry + r0 * ld_bytes);
+        const uint32_t rowoff = dr * (uint32_t)ld_bytes;
+        if (off + 16u <= kbytes) {
+            out = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, rowoff + off, 0, 0));
+        } else if (off < kbytes) {
+            const uint32_t n = kbytes - off, sh = 16u - n;
+            const i32x4 w =
+                __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, rowoff + kbytes - 16u, 0, 0));
+            out = pack_chunk(w, i32x4{0, 0, 0, 0}, sh >> 2, sh & 3u, n);
         }
-#pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const uint32_t c = c0 + 64u * i;
-            if (c >= chunks) break;
-            const uint32_t off = c * 16u;
-            const i32x4 out = off < kbytes ? pack_chunk(lo[i], hi[i], q, rb, kbytes - off) : i32x4{0, 0, 0, 0};
-            *(i32x4 *)(drow + off) = out;
-        }
+    } else if (off < kbytes) {
+        const uint8_t *row = entry + r * ld_bytes;
+        const uint32_t n = kbytes - off < 16u ? kbytes - off : 16u;
+        uint32_t wd[4] = {0, 0, 0, 0};
+        for (uint32_t b = 0; b < n; ++b) wd[b >> 2] |= (uint32_t)row[off + b] << (8 * (b & 3));
+        out = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
     }
+    *(i32x4 *)(pk.dst + g * pk.dst_stride_bytes + r * pk.ldd_bytes + off) = out;
 }
 
 /*
@@ -1481,7 +1480,7 @@ hipError_t launch_reduce(const ReduceParams &r0, int32_t tiles, hipStream_t stre
 
 static int64_t pack_blocks(const PackParams &pk)
 {
-    if (pk.kmajor) return ((int64_t)pk.batch * pk.rows + 3) / 4;
+    if (pk.kmajor) return (int64_t)pk.batch * (((int64_t)pk.rows * (pk.ldd_bytes / 16) + 255) / 256);
     const int64_t kblocks = (pk.ldd_bytes / pk.esize + 63) / 64;
     const int64_t rblocks = (pk.rows + 63) / 64;
     return (int64_t)pk.batch * rblocks * kblocks;

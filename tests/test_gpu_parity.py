@@ -299,6 +299,39 @@ def test_rows_misaligned_repacked_large(fmt, M, N, K):
     assert np.array_equal(C, ref)
 
 
+@pytest.mark.parametrize("fmt,K", [("bf16", 5), ("bf16", 13), ("bf16", 77), ("e4m3", 7), ("e4m3", 29),
+                                   ("e4m3", 141)])
+def test_row_repack_edges(fmt, K):
+    """The row repack pass on its edge cases: a tile whose copy schedule
+    does not clear K tails is forced, so rows that end inside a 16-byte
+    chunk are repacked; the rows start one element past a 16-byte boundary
+    and lie K + 3 / K + 5 elements apart with NaN codes in between.  K
+    covers rows shorter than one chunk (read byte by byte), rows of one
+    whole chunk and a partial one, and longer rows; every output is the
+    oracle's exact sum."""
+    M, N = 130, 200
+    lda, ldb = K + 3, K + 5
+    ops = int_ops(M, N, K, fmt, 59)
+    nan = np.uint16(0x7FC0) if fmt == "bf16" else np.uint8(0x7F)
+    dt = np.uint16 if fmt == "bf16" else np.uint8
+
+    def padded(codes, rows, ld):
+        buf = np.full(1 + rows * ld + 64, nan, dtype=dt)
+        buf[1:1 + rows * ld].reshape(rows, ld)[:, :K] = codes
+        return H.dev(buf)
+
+    Abuf, Bbuf = padded(ops.A, M, lda), padded(ops.B, N, ldb)
+    cls = 0 if fmt == "bf16" else 1
+    tile = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["dtype_class"] == cls
+            and g.gemm355_tile_info(t)["op"] == 0
+            and g.gemm355_plan(g.make_args(M, N, K, A=Abuf[1:], lda=lda, B=Bbuf[1:], ldb=ldb, C=0x200000000000,
+                                           dtype=H.out_dtype(fmt, "f32"), tile=t))["repack"] == 3][0]
+    H.say(fmt, "K", K, "row repack through forced tile", tile)
+    ref, _ = H.oracle_full(ops, alpha=1.0)
+    C = H.run(ops, out="f32", tile=tile, A_dev=Abuf[1:], B_dev=Bbuf[1:], lda=lda, ldb=ldb)
+    assert np.array_equal(C, ref)
+
+
 def test_persistent_on_off_bit_identical():
     """Same tile and the same uniform split: the persistent loop only changes
     which workgroup runs a unit, so results are bit-identical."""
