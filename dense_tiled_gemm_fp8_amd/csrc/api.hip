@@ -626,7 +626,7 @@ int32_t gemm355_num_tiles(void) { return kNumTiles; }
 
 gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_M, int32_t *T_N,
                                  int32_t *T_K, int32_t *stages, int32_t *waves, int32_t *lds_bytes,
-                                 int32_t *b_max, int32_t *op)
+                                 int32_t *b_max, int32_t *op, int32_t *schedule)
 {
     if (tile < 0 || tile >= kNumTiles) return GEMM355_EINVAL;
     const TileCfg &c = kTiles[tile];
@@ -639,6 +639,7 @@ gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_
     if (lds_bytes) *lds_bytes = c.lds_bytes;
     if (b_max) *b_max = resident_workgroups(tile);
     if (op) *op = c.op;
+    if (schedule) *schedule = c.spread;
     return GEMM355_OK;
 }
 

@@ -164,7 +164,7 @@ __device__ __forceinline__ float unit_alpha(const GemmParams &p, int32_t batch)
  * RB bytes of K per row (64 or 128: 32/64 bf16, 64/128 8-bit, 256 FP4 or 128
  * FP6 values); the LDS holds a ring of STAGES K-tiles.  Template knobs
  * beyond the shape: EL, the element class (bf16, 8-bit, block-scaled 8-, 4-
- * and 6-bit); SPREAD, the copy schedule (0-3, tiles.h); OP, the operation
+ * and 6-bit); SPREAD, the copy schedule (0-5, tiles.h); OP, the operation
  * (matrix product, or a convolution whose A rows are gathered from NHWC
  * images); FMT, the operand-format pair of the 8- and 6-bit classes.
  *
@@ -256,8 +256,20 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
     static_assert(!MX || (SPREAD == 0 && RB == 128 && MI == 32 && TM % 64 == 0 && SC * 64 * NW == SW * (TM + TN)),
                   "block scales: whole dwords per row and K-tile, whole 64-row copies per wavefront");
     constexpr int NB = SPREAD == 2 ? 4 : 2;     /* fragment buffers */
+    /* SPREAD 5: schedule 0 with B's ring one stage deeper than A's, the
+     * spare LDS of a two-stage 256 x 256 tile.  A's stages sit at s A_BYTES,
+     * B's at B_BASE + t B_BYTES.  B's copies of K-tile kt+2 then go in the
+     * first K-step of K-tile kt (B's stage of kt-1 is free since the barrier
+     * in kt-1's middle) and A's in its last step, as in schedule 0: half the
+     * copies per step, each with at least a K-tile to land.  Otherwise B
+     * follows A in each stage. */
+    static_assert(SPREAD != 5 || (!MX && !FP6 && !CONV && STAGES == 2 && KSTEPS == 2),
+                  "deeper B ring: two stages of two K-steps");
+    constexpr int BST = SPREAD == 5 ? STAGES + 1 : STAGES;
+    constexpr int B_BASE = SPREAD == 5 ? STAGES * A_BYTES : A_BYTES;
+    constexpr int LDS_BYTES = SPREAD == 5 ? STAGES * A_BYTES + BST * B_BYTES : STAGES * STAGE_BYTES;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
@@ -415,7 +427,9 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 }
             }
         };
-        auto dma = [&](auto dc, uint32_t so, uint32_t kb, const KV &kv) __attribute__((always_inline)) {
+        /* copy d of a K-tile into the stage whose A part is at byte so and B
+         * part at byte sob */
+        auto dma = [&](auto dc, uint32_t so, uint32_t sob, uint32_t kb, const KV &kv) __attribute__((always_inline)) {
             constexpr int d = decltype(dc)::value;
             constexpr int di = d < A_LOADS ? d : d - A_LOADS;
             const bool ok = kv.v[TWO ? di & 1 : 0];
@@ -428,7 +442,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             } else if constexpr (d < A_LOADS) {
                 dma16<d * CW * 1024>(ra, dst, ok ? aoff[d] + kb : kOOB);
             } else if constexpr (d < A_LOADS + B_LOADS) {
-                dma16<A_BYTES + (d - A_LOADS) * CW * 1024>(rb, dst, ok ? boff[di] + kb : kOOB);
+                dma16<(d - A_LOADS) * CW * 1024>(rb, smem_base + sob + cw * 1024, ok ? boff[di] + kb : kOOB);
             } else {
                 /* K-tile kb / KTB of the regrouped scales */
                 constexpr int q = d - A_LOADS - B_LOADS;
@@ -441,9 +455,10 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * iteration i (in the stage at so) have landed, each lane that
          * fetched such a chunk clears its bytes past K in LDS, before the
          * barrier that shows the stage to the other waves.  Only copy
-         * schedules 0 and 4 (tile and prologue waits below) take this path. */
-        auto zero_tail = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
-            if constexpr (!FP6 && !MX && !CONV && (SPREAD == 0 || SPREAD == 4)) {
+         * schedules 0, 4 and 5 (tile and prologue waits below) take this
+         * path. */
+        auto zero_tail = [&](uint32_t so, uint32_t sob, int32_t i) __attribute__((always_inline)) {
+            if constexpr (!FP6 && !MX && !CONV && (SPREAD == 0 || SPREAD == 4 || SPREAD == 5)) {
                 const int32_t kb = ktile(i) * KTB;
                 if (p.Kv > 0 && i < nkt && kb + KTB > p.Kv) {
                     unroll<A_LOADS + B_LOADS>([&](auto dc) __attribute__((always_inline)) {
@@ -451,8 +466,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                         constexpr int di = d < A_LOADS ? d : d - A_LOADS;
                         const int32_t v = p.Kv - (kb + lchunk[TWO ? di & 1 : 0] * 16);
                         if (v > 0 && v < 16) {
-                            constexpr int DOFF = d < A_LOADS ? d * CW * 1024 : A_BYTES + (d - A_LOADS) * CW * 1024;
-                            i32x4 *c = (i32x4 *)(smem + so + DOFF + cw * 1024 + lane_u * 16);
+                            const uint32_t doff = d < A_LOADS ? so + d * CW * 1024 : sob + (d - A_LOADS) * CW * 1024;
+                            i32x4 *c = (i32x4 *)(smem + doff + cw * 1024 + lane_u * 16);
                             i32x4 w = *c;
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
@@ -468,11 +483,11 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 }
             }
         };
-        auto copy_tile = [&](uint32_t so, int32_t i) __attribute__((always_inline)) {
+        auto copy_tile = [&](uint32_t so, uint32_t sob, int32_t i) __attribute__((always_inline)) {
             const KV kv = kvalid(i);
             const uint32_t kb = (uint32_t)ktile(i) * KTB;
             next_tap();
-            unroll<LOADS>([&](auto dc) __attribute__((always_inline)) { dma(dc, so, kb, kv); });
+            unroll<LOADS>([&](auto dc) __attribute__((always_inline)) { dma(dc, so, sob, kb, kv); });
         };
 
         /* Fragment of MFMA K-step ks for block blk of this wave, from the
@@ -558,13 +573,14 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         Frag fa[NB][FM], fb[NB][FN];
 
         /* One K-step: the FM x FN MFMAs on buffer CUR, interleaved slot by
-         * slot with the fragment reads of step nks of the stage at `ns` into
-         * buffer CUR^1 and with copies D0 .. D0+DN-1 of the K-tile at byte
-         * kb into the stage at byte offset dso, copy j at slot
-         * j * SLOTS / DN.  The scheduling barriers keep this interleave as
-         * written. */
-        auto step = [&](auto cur_c, auto d0_c, auto dn_c, const uint8_t *ns, int nks, uint32_t dso,
-                        uint32_t kb, const KV &kv, auto ks_c) __attribute__((always_inline)) {
+         * slot with the fragment reads of step nks of the stage whose A and
+         * B parts are at `ns` and `nbs` into buffer CUR^1 and with copies
+         * D0 .. D0+DN-1 of the K-tile at byte kb into the stage whose parts
+         * are at byte offsets dso and dsob, copy j at slot j * SLOTS / DN.
+         * The scheduling barriers keep this interleave as written. */
+        auto step = [&](auto cur_c, auto d0_c, auto dn_c, const uint8_t *ns, const uint8_t *nbs, int nks,
+                        uint32_t dso, uint32_t dsob, uint32_t kb, const KV &kv, auto ks_c)
+                        __attribute__((always_inline)) {
             constexpr int CUR = decltype(cur_c)::value;
             /* K-step of the tile the MFMAs work on (MX: its blocks are bytes
              * 8 KS KB_STEP / 32 + 8 hi of the scale dwords) */
@@ -630,13 +646,13 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     /* B's next fragments during row 0; row i's next A
                      * fragment right after its last MFMA */
                     if constexpr (t < FN)
-                        fb[TGT][t] = frag(ns + A_BYTES + wn * WTN * RB, nks, t);
+                        fb[TGT][t] = frag(nbs + wn * WTN * RB, nks, t);
                     if constexpr (t < NM && t % FN == FN - 1)
                         fa[0][t / FN] = frag(ns + wm * WTM * RB, nks, t / FN);
                 } else if constexpr (t < FM)
                     fa[TGT][t] = frag(ns + wm * WTM * RB, nks, t);
                 else if constexpr (t < NR)
-                    fb[TGT][t - FM] = frag(ns + A_BYTES + wn * WTN * RB, nks, t - FM);
+                    fb[TGT][t - FM] = frag(nbs + wn * WTN * RB, nks, t - FM);
                 else if constexpr (SCALES && t < NR + NS) {
                     /* dword u of the step's scale reads: plane u / (FM + FN) */
                     constexpr int u = t - NR, w = u / (FM + FN), v = u % (FM + FN);
@@ -652,12 +668,13 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     constexpr int FREE = SLOTS - NR;
                     unroll<DN>([&](auto jc) __attribute__((always_inline)) {
                         constexpr int j = decltype(jc)::value;
-                        if constexpr (NR + (j * FREE) / DN == t) dma(std::integral_constant<int, D0 + j>{}, dso, kb, kv);
+                        if constexpr (NR + (j * FREE) / DN == t)
+                            dma(std::integral_constant<int, D0 + j>{}, dso, dsob, kb, kv);
                     });
                 } else if constexpr (DN > 0) {
                     constexpr int j = (t * DN + SLOTS - 1) / SLOTS;
                     if constexpr (j < DN && (j * SLOTS) / DN == t)
-                        dma(std::integral_constant<int, D0 + j>{}, dso, kb, kv);
+                        dma(std::integral_constant<int, D0 + j>{}, dso, dsob, kb, kv);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -683,8 +700,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
         auto tile2 = [&](uint32_t so, uint32_t nso, int32_t kt) __attribute__((always_inline)) {
             const uint8_t *cs = smem + so;
             const KV kv0{{false, false}, false};
-            step(IC<0>{}, IC<0>{}, IC<0>{}, cs, 2, so, 0u, kv0, IC<0>{});
-            step(IC<1>{}, IC<0>{}, IC<0>{}, cs, 3, so, 0u, kv0, IC<1>{});
+            step(IC<0>{}, IC<0>{}, IC<0>{}, cs, cs + A_BYTES, 2, so, so + A_BYTES, 0u, kv0, IC<0>{});
+            step(IC<1>{}, IC<0>{}, IC<0>{}, cs, cs + A_BYTES, 3, so, so + A_BYTES, 0u, kv0, IC<1>{});
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             /* tile kt+1 landed (its copies are the only ones outstanding) */
             wait_vmcnt<0>();
@@ -692,8 +709,10 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             asm volatile("" ::: "memory");
             const KV kv = kvalid(kt + 2);
             const uint32_t kb = (uint32_t)ktile(kt + 2) * KTB;
-            step(IC<2>{}, IC<0>{}, IC<LOADS / 2>{}, smem + nso, 0, so, kb, kv, IC<2>{});
-            step(IC<3>{}, IC<LOADS / 2>{}, IC<LOADS / 2>{}, smem + nso, 1, so, kb, kv, IC<3>{});
+            step(IC<2>{}, IC<0>{}, IC<LOADS / 2>{}, smem + nso, smem + nso + A_BYTES, 0, so, so + A_BYTES, kb, kv,
+                 IC<2>{});
+            step(IC<3>{}, IC<LOADS / 2>{}, IC<LOADS / 2>{}, smem + nso, smem + nso + A_BYTES, 1, so, so + A_BYTES, kb,
+                 kv, IC<3>{});
         };
 
         auto tile = [&](auto pc, uint32_t so, uint32_t nso, uint32_t dso, int32_t kt) __attribute__((always_inline)) {
@@ -713,7 +732,8 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                 constexpr int ks = decltype(kc)::value;
                 constexpr int D0 = SP1 ? ks * LOADS / KSTEPS : 0;
                 constexpr int DN = SP1 ? (ks + 1) * LOADS / KSTEPS - D0 : 0;
-                step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, ks + 1, dso, kb, kv, IC<ks>{});
+                step(IC<(ks + P) & 1>{}, IC<D0>{}, IC<DN>{}, cs, cs + A_BYTES, ks + 1, dso, dso + A_BYTES, kb, kv,
+                     IC<ks>{});
             });
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             /* tile kt+1 landed: later copies may still be in flight (SPREAD
@@ -721,19 +741,21 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             if constexpr (SPREAD != 3)
                 wait_vmcnt<SP1 ? (STAGES - 3) * LOADS + LPRE : (STAGES - 2) * LOADS>();
             /* K-tile kt+1 (stage nso) has landed */
-            zero_tail(nso, kt + 1);
+            zero_tail(nso, nso + A_BYTES, kt + 1);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             if constexpr (SP1) {
-                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, 0, dso, kb, kv,
-                     IC<KSTEPS - 1>{});
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<LPRE>{}, IC<LOADS - LPRE>{}, smem + nso, smem + nso + A_BYTES, 0, dso,
+                     dso + A_BYTES, kb, kv, IC<KSTEPS - 1>{});
             } else if constexpr (SPREAD == 3) {
-                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<0>{}, smem + nso, 0, so, 0u, kv, IC<KSTEPS - 1>{});
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<0>{}, smem + nso, smem + nso + A_BYTES, 0, so,
+                     so + A_BYTES, 0u, kv, IC<KSTEPS - 1>{});
             } else {
                 kv = kvalid(kt + STAGES);
                 kb = (uint32_t)ktile(kt + STAGES) * KTB;
                 next_tap();
-                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, 0, so, kb, kv, IC<KSTEPS - 1>{});
+                step(IC<(KSTEPS - 1 + P) & 1>{}, IC<0>{}, IC<LOADS>{}, smem + nso, smem + nso + A_BYTES, 0, so,
+                     so + A_BYTES, kb, kv, IC<KSTEPS - 1>{});
             }
         };
         auto next_stage = [](uint32_t so) __attribute__((always_inline)) {
@@ -750,13 +772,13 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
              * landed.  Same barrier count as the MFMA wavefronts. */
             unroll<STAGES - 1>([&](auto sc) __attribute__((always_inline)) {
                 constexpr int st = decltype(sc)::value;
-                copy_tile(st * STAGE_BYTES, st);
+                copy_tile(st * STAGE_BYTES, st * STAGE_BYTES + A_BYTES, st);
             });
             wait_vmcnt<(STAGES - 2) * LOADS>();
             __builtin_amdgcn_s_barrier();
             uint32_t dso = (STAGES - 1) * STAGE_BYTES;
             for (int32_t kt = 0; kt < nkt; ++kt) {
-                copy_tile(dso, kt + STAGES - 1);
+                copy_tile(dso, dso + A_BYTES, kt + STAGES - 1);
                 wait_vmcnt<(STAGES - 2) * LOADS>();
                 __builtin_amdgcn_s_barrier();
                 dso = next_stage(dso);
@@ -765,14 +787,20 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             int32_t kt = 0;
             /* prologue: the first PRE K-tiles of the unit (SPREAD 3: issued
              * by the producers) */
-            if constexpr (SPREAD != 3) {
+            if constexpr (SPREAD == 5) {
+                /* K-tiles 0 and 1: A in stages 0 and 1, B in B's stages 0 and 1 */
+                copy_tile(0u, B_BASE, kt);
+                copy_tile(A_BYTES, B_BASE + B_BYTES, kt + 1);
+                wait_vmcnt<LOADS>();
+                zero_tail(0u, B_BASE, kt);
+            } else if constexpr (SPREAD != 3) {
                 constexpr int PRE = SPREAD == 1 ? STAGES - 1 : STAGES;
                 unroll<PRE>([&](auto sc) __attribute__((always_inline)) {
                     constexpr int st = decltype(sc)::value;
-                    copy_tile(st * STAGE_BYTES, kt + st);
+                    copy_tile(st * STAGE_BYTES, st * STAGE_BYTES + A_BYTES, kt + st);
                 });
                 wait_vmcnt<(PRE - 1) * LOADS>();
-                zero_tail(0u, kt);
+                zero_tail(0u, A_BYTES, kt);
             }
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
@@ -782,7 +810,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
 #pragma unroll
                 for (int i = 0; i < FM; ++i) fa[b][i] = frag(smem + wm * WTM * RB, b, i);
 #pragma unroll
-                for (int j = 0; j < FN; ++j) fb[b][j] = frag(smem + A_BYTES + wn * WTN * RB, b, j);
+                for (int j = 0; j < FN; ++j) fb[b][j] = frag(smem + B_BASE + wn * WTN * RB, b, j);
             });
             read_scales(smem);
             uint32_t so = 0, dso = (STAGES - 1) * STAGE_BYTES;
@@ -791,6 +819,30 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     const uint32_t nso = next_stage(so);
                     tile2(so, nso, kt);
                     so = nso;
+                }
+            } else if constexpr (SPREAD == 5) {
+                /* A's stage of K-tile kt at sa (two), B's at sb (three) */
+                uint32_t sa = 0, sb = B_BASE;
+                auto next_b = [](uint32_t b) __attribute__((always_inline)) {
+                    return b + B_BYTES == B_BASE + BST * B_BYTES ? (uint32_t)B_BASE : b + B_BYTES;
+                };
+                for (; kt < nkt; ++kt) {
+                    const uint32_t na = sa ^ (uint32_t)A_BYTES, nb = next_b(sb), db = next_b(nb);
+                    /* step 0: B's copies of K-tile kt+2 into B's stage of kt-1 */
+                    KV kv = kvalid(kt + 2);
+                    const uint32_t kb = (uint32_t)ktile(kt + 2) * KTB;
+                    step(IC<0>{}, IC<A_LOADS>{}, IC<B_LOADS>{}, smem + sa, smem + sb, 1, 0u, db, kb, kv, IC<0>{});
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    /* K-tile kt+1 landed: only this step's copies may be
+                     * outstanding */
+                    wait_vmcnt<B_LOADS>();
+                    zero_tail(na, nb, kt + 1);
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    /* step 1: A's copies of K-tile kt+2 into this tile's A stage */
+                    step(IC<1>{}, IC<0>{}, IC<A_LOADS>{}, smem + na, smem + nb, 0, sa, 0u, kb, kv, IC<1>{});
+                    sa = na;
+                    sb = nb;
                 }
             } else if constexpr (KSTEPS % 2 == 0) {
                 /* one loop body; the stage advances around the ring */
@@ -847,7 +899,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * segment that straddles N, and every result when C's rows are not
          * 16-byte aligned (vec false), are stored element by element in a
          * second, rolled loop. */
-        constexpr int WAVE_LDS = STAGES * STAGE_BYTES / NW;
+        constexpr int WAVE_LDS = LDS_BYTES / NW;
         /* (no padding where a wave's share holds just one unpadded block row) */
         constexpr int CWB = WTN * 4 + (MI * (WTN * 4 + 16) <= WAVE_LDS ? 16 : 0), CW = WTN / 4;
         constexpr int FMP = [] {
@@ -1423,7 +1475,8 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(59, 256, 256, 4, 1, 128, 2, 2, 2, 0, 32, 0)                                                   \
     X(60, 128, 128, 4, 2, 128, 2, 2, 2, 0, 32, 0)                                                   \
     X(61, 128, 128, 4, 1, 128, 4, 2, 2, 0, 32, 0)                                                   \
-    X(62, 256, 256, false, 1, 128, 2, 2, 2, 4, 16, 0)
+    X(62, 256, 256, false, 1, 128, 2, 2, 2, 4, 16, 0)                                               \
+    X(63, 256, 256, false, 1, 128, 2, 2, 4, 5, 16, 0)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn)                                                      \

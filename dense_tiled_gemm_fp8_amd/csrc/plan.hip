@@ -404,7 +404,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
      * except rows that are not 16-byte aligned in products large enough
      * for a repack pass to pay (kRepackMisalignedSec); if K ends inside a
      * 16-byte chunk, the copy schedules that clear the chunk's bytes past K
-     * in LDS (0 and 4) are the only candidates.  Other operands (the
+     * in LDS (0, 4 and 5) are the only candidates.  Other operands (the
      * transposed layouts; block-scaled rows that are not 16-byte aligned or
      * do not end on a chunk) are repacked, zero-filled to a whole number of
      * K-tiles. */
@@ -413,7 +413,8 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
     const int64_t packed_ld = cdiv(std::max<int64_t>(kbytes, 1), 128) * 128;
     const bool in_place = (dclass == 0 || dclass == 1) && !conv;
     const bool ktail = kbytes % 16 != 0;
-    const bool tail_tile_ok = a.tile < 0 || kTiles[a.tile].spread == 0 || kTiles[a.tile].spread == 4;
+    const bool tail_tile_ok = a.tile < 0 || kTiles[a.tile].spread == 0 || kTiles[a.tile].spread == 4 ||
+                              kTiles[a.tile].spread == 5;
     const double peak_cu = fp4 || fp6 ? kPeakFp4PerCu : dclass ? kPeakFp8PerCu : kPeakBf16PerCu;
     const bool repack_misaligned =
         2.0 * (double)M * (double)N * (double)K * (double)batch / (peak_cu * S) >= kRepackMisalignedSec;
@@ -465,7 +466,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
         const TileCfg &cfg = kTiles[t];
         if (cfg.dtype_class != dclass || cfg.op != want_op) continue;
         if (a.tile >= 0 && a.tile != t) continue;
-        if (P.Kv && cfg.spread != 0 && cfg.spread != 4) continue;
+        if (P.Kv && cfg.spread != 0 && cfg.spread != 4 && cfg.spread != 5) continue;
         Cand base;
         base.tile = t;
         base.tiles_m = cdiv(std::max<int64_t>(M, 1), cfg.TM);

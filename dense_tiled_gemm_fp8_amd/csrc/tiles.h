@@ -40,11 +40,14 @@ struct TileCfg {
                               K-tiles ahead, and the waves_m x waves_n MFMA
                               wavefronts only read LDS (3 stages or more);
                               4 as 0 with A's fragments read in place, one
-                              row at a time (bf16)                          */
+                              row at a time (bf16); 5 as 0 with B's ring
+                              one stage deeper, B's copies of a K-tile in
+                              the first K-step two tiles before and A's in
+                              the last (2 stages of 2 K-steps)              */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
     int32_t lds_bytes;     /* stages * (TM + TN) * RB, plus 4 (8 for FP4)
                               bytes of block scales per row and stage for
-                              MX                                            */
+                              MX; one more B stage with copy schedule 5     */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
     int32_t vgpr_budget;   /* 512 / (min_blocks * tile_waves / 4): registers
                               per lane one wave may hold                    */
@@ -155,6 +158,9 @@ constexpr TileCfg kTiles[] = {
     {4, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 132, 1, 512, {0.35f, 0.35f, 0.35f, 0.35f}, 1.34f},
     /* 16 x 16 blocks with A's fragments read in place (copy schedule 4) */
     {0, 256, 256, 64, 128, 2, 2, 2, 4, 16, 2 * (256 + 256) * 128, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.26f},
+    /* the 8-wavefront 16 x 16 tile with B's ring a stage deeper (copy
+     * schedule 5): the whole 160 KiB of LDS */
+    {0, 256, 256, 64, 128, 2, 2, 4, 5, 16, 2 * 256 * 128 + 3 * 256 * 128, 1, 256, {0.66f, 0.66f, 0.66f, 0.66f}, 1.00f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

@@ -107,7 +107,7 @@ _lib.gemm355_unit.argtypes = [ctypes.POINTER(gemm355_args), _i64] + [ctypes.POIN
 _lib.gemm355_num_tiles.restype = _i32
 _lib.gemm355_num_tiles.argtypes = []
 _lib.gemm355_tile_info.restype = ctypes.c_int
-_lib.gemm355_tile_info.argtypes = [_i32] + [ctypes.POINTER(_i32)] * 9
+_lib.gemm355_tile_info.argtypes = [_i32] + [ctypes.POINTER(_i32)] * 10
 _lib.gemm355_tile_occupancy.restype = ctypes.c_int
 _lib.gemm355_tile_occupancy.argtypes = [_i32, ctypes.POINTER(_i32)]
 _lib.gemm355_quantize.restype = ctypes.c_int
@@ -229,9 +229,9 @@ def gemm355_num_tiles() -> int:
 
 
 def gemm355_tile_info(tile: int) -> Dict[str, int]:
-    vals = [_i32() for _ in range(9)]
+    vals = [_i32() for _ in range(10)]
     _check(_lib.gemm355_tile_info(tile, *[ctypes.byref(v) for v in vals]), "gemm355_tile_info")
-    names = ("dtype_class", "T_M", "T_N", "T_K", "stages", "waves", "lds_bytes", "b_max", "op")
+    names = ("dtype_class", "T_M", "T_N", "T_K", "stages", "waves", "lds_bytes", "b_max", "op", "schedule")
     return dict(zip(names, (v.value for v in vals)))
 
 

@@ -359,13 +359,20 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
  * ring depth; waves: wavefronts per workgroup; lds_bytes: LDS per
  * workgroup; b_max: resident workgroups per compute unit from the LDS,
  * register and wavefront-slot limits; op: 0 matrix product, 1 convolution
- * (gemm355_conv2d).  Outputs are host pointers; NULL ones are skipped.
- * EINVAL if tile is not in [0, gemm355_num_tiles()). */
+ * (gemm355_conv2d); schedule: the copy schedule of the main loop (0: a
+ * K-tile's copies in the last K-step of the tile `stages` before; 1: spread
+ * over the K-steps, 3 or more stages; 2: fragments two K-steps ahead, copies
+ * over the last two K-steps; 3: producer wavefronts issue every copy; 4: as
+ * 0 with A's fragments single-buffered; 5: as 0 with B's ring one stage
+ * deeper than A's, B's copies in the first K-step, so lds_bytes holds
+ * stages A tiles and stages + 1 B tiles).  Outputs are host pointers; NULL
+ * ones are skipped.  EINVAL if tile is not in [0, gemm355_num_tiles()). */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,
                                  int32_t *T_M, int32_t *T_N, int32_t *T_K,
                                  int32_t *stages, int32_t *waves,
-                                 int32_t *lds_bytes, int32_t *b_max, int32_t *op);
+                                 int32_t *lds_bytes, int32_t *b_max, int32_t *op,
+                                 int32_t *schedule);
 
 /* Workgroups of a tile's main-loop kernel that fit on one compute unit of
  * the current device, as the HIP runtime reports it
