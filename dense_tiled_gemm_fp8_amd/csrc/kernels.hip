@@ -1476,7 +1476,8 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(60, 128, 128, 4, 2, 128, 2, 2, 2, 0, 32, 0)                                                   \
     X(61, 128, 128, 4, 1, 128, 4, 2, 2, 0, 32, 0)                                                   \
     X(62, 256, 256, false, 1, 128, 2, 2, 2, 4, 16, 0)                                               \
-    X(63, 256, 256, false, 1, 128, 2, 2, 4, 5, 16, 0)
+    X(63, 256, 256, false, 1, 128, 2, 2, 4, 5, 16, 0)                                               \
+    X(64, 256, 256, 1, 1, 128, 2, 2, 2, 5, 32, 0)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn)                                                      \

@@ -161,6 +161,9 @@ constexpr TileCfg kTiles[] = {
     /* the 8-wavefront 16 x 16 tile with B's ring a stage deeper (copy
      * schedule 5): the whole 160 KiB of LDS */
     {0, 256, 256, 64, 128, 2, 2, 4, 5, 16, 2 * 256 * 128 + 3 * 256 * 128, 1, 256, {0.66f, 0.66f, 0.66f, 0.66f}, 1.00f},
+    /* the 8-bit 256 x 256 tile (4 wavefronts, 32 x 32 blocks) with copy
+     * schedule 5 */
+    {1, 256, 256, 128, 128, 2, 2, 2, 5, 32, 2 * 256 * 128 + 3 * 256 * 128, 1, 512, {0.66f, 0.66f, 0.66f, 0.66f}, 1.12f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 
