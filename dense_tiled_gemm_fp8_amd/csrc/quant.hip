@@ -2,8 +2,8 @@
  * quant.hip -- per-tensor scaling of fp32 or bf16 tensors to the 8-bit
  * formats of the Hopper row of the input/accumulate table (page "The Tensor
  * Core"): OCP E4M3FN and OCP E5M2.  The page "10. Tensor Cores, shapes, and
- * tile alignment" (section "Practical shape sweep") asks that a GEMM be
- * judged with this quantisation overhead included.
+ * tile alignment" (section "Practical shape sweep") counts this quantisation
+ * as part of an 8-bit product's cost when its speed is measured.
  *
  *   amax_kernel      per-block maxima of |x| over contiguous shares of each
  *                    tensor

@@ -387,8 +387,8 @@ GEMM355_API gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_
 /*
  * gemm355_quantize -- per-tensor scaling of `batch` tensors of n elements each
  * to an 8-bit format, on the device (page "10. Tensor Cores, ...", section
- * "Practical shape sweep": a GEMM must be judged with its quantisation
- * overhead included).  For tensor g (elements x[g*n .. g*n + n - 1]):
+ * "Practical shape sweep": the quantisation is part of an 8-bit product's
+ * measured cost).  For tensor g (elements x[g*n .. g*n + n - 1]):
  *     amax  = max_i |x_i|                       (exact)
  *     s     = amax / F  in fp32, rounded to nearest (s = 1 if amax == 0),
  *             F = 448 (E4M3) or 57344 (E5M2)
