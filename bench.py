@@ -530,8 +530,8 @@ def cpu_baseline(torch, budget_s=15.0):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
-              "(the path would shard by output tiles, see the design notes)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU; --gpus %d is not supported (the product would shard by "
+              "row blocks of C, one per GPU, each running this library on its block)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_bytes:
         copy_reference(args.copy_bytes)
