@@ -231,15 +231,20 @@ def test_plan_reports_efficiency_levers(g):
                     dtype=g.BF16_BF16, cus=256)
     p = g.gemm355_plan(a)
     assert (p["T_M"], p["T_N"], p["G"], p["eta_wave_num"], p["eta_wave_den"]) == (256, 256, 256, 1, 1)
-    # every named shape except the single-tile-grid 256^3 call fills the device
-    # to eta_sched >= 0.95 (the tail and long-K shapes through the levers above)
-    shapes = [(4000, 4000, 4000, 1, g.BF16_F32), (1000, 3000, 777, 1, g.BF16_F32),
-              (8192, 8192, 8192, 1, g.E4M3_F32), (512, 1024, 4096, 64, g.E4M3_F32)]
+    # the large named shapes fill the device to eta_sched >= 0.95 (the tail
+    # and long-K shapes through the levers above)
+    shapes = [(4000, 4000, 4000, 1, g.BF16_F32), (8192, 8192, 8192, 1, g.E4M3_F32),
+              (512, 1024, 4096, 64, g.E4M3_F32)]
     for (M, N, K, batch, dt) in shapes:
         a = g.make_args(M, N, K, A=0x10000, B=0x1000000000, C=0x200000000000, dtype=dt, batch=batch,
                         stride_a=M * K, stride_b=N * K, stride_c=M * N, cus=256)
         p = g.gemm355_plan(a)
         assert Fraction(p["eta_sched_num"], p["eta_sched_den"]) >= Fraction(95, 100), (M, N, K)
+    # 1000 x 3000 x 777: 192 tiles of 128 x 128 in one round (eta_sched 3/4)
+    # model faster than 752 of 64 x 64 (47/48) by more than the tie band
+    p = g.gemm355_plan(g.make_args(1000, 3000, 777, A=0x10000, B=0x1000000000, C=0x200000000000, cus=256))
+    assert (p["T_M"], p["T_N"], p["G"]) == (128, 128, 192)
+    assert (p["eta_sched_num"], p["eta_sched_den"]) == (3, 4)
 
 
 def test_plan_fits_short_k_and_narrow_shapes(g):
