@@ -34,10 +34,11 @@ SHAPES = {
     "bf16": [(100352, 64, 256, 1), (100352, 128, 1152, 1), (50176, 256, 2304, 1), (1000, 3000, 777, 1),
              (4096, 4096, 4096, 1), (256, 256, 65536, 1), (128, 512, 131072, 1), (64, 64, 262144, 1),
              (8192, 8192, 1024, 1), (16384, 512, 512, 1), (2048, 2048, 2048, 1), (4096, 1024, 512, 1),
-             (32768, 256, 1024, 1)],
+             (32768, 256, 1024, 1), (3072, 3072, 3072, 1), (768, 3072, 2048, 1), (2560, 1024, 2048, 1),
+             (6144, 6144, 1024, 1), (768, 1000, 1024, 1)],
     "e4m3": [(8192, 8192, 8192, 1), (512, 1024, 4096, 64), (256, 256, 131072, 1), (100352, 128, 2304, 1),
              (16384, 512, 1024, 1), (2048, 2048, 2048, 1), (4096, 1024, 1024, 1), (32768, 256, 2048, 1),
-             (64, 64, 524288, 1)],
+             (64, 64, 524288, 1), (512, 3000, 4096, 1), (4096, 2560, 4096, 1)],
     # N, H, W, C, K, R, S, pad: ResNet-like layers
     "conv": [(32, 56, 56, 128, 128, 3, 3, 1), (64, 28, 28, 256, 256, 3, 3, 1), (32, 56, 56, 256, 64, 1, 1, 0),
              (32, 56, 56, 64, 64, 3, 3, 1), (32, 14, 14, 512, 512, 3, 3, 1), (64, 56, 56, 64, 256, 1, 1, 0),

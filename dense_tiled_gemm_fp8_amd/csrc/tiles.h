@@ -73,67 +73,67 @@ constexpr int32_t kMaxWavesPerSimd = 8;
 
 constexpr TileCfg kTiles[] = {
     /* bf16, 128-byte K-tiles, 2 stages */
-    {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.18f},
-    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.32f, 0.42f, 0.42f, 0.42f}, 1.24f},
-    {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.10f, 0.17f, 0.20f, 0.21f}, 1.28f},
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.16f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.34f, 0.45f, 0.45f, 0.45f}, 1.16f},
+    {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.11f, 0.18f, 0.21f, 0.22f}, 1.16f},
     /* E4M3, 128-byte K-tiles, 2 stages */
-    {1, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.64f, 0.64f, 0.64f, 0.64f}, 1.12f},
-    {1, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.35f, 0.47f, 0.47f, 0.47f}, 1.04f},
-    {1, 64, 64, 128, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.12f, 0.20f, 0.22f, 0.23f}, 1.14f},
+    {1, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.68f, 0.68f, 0.68f, 0.68f}, 1.04f},
+    {1, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.37f, 0.50f, 0.50f, 0.50f}, 0.94f},
+    {1, 64, 64, 128, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.13f, 0.21f, 0.23f, 0.24f}, 1.02f},
     /* 256 x 256 with 64-byte K-tiles and a deeper ring */
-    {0, 256, 256, 32, 64, 4, 2, 2, 0, 32, 4 * (256 + 256) * 64, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.12f},
-    {0, 256, 256, 32, 64, 5, 2, 2, 0, 32, 5 * (256 + 256) * 64, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.06f},
-    {1, 256, 256, 64, 64, 4, 2, 2, 0, 32, 4 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.18f},
-    {1, 256, 256, 64, 64, 5, 2, 2, 0, 32, 5 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.16f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 0, 32, 4 * (256 + 256) * 64, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.06f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 0, 32, 5 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.02f},
+    {1, 256, 256, 64, 64, 4, 2, 2, 0, 32, 4 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.02f},
+    {1, 256, 256, 64, 64, 5, 2, 2, 0, 32, 5 * (256 + 256) * 64, 1, 512, {0.61f, 0.61f, 0.61f, 0.61f}, 1.02f},
     /* 256 x 256 with 8 wavefronts (2 x 4, two per SIMD) */
-    {0, 256, 256, 64, 128, 2, 2, 4, 0, 32, 2 * (256 + 256) * 128, 1, 256, {0.55f, 0.55f, 0.55f, 0.55f}, 0.96f},
-    {0, 256, 256, 32, 64, 4, 2, 4, 0, 32, 4 * (256 + 256) * 64, 1, 256, {0.50f, 0.50f, 0.50f, 0.50f}, 1.04f},
-    {1, 256, 256, 128, 128, 2, 2, 4, 0, 32, 2 * (256 + 256) * 128, 1, 256, {0.59f, 0.59f, 0.59f, 0.59f}, 0.92f},
-    {1, 256, 256, 64, 64, 4, 2, 4, 0, 32, 4 * (256 + 256) * 64, 1, 256, {0.62f, 0.62f, 0.62f, 0.62f}, 0.98f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 32, 2 * (256 + 256) * 128, 1, 256, {0.58f, 0.58f, 0.58f, 0.58f}, 1.16f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 0, 32, 4 * (256 + 256) * 64, 1, 256, {0.53f, 0.53f, 0.53f, 0.53f}, 1.16f},
+    {1, 256, 256, 128, 128, 2, 2, 4, 0, 32, 2 * (256 + 256) * 128, 1, 256, {0.63f, 0.63f, 0.63f, 0.63f}, 1.06f},
+    {1, 256, 256, 64, 64, 4, 2, 4, 0, 32, 4 * (256 + 256) * 64, 1, 256, {0.66f, 0.66f, 0.66f, 0.66f}, 1.02f},
     /* small tiles with deep rings for streaming (small M, N, long K) */
-    {0, 64, 64, 64, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.10f, 0.10f, 0.10f, 0.10f}, 1.56f},
-    {0, 64, 64, 64, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.10f, 0.17f, 0.17f, 0.17f}, 2.48f},
-    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.32f, 0.32f, 0.32f, 0.32f}, 1.40f},
-    {1, 64, 64, 128, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.12f, 0.12f, 0.12f, 0.12f}, 1.50f},
-    {1, 64, 64, 128, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.12f, 0.20f, 0.20f, 0.20f}, 1.68f},
-    {1, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.35f, 0.35f, 0.35f, 0.35f}, 1.34f},
+    {0, 64, 64, 64, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.11f, 0.11f, 0.11f, 0.11f}, 1.54f},
+    {0, 64, 64, 64, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.11f, 0.18f, 0.18f, 0.18f}, 2.02f},
+    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.34f, 0.34f, 0.34f, 0.34f}, 1.40f},
+    {1, 64, 64, 128, 128, 8, 2, 2, 0, 32, 8 * (64 + 64) * 128, 1, 512, {0.13f, 0.13f, 0.13f, 0.13f}, 1.38f},
+    {1, 64, 64, 128, 128, 4, 2, 2, 0, 32, 4 * (64 + 64) * 128, 2, 256, {0.13f, 0.21f, 0.21f, 0.21f}, 1.46f},
+    {1, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.37f, 0.37f, 0.37f, 0.37f}, 1.10f},
     /* 64 x 64 with one wavefront (four MFMA blocks per K-step) */
-    {0, 64, 64, 64, 128, 2, 1, 1, 0, 32, 2 * (64 + 64) * 128, 4, 512, {0.07f, 0.14f, 0.20f, 0.24f}, 1.02f},
-    {0, 64, 64, 64, 128, 4, 1, 1, 0, 32, 4 * (64 + 64) * 128, 2, 512, {0.07f, 0.14f, 0.14f, 0.14f}, 2.50f},
-    {1, 64, 64, 128, 128, 2, 1, 1, 0, 32, 2 * (64 + 64) * 128, 4, 512, {0.08f, 0.16f, 0.22f, 0.27f}, 1.00f},
-    {1, 64, 64, 128, 128, 4, 1, 1, 0, 32, 4 * (64 + 64) * 128, 2, 512, {0.08f, 0.16f, 0.16f, 0.16f}, 2.50f},
+    {0, 64, 64, 64, 128, 2, 1, 1, 0, 32, 2 * (64 + 64) * 128, 4, 512, {0.07f, 0.15f, 0.21f, 0.25f}, 1.00f},
+    {0, 64, 64, 64, 128, 4, 1, 1, 0, 32, 4 * (64 + 64) * 128, 2, 512, {0.07f, 0.15f, 0.15f, 0.15f}, 2.50f},
+    {1, 64, 64, 128, 128, 2, 1, 1, 0, 32, 2 * (64 + 64) * 128, 4, 512, {0.08f, 0.17f, 0.23f, 0.29f}, 0.88f},
+    {1, 64, 64, 128, 128, 4, 1, 1, 0, 32, 4 * (64 + 64) * 128, 2, 512, {0.08f, 0.17f, 0.17f, 0.17f}, 1.50f},
     /* 256 x 256, 64-byte K-tiles, copies spread over the K-steps */
-    {0, 256, 256, 32, 64, 4, 2, 2, 1, 32, 4 * (256 + 256) * 64, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.18f},
-    {0, 256, 256, 32, 64, 5, 2, 2, 1, 32, 5 * (256 + 256) * 64, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.14f},
-    {0, 256, 256, 32, 64, 4, 2, 4, 1, 32, 4 * (256 + 256) * 64, 1, 256, {0.49f, 0.49f, 0.49f, 0.49f}, 1.04f},
-    {0, 256, 256, 32, 64, 5, 2, 4, 1, 32, 5 * (256 + 256) * 64, 1, 256, {0.49f, 0.49f, 0.49f, 0.49f}, 1.04f},
-    {1, 256, 256, 64, 64, 4, 2, 2, 1, 32, 4 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.26f},
-    {1, 256, 256, 64, 64, 5, 2, 2, 1, 32, 5 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.20f},
-    {1, 256, 256, 64, 64, 4, 2, 4, 1, 32, 4 * (256 + 256) * 64, 1, 256, {0.55f, 0.55f, 0.55f, 0.55f}, 1.04f},
-    {1, 256, 256, 64, 64, 5, 2, 4, 1, 32, 5 * (256 + 256) * 64, 1, 256, {0.55f, 0.55f, 0.55f, 0.55f}, 1.04f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 1, 32, 4 * (256 + 256) * 64, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.12f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 1, 32, 5 * (256 + 256) * 64, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.10f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 1, 32, 4 * (256 + 256) * 64, 1, 256, {0.52f, 0.52f, 0.52f, 0.52f}, 1.16f},
+    {0, 256, 256, 32, 64, 5, 2, 4, 1, 32, 5 * (256 + 256) * 64, 1, 256, {0.52f, 0.52f, 0.52f, 0.52f}, 1.16f},
+    {1, 256, 256, 64, 64, 4, 2, 2, 1, 32, 4 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.12f},
+    {1, 256, 256, 64, 64, 5, 2, 2, 1, 32, 5 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.04f},
+    {1, 256, 256, 64, 64, 4, 2, 4, 1, 32, 4 * (256 + 256) * 64, 1, 256, {0.58f, 0.58f, 0.58f, 0.58f}, 1.18f},
+    {1, 256, 256, 64, 64, 5, 2, 4, 1, 32, 5 * (256 + 256) * 64, 1, 256, {0.58f, 0.58f, 0.58f, 0.58f}, 1.16f},
     /* 256 x 256 with 16 wavefronts (4 x 4, four per SIMD, 64 x 64 each) */
-    {0, 256, 256, 64, 128, 2, 4, 4, 0, 32, 2 * (256 + 256) * 128, 1, 128, {0.49f, 0.49f, 0.49f, 0.49f}, 0.88f},
-    {0, 256, 256, 32, 64, 4, 4, 4, 0, 32, 4 * (256 + 256) * 64, 1, 128, {0.49f, 0.49f, 0.49f, 0.49f}, 0.88f},
-    {0, 256, 256, 32, 64, 4, 4, 4, 1, 32, 4 * (256 + 256) * 64, 1, 128, {0.49f, 0.49f, 0.49f, 0.49f}, 0.86f},
+    {0, 256, 256, 64, 128, 2, 4, 4, 0, 32, 2 * (256 + 256) * 128, 1, 128, {0.52f, 0.52f, 0.52f, 0.52f}, 1.20f},
+    {0, 256, 256, 32, 64, 4, 4, 4, 0, 32, 4 * (256 + 256) * 64, 1, 128, {0.52f, 0.52f, 0.52f, 0.52f}, 1.14f},
+    {0, 256, 256, 32, 64, 4, 4, 4, 1, 32, 4 * (256 + 256) * 64, 1, 128, {0.52f, 0.52f, 0.52f, 0.52f}, 1.12f},
     /* 256 x 256 with 16 x 16 MFMA blocks */
-    {0, 256, 256, 64, 128, 2, 2, 2, 0, 16, 2 * (256 + 256) * 128, 1, 512, {0.60f, 0.60f, 0.60f, 0.60f}, 1.06f},
-    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.64f, 0.64f, 0.64f, 0.64f}, 1.00f},
-    {0, 256, 256, 32, 64, 4, 2, 4, 0, 16, 4 * (256 + 256) * 64, 1, 256, {0.49f, 0.49f, 0.49f, 0.49f}, 1.20f},
-    {0, 256, 256, 32, 64, 4, 2, 2, 0, 16, 4 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.10f},
-    {0, 256, 256, 32, 64, 4, 2, 2, 1, 16, 4 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.12f},
-    {0, 256, 256, 32, 64, 5, 2, 2, 0, 16, 5 * (256 + 256) * 64, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.08f},
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 16, 2 * (256 + 256) * 128, 1, 512, {0.64f, 0.64f, 0.64f, 0.64f}, 1.08f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.68f, 0.68f, 0.68f, 0.68f}, 1.12f},
+    {0, 256, 256, 32, 64, 4, 2, 4, 0, 16, 4 * (256 + 256) * 64, 1, 256, {0.52f, 0.52f, 0.52f, 0.52f}, 1.24f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 0, 16, 4 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.04f},
+    {0, 256, 256, 32, 64, 4, 2, 2, 1, 16, 4 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.10f},
+    {0, 256, 256, 32, 64, 5, 2, 2, 0, 16, 5 * (256 + 256) * 64, 1, 512, {0.58f, 0.58f, 0.58f, 0.58f}, 1.04f},
     /* 32 x 32 MFMA blocks, fragments read two K-steps ahead, copies over the
      * last two K-steps of each K-tile */
-    {0, 256, 256, 64, 128, 2, 2, 2, 2, 32, 2 * (256 + 256) * 128, 1, 512, {0.63f, 0.63f, 0.63f, 0.63f}, 1.02f},
-    {0, 256, 256, 64, 128, 2, 2, 4, 2, 32, 2 * (256 + 256) * 128, 1, 256, {0.59f, 0.59f, 0.59f, 0.59f}, 0.94f},
-    {0, 128, 128, 64, 128, 2, 2, 2, 2, 32, 2 * (128 + 128) * 128, 2, 256, {0.35f, 0.45f, 0.45f, 0.45f}, 1.18f},
+    {0, 256, 256, 64, 128, 2, 2, 2, 2, 32, 2 * (256 + 256) * 128, 1, 512, {0.67f, 0.67f, 0.67f, 0.67f}, 1.04f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 2, 32, 2 * (256 + 256) * 128, 1, 256, {0.63f, 0.63f, 0.63f, 0.63f}, 1.12f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 2, 32, 2 * (128 + 128) * 128, 2, 256, {0.37f, 0.48f, 0.48f, 0.48f}, 1.12f},
     /* 256 x 128, 3 stages: producer wavefronts (warp specialisation) with
      * 32 x 32 and 16 x 16 blocks and for E4M3, and the same tile with
      * uniform wavefronts for comparison */
-    {0, 256, 128, 64, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.49f, 0.49f, 0.49f, 0.49f}, 1.06f},
-    {0, 256, 128, 64, 128, 3, 2, 2, 3, 16, 3 * (256 + 128) * 128, 1, 256, {0.49f, 0.49f, 0.49f, 0.49f}, 1.12f},
-    {1, 256, 128, 128, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.55f, 0.55f, 0.55f, 0.55f}, 0.92f},
-    {0, 256, 128, 64, 128, 3, 2, 2, 0, 32, 3 * (256 + 128) * 128, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.18f},
+    {0, 256, 128, 64, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.52f, 0.52f, 0.52f, 0.52f}, 1.08f},
+    {0, 256, 128, 64, 128, 3, 2, 2, 3, 16, 3 * (256 + 128) * 128, 1, 256, {0.52f, 0.52f, 0.52f, 0.52f}, 1.26f},
+    {1, 256, 128, 128, 128, 3, 2, 2, 3, 32, 3 * (256 + 128) * 128, 1, 256, {0.58f, 0.58f, 0.58f, 0.58f}, 1.06f},
+    {0, 256, 128, 64, 128, 3, 2, 2, 0, 32, 3 * (256 + 128) * 128, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.10f},
     /* block-scaled 8-bit (MX): the 8-bit tiles with the scale dwords of
      * each K-tile in the stage */
     {2, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 132, 1, 512, {0.62f, 0.62f, 0.62f, 0.62f}, 1.12f},
@@ -157,13 +157,13 @@ constexpr TileCfg kTiles[] = {
     {4, 128, 128, 128, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 132, 2, 256, {0.35f, 0.47f, 0.47f, 0.47f}, 1.04f},
     {4, 128, 128, 128, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 132, 1, 512, {0.35f, 0.35f, 0.35f, 0.35f}, 1.34f},
     /* 16 x 16 blocks with A's fragments read in place (copy schedule 4) */
-    {0, 256, 256, 64, 128, 2, 2, 2, 4, 16, 2 * (256 + 256) * 128, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.26f},
+    {0, 256, 256, 64, 128, 2, 2, 2, 4, 16, 2 * (256 + 256) * 128, 1, 512, {0.52f, 0.52f, 0.52f, 0.52f}, 1.20f},
     /* the 8-wavefront 16 x 16 tile with B's ring a stage deeper (copy
      * schedule 5): the whole 160 KiB of LDS */
-    {0, 256, 256, 64, 128, 2, 2, 4, 5, 16, 2 * 256 * 128 + 3 * 256 * 128, 1, 256, {0.66f, 0.66f, 0.66f, 0.66f}, 1.00f},
+    {0, 256, 256, 64, 128, 2, 2, 4, 5, 16, 2 * 256 * 128 + 3 * 256 * 128, 1, 256, {0.70f, 0.70f, 0.70f, 0.70f}, 1.18f},
     /* the 8-bit 256 x 256 tile (4 wavefronts, 32 x 32 blocks) with copy
      * schedule 5 */
-    {1, 256, 256, 128, 128, 2, 2, 2, 5, 32, 2 * 256 * 128 + 3 * 256 * 128, 1, 512, {0.66f, 0.66f, 0.66f, 0.66f}, 1.12f},
+    {1, 256, 256, 128, 128, 2, 2, 2, 5, 32, 2 * 256 * 128 + 3 * 256 * 128, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 1.24f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 
