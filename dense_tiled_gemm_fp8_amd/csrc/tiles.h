@@ -146,11 +146,11 @@ constexpr TileCfg kTiles[] = {
     {3, 128, 128, 256, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 136, 1, 512, {0.35f, 0.35f, 0.35f, 0.35f}, 1.34f},
     /* convolution (bf16): the matrix tiles 0, 1, 2, 36 and 16 with A
      * gathered from the images */
-    {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.67f, 0.67f, 0.67f, 0.67f}, 1.16f, 1},
-    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.43f, 0.58f, 0.58f, 0.58f}, 1.90f, 1},
-    {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.14f, 0.24f, 0.27f, 0.29f}, 2.50f, 1},
-    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.77f, 0.77f, 0.77f, 0.77f}, 1.24f, 1},
-    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.43f, 0.43f, 0.43f, 0.43f}, 1.64f, 1},
+    {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.76f, 0.76f, 0.76f, 0.76f}, 1.16f, 1},
+    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.41f, 0.66f, 0.66f, 0.66f}, 1.82f, 1},
+    {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.16f, 0.27f, 0.31f, 0.33f}, 2.36f, 1},
+    {0, 256, 256, 64, 128, 2, 2, 4, 0, 16, 2 * (256 + 256) * 128, 1, 256, {0.88f, 0.88f, 0.88f, 0.88f}, 1.42f, 1},
+    {0, 128, 128, 64, 128, 4, 2, 2, 0, 32, 4 * (128 + 128) * 128, 1, 512, {0.49f, 0.49f, 0.49f, 0.49f}, 1.46f, 1},
     /* block-scaled FP6: K-tiles of 128 values (96 bytes) staged in 128-byte
      * rows, one scale dword per row and stage */
     {4, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 132, 1, 512, {0.62f, 0.62f, 0.62f, 0.62f}, 1.12f},
