@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -158,6 +159,8 @@ struct ScratchKey {
     }
 };
 std::map<ScratchKey, std::unique_ptr<Scratch>> g_scratch;
+/* largest library-owned buffer a call may hold (gemm355_set_scratch_limit) */
+std::atomic<uint64_t> g_scratch_limit{UINT64_MAX};
 
 gemm355_status library_scratch(size_t need, void *stream, void **out, std::unique_lock<std::mutex> &hold)
 {
@@ -174,6 +177,10 @@ gemm355_status library_scratch(size_t need, void *stream, void **out, std::uniqu
     }
     /* entries are never erased before unload, so s stays valid */
     hold = std::unique_lock<std::mutex>(s->mu);
+    const uint64_t limit = g_scratch_limit.load();
+    /* over the cap: refused like a failed allocation, before the buffer
+     * that earlier calls may still read is touched */
+    if (need > limit) return GEMM355_ENOMEM;
     if (s->bytes < need) {
         if (s->ptr) {
             /* earlier calls on this stream may still read the old buffer */
@@ -183,6 +190,7 @@ gemm355_status library_scratch(size_t need, void *stream, void **out, std::uniqu
             s->bytes = 0;
         }
         size_t grow = need + need / 4;
+        if (grow > limit) grow = (size_t)limit;
         if (hipMalloc(&s->ptr, grow) != hipSuccess) {
             (void)hipGetLastError();
             s->ptr = nullptr;
@@ -643,6 +651,13 @@ gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class, int32_t *T_
     return GEMM355_OK;
 }
 
+gemm355_status gemm355_set_scratch_limit(uint64_t bytes, uint64_t *previous)
+{
+    const uint64_t old = g_scratch_limit.exchange(bytes);
+    if (previous) *previous = old;
+    return GEMM355_OK;
+}
+
 gemm355_status gemm355_tile_occupancy(int32_t tile, int32_t *blocks_per_cu)
 {
     if (tile < 0 || tile >= kNumTiles || !blocks_per_cu) return GEMM355_EINVAL;
@@ -704,7 +719,7 @@ const char *gemm355_status_string(gemm355_status status)
     case GEMM355_EINVAL: return "invalid argument";
     case GEMM355_EALIGN: return "misaligned pointer";
     case GEMM355_EUNSUPPORTED: return "unsupported size";
-    case GEMM355_ENOMEM: return "workspace too small or allocation failed";
+    case GEMM355_ENOMEM: return "workspace too small, scratch over its cap, or allocation failed";
     case GEMM355_EHIP: return "HIP runtime error";
     case GEMM355_ETOOBIG: return "needs more scratch than the allocation-free entry point's fixed buffer";
     default: return "unknown status";

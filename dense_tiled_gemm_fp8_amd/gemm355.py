@@ -119,6 +119,8 @@ _lib.gemm355_conv2d_plan.argtypes = [ctypes.POINTER(gemm355_conv_args), ctypes.P
 _lib.gemm355_conv2d_out_size.restype = ctypes.c_int
 _lib.gemm355_conv2d_out_size.argtypes = [ctypes.POINTER(gemm355_conv_args), ctypes.POINTER(_i64),
                                          ctypes.POINTER(_i64)]
+_lib.gemm355_set_scratch_limit.restype = ctypes.c_int
+_lib.gemm355_set_scratch_limit.argtypes = [ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
 _lib.gemm355_status_string.restype = ctypes.c_char_p
 _lib.gemm355_status_string.argtypes = [ctypes.c_int]
 
@@ -126,7 +128,8 @@ EXPORTED = ("gemm355_gemm", "gemm355_gemm_ex", "gemm355_gemm_noalloc",
             "gemm355_plan", "gemm355_eta_wave",
             "gemm355_eta_pad", "gemm355_kslice", "gemm355_unit", "gemm355_num_tiles",
             "gemm355_tile_info", "gemm355_tile_occupancy", "gemm355_quantize",
-            "gemm355_conv2d", "gemm355_conv2d_plan", "gemm355_conv2d_out_size", "gemm355_status_string")
+            "gemm355_conv2d", "gemm355_conv2d_plan", "gemm355_conv2d_out_size", "gemm355_set_scratch_limit",
+            "gemm355_status_string")
 
 
 class Gemm355Error(RuntimeError):
@@ -233,6 +236,16 @@ def gemm355_tile_info(tile: int) -> Dict[str, int]:
     _check(_lib.gemm355_tile_info(tile, *[ctypes.byref(v) for v in vals]), "gemm355_tile_info")
     names = ("dtype_class", "T_M", "T_N", "T_K", "stages", "waves", "lds_bytes", "b_max", "op", "schedule")
     return dict(zip(names, (v.value for v in vals)))
+
+
+SCRATCH_UNLIMITED = (1 << 64) - 1
+
+
+def gemm355_set_scratch_limit(nbytes: int) -> int:
+    """Cap on library-owned scratch (SCRATCH_UNLIMITED: none); returns the previous cap."""
+    prev = ctypes.c_uint64()
+    _check(_lib.gemm355_set_scratch_limit(nbytes, ctypes.byref(prev)), "gemm355_set_scratch_limit")
+    return prev.value
 
 
 def gemm355_tile_occupancy(tile: int) -> int:

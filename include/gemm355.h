@@ -52,7 +52,9 @@ typedef enum gemm355_status {
                                   dtype with K not a multiple of 128, or an
                                   MX FP4 / FP6 call outside its limits */
     GEMM355_ENOMEM = 4,        /* caller workspace smaller than the plan's
-                                  workspace_bytes, or allocation failed */
+                                  workspace_bytes, library scratch over the
+                                  cap of gemm355_set_scratch_limit, or
+                                  allocation failed */
     GEMM355_EHIP = 5,          /* a HIP runtime call failed (no device,
                                   launch failure) */
     GEMM355_ETOOBIG = 6        /* gemm355_gemm_noalloc: the plan needs more
@@ -302,6 +304,22 @@ GEMM355_API gemm355_status gemm355_gemm_noalloc(const gemm355_args *args, void *
  * them; EHIP only when args->cus == 0 and the device query fails.
  */
 GEMM355_API gemm355_status gemm355_plan(const gemm355_args *args, gemm355_plan_t *out);
+
+/*
+ * gemm355_set_scratch_limit -- cap on the scratch the library allocates for
+ * itself (page "10. Tensor Cores, ...", section "When shape alone can't fix
+ * wave efficiency": split-K's partial sums go to a buffer of their own,
+ * combined by a second pass; repacked rows and regrouped block scales use
+ * the same buffer).  A call of gemm355_gemm, gemm355_gemm_ex without a
+ * workspace, gemm355_conv2d or gemm355_quantize whose plan needs more than
+ * `bytes` returns ENOMEM before anything is launched, and a buffer is
+ * never grown past the cap; buffers already larger are kept until unload.
+ * Calls with a caller workspace and gemm355_gemm_noalloc are not affected.
+ * UINT64_MAX (the default) means no cap; 0 refuses every call that needs
+ * scratch.  The previous cap goes to *previous (may be NULL).  Process-wide,
+ * for every device; thread-safe.  Never fails.
+ */
+GEMM355_API gemm355_status gemm355_set_scratch_limit(uint64_t bytes, uint64_t *previous);
 
 /*
  * Wave efficiency G / (ceil(G/(S*b)) * S * b) for G tiles on S compute units

@@ -374,6 +374,17 @@ def test_argument_errors(g):
     assert g.gemm355_status_string(g.ENOMEM).startswith("workspace")
 
 
+def test_scratch_limit_roundtrip(g):
+    """The library-scratch cap is a process-wide value: each set returns the
+    previous one, the default is no cap."""
+    prev = g.gemm355_set_scratch_limit(12345)
+    try:
+        assert prev == g.SCRATCH_UNLIMITED
+        assert g.gemm355_set_scratch_limit(0) == 12345
+    finally:
+        assert g.gemm355_set_scratch_limit(prev) == 0
+
+
 def test_quantize_argument_errors(g):
     """Argument checks of the quantiser run before anything touches a device."""
     X, Q, S = 0x10000, 0x1000000000, 0x200000000000

@@ -435,6 +435,50 @@ def test_library_scratch_concurrent_calls_one_stream():
             assert np.array_equal(C.double().cpu().numpy(), ref), (M, N, K)
 
 
+def test_library_scratch_cap_enomem():
+    """Library-owned scratch over the cap of gemm355_set_scratch_limit: the
+    call returns ENOMEM before launching anything (C keeps its NaN fill) and
+    a repacking call is refused the same way; at a cap equal to the plan's
+    need the same split-K call runs and gives the oracle's bits."""
+    M, N, K = 200, 168, 4096
+    ops = int_ops(M, N, K, "bf16", 77)
+    ref, _ = H.oracle_full(ops, alpha=1.0)
+    A, B = H.dev(ops.A), H.dev(ops.B)
+    C = torch.full((M, N), float("nan"), device="cuda")
+    a = g.make_args(M, N, K, A=A, B=B, C=C, dtype=g.BF16_F32, split_k=4, tile=2)
+    need = g.gemm355_plan(a)["workspace_bytes"]
+    assert need > 0
+    prev = g.gemm355_set_scratch_limit(need - 1)
+    try:
+        H.say("scratch cap", need - 1, "below the need", need)
+        with pytest.raises(g.Gemm355Error) as e:
+            g.gemm355_gemm_ex(a)
+        assert e.value.status == g.ENOMEM
+        # a caller workspace is not subject to the cap
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        Cw = torch.full((M, N), float("nan"), device="cuda")
+        g.gemm355_gemm_ex(g.make_args(M, N, K, A=A, B=B, C=Cw, dtype=g.BF16_F32, split_k=4, tile=2,
+                                      workspace=ws, workspace_bytes=need))
+        # a cap of 0 refuses every call that needs scratch, not the others
+        assert g.gemm355_set_scratch_limit(0) == need - 1
+        with pytest.raises(g.Gemm355Error) as e:
+            g.gemm355_gemm_ex(a)
+        assert e.value.status == g.ENOMEM
+        C0 = torch.full((M, N), float("nan"), device="cuda")
+        g.gemm355_gemm_ex(g.make_args(M, N, K, A=A, B=B, C=C0, dtype=g.BF16_F32, split_k=1, persistent=0,
+                                      tile=2))
+        torch.cuda.synchronize()
+        assert torch.isnan(C).all()
+        g.gemm355_set_scratch_limit(need)
+        H.say("scratch cap", need)
+        g.gemm355_gemm_ex(a)
+        torch.cuda.synchronize()
+    finally:
+        g.gemm355_set_scratch_limit(prev)
+    for out in (C, Cw, C0):
+        assert np.array_equal(out.double().cpu().numpy(), ref)
+
+
 def test_degenerate_sizes():
     ops = ops_from(5, 7, 0, "bf16", 37)
     H.say("K = 0")
