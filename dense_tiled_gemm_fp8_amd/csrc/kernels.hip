@@ -265,9 +265,22 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
      * follows A in each stage. */
     static_assert(SPREAD != 5 || (!MX && !FP6 && !CONV && STAGES == 2 && KSTEPS == 2),
                   "deeper B ring: two stages of two K-steps");
-    constexpr int BST = SPREAD == 5 ? STAGES + 1 : STAGES;
-    constexpr int B_BASE = SPREAD == 5 ? STAGES * A_BYTES : A_BYTES;
-    constexpr int LDS_BYTES = SPREAD == 5 ? STAGES * A_BYTES + BST * B_BYTES : STAGES * STAGE_BYTES;
+    /* SPREAD 6: schedule 5's rings and copies in a ping-pong loop, the
+     * alternative to producer wavefronts (schedule 3) that keeps every
+     * wavefront an MFMA wavefront (page "10. Tensor Cores, shapes, and tile
+     * alignment", section "Warp specialization is not ordinary occupancy",
+     * splits copies and MMA between warps).  The wavefronts of block row 1
+     * run one phase behind those of block row 0, and each wavefront
+     * alternates a phase of MFMAs only with a phase of fragment reads and
+     * copies, so each SIMD (which holds one wavefront of each block row)
+     * has one wavefront issuing MFMAs while the other feeds the next step.
+     * Four barriers per K-tile keep the phases aligned. */
+    static_assert(SPREAD != 6 || (!MX && !FP6 && !CONV && STAGES == 2 && KSTEPS == 2 && WGM == 2 && WGN == 4),
+                  "ping-pong: two block rows of four wavefronts, two stages of two K-steps");
+    constexpr bool DEEP_B = SPREAD == 5 || SPREAD == 6;
+    constexpr int BST = DEEP_B ? STAGES + 1 : STAGES;
+    constexpr int B_BASE = DEEP_B ? STAGES * A_BYTES : A_BYTES;
+    constexpr int LDS_BYTES = DEEP_B ? STAGES * A_BYTES + BST * B_BYTES : STAGES * STAGE_BYTES;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
@@ -458,7 +471,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
          * schedules 0, 4 and 5 (tile and prologue waits below) take this
          * path. */
         auto zero_tail = [&](uint32_t so, uint32_t sob, int32_t i) __attribute__((always_inline)) {
-            if constexpr (!FP6 && !MX && !CONV && (SPREAD == 0 || SPREAD == 4 || SPREAD == 5)) {
+            if constexpr (!FP6 && !MX && !CONV && (SPREAD == 0 || SPREAD == 4 || DEEP_B)) {
                 const int32_t kb = ktile(i) * KTB;
                 if (p.Kv > 0 && i < nkt && kb + KTB > p.Kv) {
                     unroll<A_LOADS + B_LOADS>([&](auto dc) __attribute__((always_inline)) {
@@ -787,7 +800,7 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
             int32_t kt = 0;
             /* prologue: the first PRE K-tiles of the unit (SPREAD 3: issued
              * by the producers) */
-            if constexpr (SPREAD == 5) {
+            if constexpr (DEEP_B) {
                 /* K-tiles 0 and 1: A in stages 0 and 1, B in B's stages 0 and 1 */
                 copy_tile(0u, B_BASE, kt);
                 copy_tile(A_BYTES, B_BASE + B_BYTES, kt + 1);
@@ -844,6 +857,94 @@ __global__ __launch_bounds__((WGM * WGN + (SPREAD == 3 ? 4 : 0)) * 64, MINB) voi
                     sa = na;
                     sb = nb;
                 }
+            } else if constexpr (SPREAD == 6) {
+                /* Per K-tile kt, four phases, each closed by a barrier:
+                 *   M0  the FM x FN MFMAs of K-step 0 (buffer 0)
+                 *   R0  K-step 1's fragments of kt into buffer 1; B's copies
+                 *       of kt+2 into B's stage of kt-1; then this wave's
+                 *       copies of kt+1 have landed
+                 *   M1  the MFMAs of K-step 1 (buffer 1)
+                 *   R1  K-step 0's fragments of kt+1 into buffer 0; A's
+                 *       copies of kt+2 into A's stage of kt
+                 * Block row 1 passes one barrier more before the loop and
+                 * block row 0 one more after it, so every wavefront passes
+                 * the same number and each barrier closes a phase of one
+                 * kind in block row 0 and of the other kind in block row 1.
+                 * Stage use: R1 of either row reads kt+1 after the barrier
+                 * that closes R0 of row 1 (row 0's R0 closed a phase
+                 * earlier), so every copy of kt+1 has landed; A's stage of
+                 * kt is last read in R0 of row 1, closed before row 0's R1
+                 * copies into it; B's stage of kt-1 was last read in R0 of
+                 * kt-1. */
+                auto mma = [&](auto cur_c) __attribute__((always_inline)) {
+                    constexpr int CUR = decltype(cur_c)::value;
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    unroll<FM * FN>([&](auto tc) __attribute__((always_inline)) {
+                        constexpr int t = decltype(tc)::value, i = t / FN, j = t % FN;
+                        if constexpr (!FP8 && MI == 32)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                        else if constexpr (!FP8)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[CUR][i], fb[CUR][j], acc[i][j], 0, 0, 0);
+                        else if constexpr (MI == 32)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[CUR][i], fb[CUR][j], acc[i][j],
+                                                                                         FA, FB, 0, 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[CUR][i], fb[CUR][j], acc[i][j],
+                                                                                          FA, FB, 0, 0, 0, 0);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                /* fragments of step nks of the stage at ns / nbs into buffer
+                 * TGT, with copies D0 .. D0+DN-1 spread over the reads */
+                auto feed = [&](auto tgt_c, const uint8_t *ns, const uint8_t *nbs, int nks, auto d0_c, auto dn_c,
+                                uint32_t dso, uint32_t dsob, uint32_t kb, const KV &kv) __attribute__((always_inline)) {
+                    constexpr int TGT = decltype(tgt_c)::value;
+                    constexpr int D0 = decltype(d0_c)::value, DN = decltype(dn_c)::value, NR = FM + FN;
+                    unroll<NR>([&](auto tc) __attribute__((always_inline)) {
+                        constexpr int t = decltype(tc)::value;
+                        if constexpr (t < FM)
+                            fa[TGT][t] = frag(ns + wm * WTM * RB, nks, t);
+                        else
+                            fb[TGT][t - FM] = frag(nbs + wn * WTN * RB, nks, t - FM);
+                        constexpr int j = (t * DN + NR - 1) / NR;
+                        if constexpr (j < DN && (j * NR) / DN == t)
+                            dma(std::integral_constant<int, D0 + j>{}, dso, dsob, kb, kv);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                };
+                auto phase_end = [&]() __attribute__((always_inline)) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                uint32_t sa = 0, sb = B_BASE;
+                auto next_b = [](uint32_t b) __attribute__((always_inline)) {
+                    return b + B_BYTES == B_BASE + BST * B_BYTES ? (uint32_t)B_BASE : b + B_BYTES;
+                };
+                const bool lag = wm == 1;
+                if (lag) phase_end();
+                for (; kt < nkt; ++kt) {
+                    const uint32_t na = sa ^ (uint32_t)A_BYTES, nb = next_b(sb), db = next_b(nb);
+                    const KV kv = kvalid(kt + 2);
+                    const uint32_t kb = (uint32_t)ktile(kt + 2) * KTB;
+                    mma(IC<0>{});
+                    phase_end();
+                    feed(IC<1>{}, smem + sa, smem + sb, 1, IC<A_LOADS>{}, IC<B_LOADS>{}, 0u, db, kb, kv);
+                    wait_vmcnt<B_LOADS>();
+                    zero_tail(na, nb, kt + 1);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    phase_end();
+                    mma(IC<1>{});
+                    phase_end();
+                    feed(IC<0>{}, smem + na, smem + nb, 0, IC<0>{}, IC<A_LOADS>{}, sa, 0u, kb, kv);
+                    phase_end();
+                    sa = na;
+                    sb = nb;
+                }
+                if (!lag) phase_end();
             } else if constexpr (KSTEPS % 2 == 0) {
                 /* one loop body; the stage advances around the ring */
                 for (; kt < nkt; ++kt) {
@@ -1477,7 +1578,9 @@ static hipError_t launch_tile(int32_t fmt, const GemmParams &p, hipStream_t stre
     X(61, 128, 128, 4, 1, 128, 4, 2, 2, 0, 32, 0)                                                   \
     X(62, 256, 256, false, 1, 128, 2, 2, 2, 4, 16, 0)                                               \
     X(63, 256, 256, false, 1, 128, 2, 2, 4, 5, 16, 0)                                               \
-    X(64, 256, 256, 1, 1, 128, 2, 2, 2, 5, 32, 0)
+    X(64, 256, 256, 1, 1, 128, 2, 2, 2, 5, 32, 0)                                                   \
+    X(65, 256, 256, false, 1, 128, 2, 2, 4, 6, 16, 0)                                               \
+    X(66, 256, 256, 1, 1, 128, 2, 2, 4, 6, 32, 0)
 
 /* every instantiation agrees with its tile-table entry */
 #define X(id, tm, tn, f8, mb, rb, st, wm, wn, sp, mi, opn)                                                      \

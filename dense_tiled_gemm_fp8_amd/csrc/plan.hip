@@ -420,7 +420,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
     const bool in_place = (dclass == 0 || dclass == 1) && !conv;
     const bool ktail = kbytes % 16 != 0;
     const bool tail_tile_ok = a.tile < 0 || kTiles[a.tile].spread == 0 || kTiles[a.tile].spread == 4 ||
-                              kTiles[a.tile].spread == 5;
+                              kTiles[a.tile].spread == 5 || kTiles[a.tile].spread == 6;
     const double peak_cu = fp4 || fp6 ? kPeakFp4PerCu : dclass ? kPeakFp8PerCu : kPeakBf16PerCu;
     const bool repack_misaligned =
         2.0 * (double)M * (double)N * (double)K * (double)batch / (peak_cu * S) >= kRepackMisalignedSec;
@@ -472,7 +472,7 @@ gemm355_status make_plan(const gemm355_args &a, int32_t S, Plan &P, const ConvSh
         const TileCfg &cfg = kTiles[t];
         if (cfg.dtype_class != dclass || cfg.op != want_op) continue;
         if (a.tile >= 0 && a.tile != t) continue;
-        if (P.Kv && cfg.spread != 0 && cfg.spread != 4 && cfg.spread != 5) continue;
+        if (P.Kv && cfg.spread != 0 && cfg.spread != 4 && cfg.spread != 5 && cfg.spread != 6) continue;
         Cand base;
         base.tile = t;
         base.tiles_m = cdiv(std::max<int64_t>(M, 1), cfg.TM);

@@ -43,11 +43,16 @@ struct TileCfg {
                               row at a time (bf16); 5 as 0 with B's ring
                               one stage deeper, B's copies of a K-tile in
                               the first K-step two tiles before and A's in
-                              the last (2 stages of 2 K-steps)              */
+                              the last (2 stages of 2 K-steps); 6 as 5 in
+                              a ping-pong loop: the two block rows of
+                              wavefronts alternate phases of MFMAs only and
+                              of fragment reads and copies, one phase apart
+                              (2 x 4 wavefronts)                            */
     int32_t mfma;          /* MFMA block edge: 32 (32x32) or 16 (16x16)      */
     int32_t lds_bytes;     /* stages * (TM + TN) * RB, plus 4 (8 for FP4)
                               bytes of block scales per row and stage for
-                              MX; one more B stage with copy schedule 5     */
+                              MX; one more B stage with copy schedules 5
+                              and 6                                         */
     int32_t min_blocks;    /* workgroups per CU the kernel is compiled for   */
     int32_t vgpr_budget;   /* 512 / (min_blocks * tile_waves / 4): registers
                               per lane one wave may hold                    */
@@ -164,6 +169,10 @@ constexpr TileCfg kTiles[] = {
     /* the 8-bit 256 x 256 tile (4 wavefronts, 32 x 32 blocks) with copy
      * schedule 5 */
     {1, 256, 256, 128, 128, 2, 2, 2, 5, 32, 2 * 256 * 128 + 3 * 256 * 128, 1, 512, {0.70f, 0.70f, 0.70f, 0.70f}, 1.24f},
+    /* copy schedule 5 in a ping-pong loop (schedule 6): the bf16 tile 63 and
+     * an 8-bit tile of 8 wavefronts with 32 x 32 blocks */
+    {0, 256, 256, 64, 128, 2, 2, 4, 6, 16, 2 * 256 * 128 + 3 * 256 * 128, 1, 256, {0.71f, 0.71f, 0.71f, 0.71f}, 1.24f},
+    {1, 256, 256, 128, 128, 2, 2, 4, 6, 32, 2 * 256 * 128 + 3 * 256 * 128, 1, 256, {0.66f, 0.66f, 0.66f, 0.66f}, 1.18f},
 };
 constexpr int32_t kNumTiles = (int32_t)(sizeof(kTiles) / sizeof(kTiles[0]));
 

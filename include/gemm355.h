@@ -383,7 +383,9 @@ GEMM355_API gemm355_status gemm355_unit(const gemm355_args *args, int64_t u,
  * over the last two K-steps; 3: producer wavefronts issue every copy; 4: as
  * 0 with A's fragments single-buffered; 5: as 0 with B's ring one stage
  * deeper than A's, B's copies in the first K-step, so lds_bytes holds
- * stages A tiles and stages + 1 B tiles).  Outputs are host pointers; NULL
+ * stages A tiles and stages + 1 B tiles; 6: schedule 5 in a ping-pong loop,
+ * the two block rows of wavefronts alternating phases of MFMAs only and of
+ * fragment reads and copies, one phase apart).  Outputs are host pointers; NULL
  * ones are skipped.  EINVAL if tile is not in [0, gemm355_num_tiles()). */
 GEMM355_API int32_t gemm355_num_tiles(void);
 GEMM355_API gemm355_status gemm355_tile_info(int32_t tile, int32_t *dtype_class,

@@ -425,10 +425,13 @@ def test_tile_table(g):
         # block-scaled tiles keep one dword of E8M0 scales (four 32-value
         # blocks) per 128 values, per row and stage
         scale_bytes = {2: 4, 3: 8, 4: 4}.get(cls, 0)
-        # copy schedule 5 keeps one more B tile than A tiles
-        b_stages = info["stages"] + (1 if info["schedule"] == 5 else 0)
+        # copy schedules 5 and 6 keep one more B tile than A tiles
+        b_stages = info["stages"] + (1 if info["schedule"] in (5, 6) else 0)
         assert info["lds_bytes"] == (info["stages"] * info["T_M"] + b_stages * info["T_N"]) * (row_bytes + scale_bytes)
-        assert info["schedule"] in range(6)
+        assert info["schedule"] in range(7)
+        if info["schedule"] == 6:
+            # the ping-pong pairs the two block rows of 2 x 4 wavefronts
+            assert info["waves"] == 8 and info["stages"] == 2
         assert info["lds_bytes"] <= 160 * 1024
         seen.add((info["dtype_class"], info["T_M"], info["T_N"]))
     assert (0, 256, 256) in seen and (1, 256, 256) in seen and (2, 256, 256) in seen and (3, 256, 256) in seen
