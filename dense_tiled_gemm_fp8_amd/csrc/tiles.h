@@ -79,7 +79,7 @@ constexpr int32_t kMaxWavesPerSimd = 8;
 constexpr TileCfg kTiles[] = {
     /* bf16, 128-byte K-tiles, 2 stages */
     {0, 256, 256, 64, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.55f, 0.55f, 0.55f, 0.55f}, 1.16f},
-    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.34f, 0.45f, 0.45f, 0.45f}, 1.16f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 0, 32, 2 * (128 + 128) * 128, 2, 256, {0.27f, 0.45f, 0.45f, 0.45f}, 1.16f},
     {0, 64, 64, 64, 128, 2, 2, 2, 0, 32, 2 * (64 + 64) * 128, 4, 128, {0.11f, 0.18f, 0.21f, 0.22f}, 1.16f},
     /* E4M3, 128-byte K-tiles, 2 stages */
     {1, 256, 256, 128, 128, 2, 2, 2, 0, 32, 2 * (256 + 256) * 128, 1, 512, {0.68f, 0.68f, 0.68f, 0.68f}, 1.04f},
@@ -131,7 +131,7 @@ constexpr TileCfg kTiles[] = {
      * last two K-steps of each K-tile */
     {0, 256, 256, 64, 128, 2, 2, 2, 2, 32, 2 * (256 + 256) * 128, 1, 512, {0.67f, 0.67f, 0.67f, 0.67f}, 1.04f},
     {0, 256, 256, 64, 128, 2, 2, 4, 2, 32, 2 * (256 + 256) * 128, 1, 256, {0.63f, 0.63f, 0.63f, 0.63f}, 1.12f},
-    {0, 128, 128, 64, 128, 2, 2, 2, 2, 32, 2 * (128 + 128) * 128, 2, 256, {0.37f, 0.48f, 0.48f, 0.48f}, 1.12f},
+    {0, 128, 128, 64, 128, 2, 2, 2, 2, 32, 2 * (128 + 128) * 128, 2, 256, {0.33f, 0.48f, 0.48f, 0.48f}, 1.12f},
     /* 256 x 128, 3 stages: producer wavefronts (warp specialisation) with
      * 32 x 32 and 16 x 16 blocks and for E4M3, and the same tile with
      * uniform wavefronts for comparison */
