@@ -366,6 +366,21 @@ def fp8_end_to_end(torch, g, inputs, args):
             "quantize_hbm_gbs": round((2 * 2 * (M + N) * K + (M + N) * K) / times["quantize"] / 1e9, 1),
             "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"],
         })
+        if not args.no_cpu_baseline:
+            from types import SimpleNamespace
+            from oracle import quant as quant_oracle
+            xa = xs[0].float().cpu().numpy().reshape(-1)
+            q_cpu = sampled_oracle(lambda n: quant_oracle.quantize(xa[:n * 65536], fmt), M * K // 65536, 65536.0,
+                                   2.0 * M * K / 65536, "gelem_s",
+                                   "the first %d x 65536 elements of A (maximum, scale, codes)")
+            torch.cuda.synchronize()
+            ops_q = SimpleNamespace(M=M, N=N, K=K, A=qa.cpu().numpy(), B=qb.cpu().numpy(), fmt=fmt, fmt_a=fmt,
+                                    fmt_b=fmt, batch=1)
+            out[-1]["cpu_oracle"] = {"quantize": q_cpu, "gemm": oracle_sample(ops_q, budget_s=1.0),
+                                     "full_s_estimate": None}
+            out[-1]["cpu_oracle"]["full_s_estimate"] = round(
+                q_cpu["full_s_estimate"] + out[-1]["cpu_oracle"]["gemm"]["full_s_estimate"], 2)
+            del xa, ops_q
     del xs
     torch.cuda.empty_cache()
     return out
@@ -388,6 +403,16 @@ def mx_products(torch, g, inputs, args):
         B = torch.from_numpy(ops.B).cuda()
         sa = torch.from_numpy(ops.bsa).cuda()
         sb = torch.from_numpy(ops.bsb).cuda()
+        cpu = None
+        if not args.no_cpu_baseline:
+            from oracle import mx as mx_oracle
+            ncol = 1024
+            Bc, sbc = ops.B[:ncol], ops.bsb[:ncol]
+            cpu = sampled_oracle(
+                lambda n: mx_oracle.gemm(ops.A[:n], ops.bsa[:n], Bc, sbc, ops.fmt_a, ops.fmt_b), M,
+                2.0 * ncol * K, M * (N / ncol), "gflops",
+                "the first %%d rows x the first %d columns of the product (binary64 values decoded from "
+                "codes and block scales, then one matrix product)" % ncol)
         del ops
         C = torch.empty((M, N), dtype=torch.float32, device="cuda")
         a = g.make_args(M, N, K, A=A, B=B, C=C, dtype=dt, block_scale_a=sa, block_scale_b=sb)
@@ -409,6 +434,8 @@ def mx_products(torch, g, inputs, args):
             "pct_mfma_peak": round(100 * flops / med / 1e12 / PEAK_TFLOPS["e4m3" if fmt in ("mxe4m3", "mxe5m2") else "fp4"], 1),
             "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"], "grid": p["grid"],
         })
+        if cpu is not None:
+            out[-1]["cpu_oracle"] = cpu
         del A, B, sa, sb, C
         torch.cuda.empty_cache()
     return out
@@ -461,9 +488,52 @@ def conv_layers(torch, g, inputs, args):
             "us_same_size_gemm": round(res["gemm"] * 1e6, 2),
             "tile": [p["T_M"], p["T_N"], p["T_K"]], "split": p["split"], "grid": p["grid"],
         })
+        if not args.no_cpu_baseline:
+            from oracle import conv as conv_oracle
+            xc = x.view(torch.int16).cpu().numpy().view(np.uint16)
+            wc = w.view(torch.int16).cpu().numpy().view(np.uint16)
+            out[-1]["cpu_oracle"] = sampled_oracle(
+                lambda n: conv_oracle.conv2d(xc[:n], wc, pad, pad), N, 2.0 * P * Q * K * Kg, N, "gflops",
+                "the first %d images (binary64, one matrix product per filter tap)")
         del x, w, y, A
         torch.cuda.empty_cache()
     return out
+
+
+def _numpy_threads():
+    """Threads of the BLAS numpy calls into (the oracle's matrix products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = sum(x.get("num_threads", 0) for x in threadpool_info() if x.get("user_api") == "blas")
+        if n:
+            return n
+    except Exception:   # threadpoolctl missing or unreadable: report the affinity set
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def sampled_oracle(run, n_max, work_per_item, full_items, unit, label, budget_s=1.0):
+    """Time the oracle (as it stands) on a bounded sample: run(n) computes n
+    items (rows, images, elements) of a workload of full_items; a probe at a
+    small n sizes the sample to about budget_s.  Returns seconds, the rate in
+    `unit` (work_per_item per item) and the full workload's time at that
+    rate."""
+    n0 = max(1, min(n_max, 8))
+    t0 = time.perf_counter()
+    run(n0)
+    probe = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(n_max, max(n0, n0 * budget_s / probe)))
+    t0 = time.perf_counter()
+    run(n)
+    t = time.perf_counter() - t0
+    if t < budget_s / 3 and n < n_max:
+        # the probe carried one-time costs: size once more from this run
+        n = int(min(n_max, n * budget_s / max(t, 1e-6)))
+        t0 = time.perf_counter()
+        run(n)
+        t = time.perf_counter() - t0
+    return {"seconds": round(t, 3), unit: round(n * work_per_item / t / 1e9, 3), "cores": _numpy_threads(),
+            "sample": label % (n,), "full_s_estimate": round(t * full_items / n, 2)}
 
 
 def oracle_sample(ops, budget_s=2.0):
