@@ -8,6 +8,7 @@
 * the work units a plan hands to the kernels cover every (tile, K-tile) once;
 * argument errors are reported before anything is launched.
 """
+import math
 import os
 import random
 import re
@@ -137,8 +138,10 @@ KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=3), dict(split_k=1,
          dict(split_k=5, persistent=1), dict(tile=1), dict(tile=2, persistent=1, split_k=1)]
 
 
-def _plan_and_check(g, M, N, K, batch, dtype, knobs):
-    if "tile" in knobs and dtype in (g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16):
+def _plan_and_check(g, M, N, K, batch, dtype, knobs, exact_tile=False):
+    if exact_tile:
+        pass
+    elif "tile" in knobs and dtype in (g.E4M3_F32, g.E5M2_F32, g.E4M3_E5M2_BF16):
         knobs = dict(knobs, tile=knobs["tile"] + 3)
     elif "tile" in knobs and dtype == g.MXE4M3_F32:
         knobs = dict(knobs, tile=knobs["tile"] + 48)           # the block-scaled 128x128 tiles
@@ -217,6 +220,51 @@ def test_units_cover_every_k_tile_once(g, M, N, K, batch, dt):
                 assert ranges == bk.kslices(p["nK"], p["split"])
         with pytest.raises(g.Gemm355Error):
             g.gemm355_unit(a, p["units"])
+
+
+def test_plan_bookkeeping_random(g):
+    """Seeded random shapes (log-uniform M, N up to 9000 and K up to 300000,
+    batches up to 7), every input dtype class, the knob sets and (in about a
+    third of the cases) a forced tile of the matching class: each plan
+    satisfies the oracle's grid, padding, eta, residency and schedule
+    arithmetic, and where the unit list is short every tile's K-tiles are
+    covered exactly once.  Block-scaled K is a multiple of 128, FP4's of 256
+    (the planner refuses any other)."""
+    rnd = random.Random(7)
+    classes = {"BF16": 0, "E4M3": 1, "E5M2": 1, "MXE4M3": 2, "MXFP4": 3, "MXFP6": 4}
+    by_class = {}
+    for t in range(g.gemm355_num_tiles()):
+        info = g.gemm355_tile_info(t)
+        if info["op"] == 0:
+            by_class.setdefault(info["dtype_class"], []).append(t)
+    for _ in range(1500):
+        M = int(math.exp(rnd.uniform(0, math.log(9000))))
+        N = int(math.exp(rnd.uniform(0, math.log(9000))))
+        K = int(math.exp(rnd.uniform(0, math.log(300000))))
+        batch = rnd.choice([1, 1, 1, 2, 3, 7])
+        name = rnd.choice(PLAN_DTYPES)
+        dtype = getattr(g, name)
+        if name.startswith("MX"):
+            step = 256 if name.startswith("MXFP4") else 128
+            K = -(-K // step) * step
+        knobs = rnd.choice(KNOBS)
+        exact = rnd.random() < 0.3
+        if exact:
+            cls = classes[name.split("_")[0]]
+            knobs = dict(rnd.choice(KNOBS[:5]), tile=rnd.choice(by_class[cls]))
+        a, p = _plan_and_check(g, M, N, K, batch, dtype, knobs, exact_tile=exact)
+        if exact:
+            assert p["tile"] == knobs["tile"]
+        if p["units"] <= 2000:
+            cover = {}
+            for u in range(p["units"]):
+                bt, i, j, kb, ke = g.gemm355_unit(a, u)
+                cover.setdefault((bt, i, j), []).append((kb, ke))
+            assert len(cover) == p["G"], (M, N, K, batch, name, knobs)
+            for ranges in cover.values():
+                ranges.sort()
+                assert ranges[0][0] == 0 and ranges[-1][1] == p["nK"]
+                assert all(e0 == b1 for (_, e0), (b1, _) in zip(ranges, ranges[1:]))
 
 
 def test_plan_reports_efficiency_levers(g):
