@@ -19,6 +19,16 @@ LIB_PATH = os.path.join(_HERE, "libgemm355.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgemm355.so is not built; run python -m dense_tiled_gemm_fp8_amd.build")
+# One HIP runtime per process: PyTorch's ROCm wheels carry their own
+# libamdhip64, which they load under a name the dynamic loader does not match
+# to a runtime already loaded from the system ROCm, so loading this library
+# first would leave two runtimes (and torch's device memory foreign to the
+# one this library launches on).  Loaded after torch, the library binds to
+# torch's runtime.
+try:
+    import torch  # noqa: F401
+except ImportError:   # no PyTorch in the process: the system runtime is the only one
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 # status codes

@@ -23,6 +23,13 @@
  *     stream).  Argument errors are reported before anything is launched;
  *     faults inside kernels surface at the caller's next synchronisation.
  *   - No entry point aborts, prints or throws; each returns a status code.
+ *   - One HIP runtime per process: the library calls the libamdhip64 the
+ *     process has loaded.  PyTorch's ROCm wheels carry their own copy,
+ *     which they load under a name the loader does not match to one loaded
+ *     first from the system ROCm; in a process that uses such a PyTorch,
+ *     load PyTorch before this library (the Python binding does), or the
+ *     process holds two runtimes and PyTorch's device memory is foreign to
+ *     the library's launches (they fail with EHIP).
  *   - All entry points are thread-safe.  Scratch the library owns is kept
  *     per device and stream; a call holds that buffer from its lookup until
  *     its last kernel is enqueued, so concurrent calls on one stream enqueue

@@ -8,6 +8,8 @@ inputs make every summation order give the same bits, so those cases demand
 bit-identical results through every tile, split, schedule, layout and batch
 path (a dropped, duplicated or stale tile, K-slice or LDS stage changes bits).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -477,6 +479,30 @@ def test_library_scratch_cap_enomem():
         g.gemm355_set_scratch_limit(prev)
     for out in (C, Cw, C0):
         assert np.array_equal(out.double().cpu().numpy(), ref)
+
+
+def test_binding_imported_before_torch():
+    """A fresh process that imports the binding before anything else: the
+    binding loads PyTorch first, so the library binds to torch's HIP runtime
+    (a second runtime loaded from the system ROCm would make torch's device
+    memory foreign to the library's launches) and a product is exact."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from dense_tiled_gemm_fp8_amd import gemm355 as g\n"
+        "from tests import gpu_helpers as H\n"
+        "maps = open('/proc/self/maps').read()\n"
+        "libs = set(l.split()[-1] for l in maps.split('\\n') if 'libamdhip64' in l)\n"
+        "assert len(libs) == 1, libs\n"
+        "ops = H.exact_ops(300, 200, 256, 'bf16', 123)\n"
+        "ref, _ = H.oracle_full(ops, 0, alpha=1.0)\n"
+        "C = H.run(ops, out='f32')\n"
+        "assert (C == ref).all()\n"
+        "print('one runtime, exact')\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    H.say("binding imported first, fresh process")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and "one runtime, exact" in r.stdout, r.stdout + r.stderr
 
 
 def test_degenerate_sizes():
