@@ -50,3 +50,55 @@ def test_random_cases_exact(block):
         for bi in range(max(batch, 1)):
             ref, _ = H.oracle_full(ops, bi, alpha=1.0)
             assert np.array_equal(Cb[bi], ref), what
+
+
+LAYOUTS = [g.A_ROW_B_COL, g.A_ROW_B_ROW, g.A_COL_B_COL, g.A_COL_B_ROW]
+
+
+def _stored(codes_rows_by_k, k_contig, ld, off, fill):
+    """A logical rows x K operand (codes) laid out K-contiguous (rows of ld
+    elements) or transposed (K rows of ld elements), starting `off` elements
+    into a buffer whose every other element is a NaN code."""
+    rows, K = codes_rows_by_k.shape
+    st = codes_rows_by_k if k_contig else np.ascontiguousarray(codes_rows_by_k.T)
+    n_rows, n_cols = st.shape
+    buf = np.full(off + n_rows * ld + 64, fill, dtype=st.dtype)
+    buf[off:off + n_rows * ld].reshape(n_rows, ld)[:, :n_cols] = st
+    return H.dev(buf)[off:]
+
+
+@pytest.mark.parametrize("block", range(3))
+def test_random_layouts_exact(block):
+    """Random storage layout (the three non-native ones are repacked on the
+    device), leading dimensions padded past the matrix with NaN codes,
+    operands starting off 16-byte boundaries, fp32 or bf16 C (bf16 against
+    the exact result rounded to nearest even), forced tiles and knobs:
+    exact integers, bit for bit."""
+    import torch
+    rnd = random.Random(2000 + block)
+    for case in range(30):
+        fmt = rnd.choice(["bf16", "e4m3", "e5m2", "e4m3e5m2"])
+        M, N, K = rnd.randint(1, 400), rnd.randint(1, 400), rnd.randint(1, 700)
+        layout = rnd.choice(LAYOUTS)
+        a_row = layout in (g.A_ROW_B_COL, g.A_ROW_B_ROW)
+        b_col = layout in (g.A_ROW_B_COL, g.A_COL_B_COL)
+        pad_a, pad_b = rnd.choice([0, 0, 1, 3, 8, 17]), rnd.choice([0, 0, 1, 3, 8, 17])
+        off_a, off_b = rnd.choice([0, 0, 1, 5]), rnd.choice([0, 0, 1, 5])
+        out = rnd.choice(["f32", "bf16"])
+        tile = rnd.choice(TILES[CLASS[fmt]] + [-1, -1])
+        knobs = rnd.choice(KNOBS)
+        ops = H.exact_ops(M, N, K, fmt, 60000 + 100 * block + case)
+        fa, fb = H.elem_formats(fmt)
+        nan = {"bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F), "e5m2": np.uint8(0x7F)}
+        lda = (K if a_row else M) + pad_a
+        ldb = (K if b_col else N) + pad_b
+        A_dev = _stored(ops.A, a_row, lda, off_a, nan[fa])
+        B_dev = _stored(ops.B, b_col, ldb, off_b, nan[fb])
+        what = "layout case %d.%d: %s M=%d N=%d K=%d layout=%d lda=%d ldb=%d off=%d,%d out=%s tile=%d %s" % (
+            block, case, fmt, M, N, K, layout, lda, ldb, off_a, off_b, out, tile, knobs)
+        H.say(what)
+        C = H.run(ops, out=out, layout=layout, A_dev=A_dev, B_dev=B_dev, lda=lda, ldb=ldb, tile=tile, **knobs)
+        ref, _ = H.oracle_full(ops, 0, alpha=1.0)
+        if out == "bf16":
+            ref = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(C, ref), what
