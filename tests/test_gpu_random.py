@@ -102,3 +102,54 @@ def test_random_layouts_exact(block):
         if out == "bf16":
             ref = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
         assert np.array_equal(C, ref), what
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_random_convolutions_exact(block):
+    """Random implicit-GEMM convolutions: image count and size, channels (64
+    to 256), filter count and size, padding, stride and dilation, every
+    convolution tile or the planner's, split and persistence knobs, fp32 or
+    bf16 output, small integer images and filters: bit for bit against the
+    oracle's convolution (bf16 output: the exact result rounded to nearest
+    even)."""
+    import torch
+    from dense_tiled_gemm_fp8_amd import inputs
+    from oracle import conv as oc
+    conv_tiles = [t for t in range(g.gemm355_num_tiles()) if g.gemm355_tile_info(t)["op"] == 1]
+    rnd = random.Random(3000 + block)
+    done = 0
+    while done < 20:
+        N, Hh, W = rnd.randint(1, 4), rnd.randint(1, 24), rnd.randint(1, 24)
+        C, K = rnd.choice([64, 128, 192, 256]), rnd.randint(1, 300)
+        R, S = rnd.randint(1, 5), rnd.randint(1, 5)
+        ph, pw = rnd.randint(0, 3), rnd.randint(0, 3)
+        sh, sw, dh, dw = rnd.choice([1, 1, 2, 3]), rnd.choice([1, 1, 2, 3]), rnd.choice([1, 1, 2]), rnd.choice([1, 1, 2])
+        P, Q = oc.out_size(Hh, W, R, S, ph, pw, sh, sw, dh, dw)
+        if P < 1 or Q < 1:
+            continue
+        tile = rnd.choice(conv_tiles + [-1, -1])
+        knobs = rnd.choice(KNOBS)
+        out = rnd.choice(["f32", "bf16"])
+        gen = inputs.rng(70000 + 100 * block + done)
+        x = inputs.small_int_codes(gen, (N, Hh, W, C), "bf16")
+        w = inputs.small_int_codes(gen, (K, R, S, C), "bf16")
+        what = "conv case %d.%d: N=%d %dx%dx%d K=%d %dx%d pad %d,%d stride %d,%d dil %d,%d out=%s tile=%d %s" % (
+            block, done, N, Hh, W, C, K, R, S, ph, pw, sh, sw, dh, dw, out, tile, knobs)
+        H.say(what)
+        # the device copies stay referenced until the call has run (make_conv_args keeps raw pointers)
+        xd, wd = H.dev(x), H.dev(w)
+        a = g.make_conv_args(N, Hh, W, C, K, R, S, x=xd, w=wd, pad_h=ph, pad_w=pw, stride_h=sh,
+                             stride_w=sw, dil_h=dh, dil_w=dw, dtype=g.BF16_BF16 if out == "bf16" else g.BF16_F32,
+                             tile=tile, **knobs)
+        y = torch.full((N, P, Q, K), float("nan"), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
+                       device="cuda")
+        a.y = y.data_ptr()
+        g.gemm355_conv2d(a)
+        torch.cuda.synchronize()
+        got = y.float().cpu().numpy().astype(np.float64)
+        del xd, wd
+        ref, _ = oc.conv2d(x, w, ph, pw, sh, sw, dh, dw)
+        if out == "bf16":
+            ref = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(got, ref), what
+        done += 1
