@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(reference kernel for scaling the HBM byte counters)")
+    ap.add_argument("--pass-floor", type=int, default=0, metavar="BYTES",
+                    help="only time two reference passes, 300 times each: an in-place add on one "
+                         "float (what any extra launch costs) and on BYTES of floats (a plain pass "
+                         "reading and writing that many bytes, to set beside the split-K combine)")
     return ap.parse_args()
 
 
@@ -101,6 +105,29 @@ def copy_reference(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": nbytes, "us_per_copy": round(us, 2),
                       "read_plus_write_tb_s": round(2 * nbytes / (us * 1e-6) / 1e12, 3)}), flush=True)
     log("copy reference: 5 x %d bytes" % nbytes)
+
+
+def pass_floor(nbytes: int) -> None:
+    """Two reference passes on the benchmark's stream, 300 times each: an
+    in-place add on one float (the cost of one more launch with next to no
+    work) and on nbytes of floats (one dependent read and write of every
+    byte).  The split-K combine is such a pass over the partial sums."""
+    import torch
+    one = torch.zeros(1, dtype=torch.float32, device="cuda")
+    big = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = {"pass_floor_bytes": nbytes}
+    for name, t in (("us_one_float", one), ("us_per_pass", big)):
+        for _ in range(20):
+            t.add_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(300):
+            t.add_(1.0)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / 300, 2)
+    print(json.dumps(out), flush=True)
+    log("pass floor: 300 x one float, 300 x %d bytes" % nbytes)
 
 
 class Case:
@@ -605,6 +632,9 @@ def main():
         sys.exit(2)
     if args.copy_bytes:
         copy_reference(args.copy_bytes)
+        return
+    if args.pass_floor:
+        pass_floor(args.pass_floor)
         return
     import numpy as np
     import torch
