@@ -184,6 +184,7 @@ class Case:
         makespan), the shader clock over the units (MHz) and the MFMA
         cycle efficiency inside units: the dense-MFMA cycles of the executed
         (padded) tile work over the measured shader cycles."""
+        import numpy as np
         p = self.plan
         if not p["units"]:
             return None
@@ -205,6 +206,19 @@ class Case:
         per_clk = (4096.0 if self.fmt == "bf16" else 8192.0) / p["b"]
         ideal = 2.0 * p["T_M"] * p["T_N"] * p["T_K"] * p["G"] * p["nK"] / per_clk
         n = float(len(st))
+        # per XCD: the hardware deals workgroups to the 8 XCDs round-robin and
+        # the kernel renumbers them so that XCD x runs the logical slots
+        # [x q, (x + 1) q), q = grid / 8; unit u runs in slot u % grid
+        xcd = None
+        if p["grid"] % 8 == 0:
+            slot_xcd = (np.arange(len(st)) % p["grid"]) // (p["grid"] // 8)
+            t0 = st[:, 0].min()
+            xcd = {"sclk_mhz": [], "last_end_us": []}
+            for x in range(8):
+                m = slot_xcd == x
+                rt = (st[m, 1] - st[m, 0]).sum()
+                xcd["sclk_mhz"].append(round(float(100.0 * (st[m, 3] - st[m, 2]).sum() / rt), 0) if rt > 0 else None)
+                xcd["last_end_us"].append(round(float((st[m, 1].max() - t0) / 100.0), 2) if m.any() else None)
         return {"eta": float(busy_rt / (p["S"] * p["b"] * span)),
                 "sclk_mhz": float(100.0 * cycles / busy_rt),
                 "mfma_cycle_eff": float(ideal / cycles),
@@ -212,7 +226,8 @@ class Case:
                 # epilogue until its stores are issued, and their completion
                 "unit_cycles": {"loop": round(float((st[:, 4] - st[:, 2]).sum()) / n),
                                 "epilogue": round(float((st[:, 5] - st[:, 4]).sum()) / n),
-                                "store_drain": round(float((st[:, 3] - st[:, 5]).sum()) / n)}}
+                                "store_drain": round(float((st[:, 3] - st[:, 5]).sum()) / n)},
+                "per_xcd": xcd}
 
     def step(self, stream):
         a = self.args[self.i % self.copies]
@@ -727,6 +742,7 @@ def main():
                 detail[-1]["sclk_mhz"] = None if me is None else round(me["sclk_mhz"], 0)
                 detail[-1]["mfma_cycle_eff"] = None if me is None else round(me["mfma_cycle_eff"], 4)
                 detail[-1]["unit_cycles"] = None if me is None else me["unit_cycles"]
+                detail[-1]["per_xcd"] = None if me is None else me["per_xcd"]
                 if c is not head:
                     del c
                     torch.cuda.empty_cache()
