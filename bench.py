@@ -130,6 +130,28 @@ def pass_floor(nbytes: int) -> None:
     log("pass floor: 300 x one float, 300 x %d bytes" % nbytes)
 
 
+def per_xcd(st, grid: int):
+    """Shader clock (MHz) and last finish (us after the first start) of the
+    units each XCD ran, from the per-unit stamps st[u] = (real-time start,
+    real-time end, cycles at start, cycles at end, ...), the real-time clock
+    ticking at 100 MHz.  The hardware deals workgroups to the 8 XCDs
+    round-robin and the kernel renumbers them so that XCD x runs the logical
+    slots [x q, (x + 1) q), q = grid / 8; unit u runs in slot u % grid.  None
+    when grid is not a multiple of 8 (the renumbering is then uneven)."""
+    import numpy as np
+    if grid <= 0 or grid % 8:
+        return None
+    slot_xcd = (np.arange(len(st)) % grid) // (grid // 8)
+    t0 = st[:, 0].min()
+    out = {"sclk_mhz": [], "last_end_us": []}
+    for x in range(8):
+        m = slot_xcd == x
+        rt = (st[m, 1] - st[m, 0]).sum()
+        out["sclk_mhz"].append(round(float(100.0 * (st[m, 3] - st[m, 2]).sum() / rt), 0) if rt > 0 else None)
+        out["last_end_us"].append(round(float((st[m, 1].max() - t0) / 100.0), 2) if m.any() else None)
+    return out
+
+
 class Case:
     """Device-resident operands of one workload shape (with rotation copies
     for HBM-bound shapes) and a callable that runs one step."""
@@ -206,19 +228,7 @@ class Case:
         per_clk = (4096.0 if self.fmt == "bf16" else 8192.0) / p["b"]
         ideal = 2.0 * p["T_M"] * p["T_N"] * p["T_K"] * p["G"] * p["nK"] / per_clk
         n = float(len(st))
-        # per XCD: the hardware deals workgroups to the 8 XCDs round-robin and
-        # the kernel renumbers them so that XCD x runs the logical slots
-        # [x q, (x + 1) q), q = grid / 8; unit u runs in slot u % grid
-        xcd = None
-        if p["grid"] % 8 == 0:
-            slot_xcd = (np.arange(len(st)) % p["grid"]) // (p["grid"] // 8)
-            t0 = st[:, 0].min()
-            xcd = {"sclk_mhz": [], "last_end_us": []}
-            for x in range(8):
-                m = slot_xcd == x
-                rt = (st[m, 1] - st[m, 0]).sum()
-                xcd["sclk_mhz"].append(round(float(100.0 * (st[m, 3] - st[m, 2]).sum() / rt), 0) if rt > 0 else None)
-                xcd["last_end_us"].append(round(float((st[m, 1].max() - t0) / 100.0), 2) if m.any() else None)
+        xcd = per_xcd(st, p["grid"])
         return {"eta": float(busy_rt / (p["S"] * p["b"] * span)),
                 "sclk_mhz": float(100.0 * cycles / busy_rt),
                 "mfma_cycle_eff": float(ideal / cycles),

@@ -1,5 +1,6 @@
 """Host-side pieces of bench.py that need no GPU: the one-GPU refusal and
-the bounded oracle sampling used for the CPU baselines."""
+the bounded oracle sampling used for the CPU baselines, and the per-XCD
+grouping of the clock-hook stamps."""
 import os
 import subprocess
 import sys
@@ -42,3 +43,21 @@ def test_sampled_oracle_sizes_and_scales():
     calls.clear()
     r = bench.sampled_oracle(run, 3, 1.0, 3, "gflops", "%d", budget_s=0.01)
     assert max(calls) == 3 and r["full_s_estimate"] == pytest.approx(r["seconds"], rel=0.05, abs=0.01)
+
+
+def test_per_xcd_groups_units_by_slot():
+    """bench.per_xcd: unit u runs in slot u % grid, slots [32x, 32x + 32) of a
+    256 grid on XCD x; the clock is cycles over real time (100 MHz ticks)."""
+    import numpy as np
+
+    grid, units = 256, 512
+    st = np.zeros((units, 6))
+    for u in range(units):
+        x = (u % grid) // 32
+        start = 0.0 if u < grid else 1000.0 + 10 * x
+        st[u, 0], st[u, 1] = start, start + 1000.0          # 10 us each
+        st[u, 2], st[u, 3] = 0.0, (1600.0 + 25 * x) * 10.0  # cycles over 10 us
+    out = bench.per_xcd(st, grid)
+    assert out["sclk_mhz"] == [1600.0 + 25 * x for x in range(8)]
+    assert out["last_end_us"] == [20.0 + 0.1 * x for x in range(8)]
+    assert bench.per_xcd(st, 250) is None
