@@ -27,7 +27,7 @@ KNOBS = [dict(), dict(split_k=1, persistent=0), dict(split_k=1, persistent=1), d
          dict(split_k=3, persistent=1), dict(split_k=6), dict(persistent=1, cus=7), dict(cus=13)]
 
 
-@pytest.mark.parametrize("block", range(4))
+@pytest.mark.parametrize("block", range(8))
 def test_random_cases_exact(block):
     rnd = random.Random(1000 + block)
     for case in range(30):
@@ -67,7 +67,7 @@ def _stored(codes_rows_by_k, k_contig, ld, off, fill):
     return H.dev(buf)[off:]
 
 
-@pytest.mark.parametrize("block", range(3))
+@pytest.mark.parametrize("block", range(5))
 def test_random_layouts_exact(block):
     """Random storage layout (the three non-native ones are repacked on the
     device), leading dimensions padded past the matrix with NaN codes,
@@ -104,7 +104,7 @@ def test_random_layouts_exact(block):
         assert np.array_equal(C, ref), what
 
 
-@pytest.mark.parametrize("block", range(2))
+@pytest.mark.parametrize("block", range(4))
 def test_random_convolutions_exact(block):
     """Random implicit-GEMM convolutions: image count and size, channels (64
     to 256), filter count and size, padding, stride and dilation, every
