@@ -8,7 +8,8 @@
  * Covers gemm355_gemm (automatic plan, forced split-K with its combine pass,
  * persistent grid), gemm355_gemm_ex (E4M3 operands, bf16 output, batch with
  * per-entry scales, a caller workspace), gemm355_gemm_noalloc, gemm355_plan,
- * K == 0, and an argument error.  Prints one line per case; exit status 0
+ * the convolution entry points (output size, plan, automatic and split-K
+ * runs), K == 0, and an argument error.  Prints one line per case; exit status 0
  * when all agree.
  */
 #include <math.h>
@@ -228,6 +229,72 @@ int main(void)
     HIP_OK(hipMemcpy(c, dC, 2 * c_bytes, hipMemcpyDeviceToHost));
     check_f32("gemm_noalloc_batch_0", c, ref, M * N, 1.0);
     check_f32("gemm_noalloc_batch_1", c + M * N, ref + M * N, M * N, 0.5);
+
+    /* Convolution (bf16 NHWC images, KRSC filters, fp32 NPQK output) with
+     * padding, stride and dilation, automatic and split along K, against a
+     * direct loop over the window. */
+    {
+        gemm355_conv_args cv;
+        memset(&cv, 0, sizeof cv);
+        cv.N = 2; cv.H = 9; cv.W = 11; cv.C = 64; cv.K = 40; cv.R = 3; cv.S = 2;
+        cv.pad_h = 1; cv.pad_w = 1; cv.stride_h = 2; cv.stride_w = 1; cv.dil_h = 1; cv.dil_w = 2;
+        cv.dtype = GEMM355_BF16_F32; cv.tile = -1; cv.persistent = -1;
+        int64_t P = 0, Q = 0;
+        expect_status("conv_out_size", gemm355_conv2d_out_size(&cv, &P, &Q), GEMM355_OK);
+        if (P != 5 || Q != 11) {
+            fprintf(stderr, "conv_out_size: P %lld Q %lld, expected 5 and 11\n", (long long)P, (long long)Q);
+            ++failures;
+        }
+        const int64_t nx = cv.N * cv.H * cv.W * cv.C, nw = cv.K * cv.R * cv.S * cv.C;
+        const int64_t ny = cv.N * P * Q * cv.K;
+        int8_t *x = malloc((size_t)nx), *w = malloc((size_t)nw);
+        uint16_t *x16 = malloc(2 * (size_t)nx), *w16 = malloc(2 * (size_t)nw);
+        int64_t *yref = malloc(sizeof(int64_t) * (size_t)ny);
+        float *y = malloc(sizeof(float) * (size_t)ny);
+        if (!x || !w || !x16 || !w16 || !yref || !y) {
+            fprintf(stderr, "host allocation failed\n");
+            return 3;
+        }
+        for (int64_t e = 0; e < nx; ++e) { x[e] = (int8_t)next_small(); x16[e] = bf16_of_int(x[e]); }
+        for (int64_t e = 0; e < nw; ++e) { w[e] = (int8_t)next_small(); w16[e] = bf16_of_int(w[e]); }
+        for (int64_t n = 0; n < cv.N; ++n)
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t q = 0; q < Q; ++q)
+                    for (int64_t k = 0; k < cv.K; ++k) {
+                        int64_t acc = 0;
+                        for (int64_t r = 0; r < cv.R; ++r)
+                            for (int64_t t = 0; t < cv.S; ++t) {
+                                const int64_t h = p * cv.stride_h - cv.pad_h + r * cv.dil_h;
+                                const int64_t v = q * cv.stride_w - cv.pad_w + t * cv.dil_w;
+                                if (h < 0 || h >= cv.H || v < 0 || v >= cv.W) continue;
+                                for (int64_t c = 0; c < cv.C; ++c)
+                                    acc += (int64_t)x[((n * cv.H + h) * cv.W + v) * cv.C + c] *
+                                           w[((k * cv.R + r) * cv.S + t) * cv.C + c];
+                            }
+                        yref[((n * P + p) * Q + q) * cv.K + k] = acc;
+                    }
+        void *dx, *dw, *dy;
+        HIP_OK(hipMalloc(&dx, 2 * (size_t)nx));
+        HIP_OK(hipMalloc(&dw, 2 * (size_t)nw));
+        HIP_OK(hipMalloc(&dy, sizeof(float) * (size_t)ny));
+        HIP_OK(hipMemcpy(dx, x16, 2 * (size_t)nx, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(dw, w16, 2 * (size_t)nw, hipMemcpyHostToDevice));
+        cv.x = dx; cv.w = dw; cv.y = dy;
+        gemm355_plan_t cplan;
+        expect_status("conv_plan", gemm355_conv2d_plan(&cv, &cplan), GEMM355_OK);
+        static const struct { const char *name; int32_t split; } cmodes[] = {
+            {"conv_auto", 0}, {"conv_split3", 3}};
+        for (size_t m = 0; m < sizeof cmodes / sizeof cmodes[0]; ++m) {
+            cv.split_k = cmodes[m].split;
+            HIP_OK(hipMemsetAsync(dy, 0xFF, sizeof(float) * (size_t)ny, stream));
+            expect_status(cmodes[m].name, gemm355_conv2d(&cv, (void *)stream), GEMM355_OK);
+            HIP_OK(hipStreamSynchronize(stream));
+            HIP_OK(hipMemcpy(y, dy, sizeof(float) * (size_t)ny, hipMemcpyDeviceToHost));
+            check_f32(cmodes[m].name, y, yref, ny, 1.0);
+        }
+        HIP_OK(hipFree(dx)); HIP_OK(hipFree(dw)); HIP_OK(hipFree(dy));
+        free(x); free(w); free(x16); free(w16); free(yref); free(y);
+    }
 
     /* K == 0 writes zeros; a negative extent is an argument error. */
     HIP_OK(hipMemsetAsync(dC, 0xFF, c_bytes, stream));
