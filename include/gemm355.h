@@ -481,10 +481,19 @@ typedef struct gemm355_conv_args {
 
 GEMM355_API gemm355_status gemm355_conv2d(const gemm355_conv_args *args, void *stream);
 
-/* The plan of that product (P and Q follow from the arguments). */
+/* The plan of that convolution's implicit product (M = N P Q, N = K,
+ * K = R S C; P and Q follow from the arguments): the same fields as
+ * gemm355_plan (tile grid, wave and padding efficiency, split and
+ * persistence, as defined on page "10. Tensor Cores, ...", sections "Shape
+ * the operation", "Padding efficiency" and "When shape alone can't fix wave
+ * efficiency").  Host arithmetic only; x, w and y are only inspected for
+ * alignment.  out is a host pointer, written on success.  Errors: the
+ * argument errors of gemm355_conv2d, EINVAL for a NULL out. */
 GEMM355_API gemm355_status gemm355_conv2d_plan(const gemm355_conv_args *args, gemm355_plan_t *out);
 
-/* Output extent of that convolution: *P = (H + 2 pad_h - dil_h (R - 1) - 1)
+/* Output extent of that convolution (the window positions of the
+ * cross-correlation that page "The Tensor Core" lowers to a matrix product):
+ * *P = (H + 2 pad_h - dil_h (R - 1) - 1)
  * / stride_h + 1 and *Q likewise along W (the window positions that fit in
  * the padded image), as gemm355_conv2d uses them to size y.  Host
  * arithmetic only; x, w and y are not inspected.  P and Q are host
@@ -493,7 +502,9 @@ GEMM355_API gemm355_status gemm355_conv2d_plan(const gemm355_conv_args *args, ge
  * pointers. */
 GEMM355_API gemm355_status gemm355_conv2d_out_size(const gemm355_conv_args *args, int64_t *P, int64_t *Q);
 
-/* Static description of a status code. */
+/* Static description of a status code (this library's own codes; no
+ * passage of the pages defines them).  Never NULL: unknown codes get a
+ * generic description. */
 GEMM355_API const char *gemm355_status_string(gemm355_status status);
 
 #ifdef __cplusplus
