@@ -9,7 +9,8 @@
  * persistent grid), gemm355_gemm_ex (E4M3 operands, bf16 output, batch with
  * per-entry scales, a caller workspace), gemm355_gemm_noalloc, gemm355_plan,
  * the convolution entry points (output size, plan, automatic and split-K
- * runs), K == 0, and an argument error.  Prints one line per case; exit status 0
+ * runs), the per-tensor quantiser (fp32 and bf16 sources, both 8-bit
+ * formats), K == 0, and an argument error.  Prints one line per case; exit status 0
  * when all agree.
  */
 #include <math.h>
@@ -63,6 +64,14 @@ static uint16_t bf16_of_int(int v)
 static uint8_t e4m3_of_int(int v)
 {
     static const uint8_t mag[5] = {0x00, 0x38, 0x40, 0x44, 0x48};
+    uint8_t c = mag[v < 0 ? -v : v];
+    return (uint8_t)(v < 0 ? (c | 0x80) : c);
+}
+
+/* OCP E5M2 codes of -4 .. 4 (bias 15; 3 = 1.5 * 2). */
+static uint8_t e5m2_of_int(int v)
+{
+    static const uint8_t mag[5] = {0x00, 0x3C, 0x40, 0x42, 0x44};
     uint8_t c = mag[v < 0 ? -v : v];
     return (uint8_t)(v < 0 ? (c | 0x80) : c);
 }
@@ -294,6 +303,73 @@ int main(void)
         }
         HIP_OK(hipFree(dx)); HIP_OK(hipFree(dw)); HIP_OK(hipFree(dy));
         free(x); free(w); free(x16); free(w16); free(yref); free(y);
+    }
+
+    /* Per-tensor quantiser, fp32 and bf16 sources, both formats: each of the
+     * two tensors holds the format's largest finite magnitude once (+ in
+     * tensor 0, - in tensor 1) and small integers elsewhere, so its scale
+     * is amax / max = 1 exactly and every code is the exact encoding. */
+    {
+        const int64_t nq = 1000, bq = 2;
+        float *xf = malloc(sizeof(float) * (size_t)(nq * bq));
+        uint16_t *xb = malloc(2 * (size_t)(nq * bq));
+        int8_t *xi = malloc((size_t)(nq * bq));
+        uint8_t *qh = malloc((size_t)(nq * bq));
+        if (!xf || !xb || !xi || !qh) {
+            fprintf(stderr, "host allocation failed\n");
+            return 3;
+        }
+        void *dxf, *dxb, *dq, *dsc;
+        HIP_OK(hipMalloc(&dxf, sizeof(float) * (size_t)(nq * bq)));
+        HIP_OK(hipMalloc(&dxb, 2 * (size_t)(nq * bq)));
+        HIP_OK(hipMalloc(&dq, (size_t)(nq * bq)));
+        HIP_OK(hipMalloc(&dsc, 2 * sizeof(float)));
+        static const struct { const char *name; gemm355_fp8 fmt; float max; uint8_t max_code; } fmts[] = {
+            {"e4m3", GEMM355_FP8_E4M3, 448.0f, 0x7E}, {"e5m2", GEMM355_FP8_E5M2, 57344.0f, 0x7B}};
+        for (size_t f = 0; f < 2; ++f) {
+            const int64_t at[2] = {17, nq + 911};   /* +max in tensor 0, -max in tensor 1 */
+            for (int64_t e = 0; e < nq * bq; ++e) xi[e] = (int8_t)next_small();
+            for (int64_t e = 0; e < nq * bq; ++e) xf[e] = (float)xi[e];
+            xf[at[0]] = fmts[f].max;
+            xf[at[1]] = -fmts[f].max;
+            for (int64_t e = 0; e < nq * bq; ++e) {
+                uint32_t u;
+                memcpy(&u, &xf[e], 4);
+                xb[e] = (uint16_t)(u >> 16);   /* exact: the values have few mantissa bits */
+            }
+            HIP_OK(hipMemcpy(dxf, xf, sizeof(float) * (size_t)(nq * bq), hipMemcpyHostToDevice));
+            HIP_OK(hipMemcpy(dxb, xb, 2 * (size_t)(nq * bq), hipMemcpyHostToDevice));
+            for (int src = 0; src < 2; ++src) {
+                char name[48];
+                snprintf(name, sizeof name, "quantize_%s_%s", src ? "bf16" : "f32", fmts[f].name);
+                HIP_OK(hipMemsetAsync(dq, 0xAA, (size_t)(nq * bq), stream));
+                HIP_OK(hipMemsetAsync(dsc, 0xFF, 2 * sizeof(float), stream));
+                expect_status(name,
+                              gemm355_quantize(src ? dxb : dxf, nq, bq, src ? GEMM355_SRC_BF16 : GEMM355_SRC_F32,
+                                               fmts[f].fmt, dq, (float *)dsc, (void *)stream),
+                              GEMM355_OK);
+                HIP_OK(hipStreamSynchronize(stream));
+                float sc[2];
+                HIP_OK(hipMemcpy(sc, dsc, sizeof sc, hipMemcpyDeviceToHost));
+                HIP_OK(hipMemcpy(qh, dq, (size_t)(nq * bq), hipMemcpyDeviceToHost));
+                int64_t bad = 0;
+                for (int64_t e = 0; e < nq * bq; ++e) {
+                    uint8_t want = f == 0 ? e4m3_of_int(xi[e]) : e5m2_of_int(xi[e]);
+                    if (e == at[0]) want = fmts[f].max_code;
+                    if (e == at[1]) want = (uint8_t)(fmts[f].max_code | 0x80);
+                    if (qh[e] != want) ++bad;
+                }
+                if (sc[0] != 1.0f || sc[1] != 1.0f || bad) {
+                    fprintf(stderr, "%s: scales %.9g %.9g, %lld codes differ\n", name, (double)sc[0],
+                            (double)sc[1], (long long)bad);
+                    ++failures;
+                } else {
+                    printf("case %s ok (%lld codes)\n", name, (long long)(nq * bq));
+                }
+            }
+        }
+        HIP_OK(hipFree(dxf)); HIP_OK(hipFree(dxb)); HIP_OK(hipFree(dq)); HIP_OK(hipFree(dsc));
+        free(xf); free(xb); free(xi); free(qh);
     }
 
     /* K == 0 writes zeros; a negative extent is an argument error. */

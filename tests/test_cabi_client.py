@@ -7,8 +7,8 @@ system HIP runtime, with no Python or PyTorch in the process that runs it.
 * GPU: the client's products (automatic plan, forced split-K, persistent
   grid, E4M3 with bf16 output and a caller workspace, a scaled batch through
   the allocation-free entry point, a convolution with padding, stride and
-  dilation, K = 0, an argument error) equal its exact integer reference bit
-  for bit.
+  dilation, the quantiser on tensors whose scale is exactly 1, K = 0, an
+  argument error) equal its exact reference bit for bit.
 """
 import os
 import shutil
@@ -50,5 +50,6 @@ def test_client_products_exact(tmp_path):
     assert r.returncode == 0 and "all cases ok" in r.stdout, r.stdout + r.stderr
     for case in ("gemm_bf16_auto", "gemm_bf16_split4", "gemm_bf16_persistent", "plan",
                  "gemm_ex_e4m3_bf16", "gemm_noalloc_batch_0", "gemm_noalloc_batch_1", "conv_auto",
-                 "conv_split3", "gemm_k0"):
+                 "conv_split3", "quantize_f32_e4m3", "quantize_bf16_e4m3", "quantize_f32_e5m2",
+                 "quantize_bf16_e5m2", "gemm_k0"):
         assert "case %s ok" % case in r.stdout, case
