@@ -77,7 +77,8 @@ def parse():
                          "graphics clocks are sampled (amd-smi) half way through")
     ap.add_argument("--vendor", action="store_true",
                     help="with --profile and a bf16 workload: time the vendor library "
-                         "(torch.matmul on the same operands) instead of this library, as context")
+                         "(torch.matmul into bf16 C, torch.mm with out_dtype float32 for fp32 C, "
+                         "on the same operand copies) instead of this library, as context")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes 5 times "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -676,8 +677,20 @@ def main():
         if args.vendor:
             if w.fmt != "bf16" or c.batch != 1:
                 sys.exit("--vendor: bf16 single products only")
-            Av, Bv = c.As[0].view(torch.bfloat16), c.Bs[0].view(torch.bfloat16)
-            c.step = lambda stream: torch.matmul(Av, Bv.t(), out=c.C)
+            # the same operand copies in turn as the library's calls (cold
+            # inputs on memory-bound shapes); fp32 C through the bf16 x bf16
+            # -> fp32 product
+            Avs = [x.view(torch.bfloat16) for x in c.As]
+            Bvs = [x.view(torch.bfloat16).t() for x in c.Bs]
+
+            def vendor_step(stream):
+                i = c.i % c.copies
+                c.i += 1
+                if c.C.dtype == torch.float32:
+                    torch.mm(Avs[i], Bvs[i], out_dtype=torch.float32)
+                else:
+                    torch.matmul(Avs[i], Bvs[i], out=c.C)
+            c.step = vendor_step
         _, ev = time_case(c, torch, args.steps, args.warmup, args.settle or 0.0)
         me = c.measured_eta(torch) if args.stamps and not args.vendor else None
         out = {"workload": c.name(), "us_per_call": round(ev / args.steps * 1e6, 2),
